@@ -1,0 +1,219 @@
+"""CPU oracle for one batch-1 decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU product path never touches it.
+The arithmetic lives in ``oracle.c`` (plain C, fp64 accumulation); this file
+only marshals numpy arrays through ctypes.
+
+Pins (each checked by a ``-m "not gpu"`` test):
+  * parameter count of the SmolLM-135M shape = 134,515,008, the figure the
+    MegaBake article prints (section "What a megakernel is");
+  * RMSNorm: closed form on constant vectors, unit RMS, scale invariance;
+  * matvec: numpy's float64 matrix product;
+  * RoPE: identity at position 0, norm preservation, relative-position
+    dot products, composition, pair structure and per-pair angle;
+  * attention: scipy softmax brute force, one position gives V_0, equal keys
+    or a zero query give the mean of V, GQA == MHA with repeated KV heads;
+  * SiLU: silu(0) = 0, silu(z) -> z for large z, scipy expit;
+  * decode step: stepwise decode equals an independent float64 full-sequence
+    causal forward; zero output projections give a closed-form logit vector
+    whose argmax is the input token.
+Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc -O2, OpenMP)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < newest:
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "intermediate", "vocab", "kv_capacity",
+        "qkv_bias")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p)] + [
+        (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "wo", "mlp_norm", "wgate", "wup",
+                           "wdown")]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x_in", "q", "k", "v", "o", "x_mid", "a", "x_final")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_SO)
+        vp, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.orc_rmsnorm.argtypes = [vp, vp, i, d, vp]
+        lib.orc_matvec.argtypes = [vp, vp, i, i, vp, vp]
+        lib.orc_matvec_residual.argtypes = [vp, i, i, vp, vp]
+        lib.orc_rope.argtypes = [vp, i, i, i, d]
+        lib.orc_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+        lib.orc_silu_mul.argtypes = [vp, vp, i, vp]
+        lib.orc_argmax.argtypes = [vp, i]
+        lib.orc_argmax.restype = i
+        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_f32.restype = ctypes.c_float
+        lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+        lib.orc_decode_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), vp, i, i, vp,
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(Trace)]
+        lib.orc_decode_step.restype = i
+        lib.orc_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _u16(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(_load().orc_f32_to_bf16(float(x)))
+
+
+def rmsnorm(x, w_bf16, eps: float) -> np.ndarray:
+    x, w = _f32(x), _u16(w_bf16)
+    out = np.empty_like(x)
+    _load().orc_rmsnorm(x.ctypes.data, w.ctypes.data, x.size, eps, out.ctypes.data)
+    return out
+
+
+def matvec(W_bf16, x, b_bf16=None) -> np.ndarray:
+    W, x = _u16(W_bf16), _f32(x)
+    M, K = W.shape
+    assert x.size == K
+    b = None if b_bf16 is None else _u16(b_bf16)
+    y = np.empty(M, dtype=np.float32)
+    _load().orc_matvec(W.ctypes.data, None if b is None else b.ctypes.data, M, K, x.ctypes.data, y.ctypes.data)
+    return y
+
+
+def matvec_residual(W_bf16, v, x) -> np.ndarray:
+    W, v = _u16(W_bf16), _f32(v)
+    out = _f32(x).copy()
+    M, K = W.shape
+    _load().orc_matvec_residual(W.ctypes.data, M, K, v.ctypes.data, out.ctypes.data)
+    return out
+
+
+def rope(v, n_heads: int, head_dim: int, pos: int, theta: float) -> np.ndarray:
+    out = _f32(v).copy()
+    assert out.size == n_heads * head_dim
+    _load().orc_rope(out.ctypes.data, n_heads, head_dim, pos, theta)
+    return out
+
+
+def attention(q, K_bf16, V_bf16, n_heads: int, n_kv: int, head_dim: int, Lc: int) -> np.ndarray:
+    """q [nq*hd] fp32; K, V [n_kv][cap][hd] bf16 of one layer; attends positions 0..Lc-1."""
+    q, K, V = _f32(q), _u16(K_bf16), _u16(V_bf16)
+    cap = K.shape[1]
+    o = np.empty(n_heads * head_dim, dtype=np.float32)
+    _load().orc_attention(q.ctypes.data, K.ctypes.data, V.ctypes.data, n_heads, n_kv, head_dim, cap, Lc,
+                          o.ctypes.data)
+    return o
+
+
+def silu_mul(g, u) -> np.ndarray:
+    g, u = _f32(g), _f32(u)
+    out = np.empty_like(g)
+    _load().orc_silu_mul(g.ctypes.data, u.ctypes.data, g.size, out.ctypes.data)
+    return out
+
+
+def argmax(v) -> int:
+    v = _f32(v)
+    return int(_load().orc_argmax(v.ctypes.data, v.size))
+
+
+class Model:
+    """Holds a workload's config, its bf16 weights and an oracle-side KV cache."""
+
+    def __init__(self, wl, weights: Dict[str, object]):
+        self.wl = wl
+        self.cfg = Config(wl.n_layers, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.intermediate,
+                          wl.vocab, wl.kv_capacity, int(wl.qkv_bias), wl.rms_eps, wl.rope_theta)
+        self._keep = []
+        self.weights = weights
+        L = wl.n_layers
+        arrs = {}
+        names = ["attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wgate", "wup", "wdown"]
+        if wl.qkv_bias:
+            names += ["bq", "bk", "bv"]
+        for n in names:
+            a = (ctypes.c_void_p * L)()
+            for l in range(L):
+                t = _u16(weights["layers"][l][n])
+                self._keep.append(t)
+                a[l] = t.ctypes.data
+            self._keep.append(a)
+            arrs[n] = ctypes.cast(a, _PP)
+        emb, fn = _u16(weights["embed"]), _u16(weights["final_norm"])
+        self._keep += [emb, fn]
+        w = Weights()
+        w.embed, w.final_norm = emb.ctypes.data, fn.ctypes.data
+        for n, p in arrs.items():
+            setattr(w, n, p)
+        self.w = w
+        self.kv = np.zeros((L, 2, wl.n_kv_heads, wl.kv_capacity, wl.head_dim), dtype=np.uint16)
+
+    def prefill_kv(self, kv_prefix: np.ndarray) -> None:
+        """Copy [NL][2][nkv][P][hd] bf16 values into slots 0..P-1."""
+        P = kv_prefix.shape[3]
+        self.kv[:, :, :, :P, :] = kv_prefix
+
+    def step(self, token: int, pos: int, trace: bool = False) -> Tuple[np.ndarray, int, Optional[dict]]:
+        wl = self.wl
+        logits = np.empty(wl.vocab, dtype=np.float32)
+        am = ctypes.c_int(-1)
+        tr, trd = None, None
+        if trace:
+            L, H, Q, KV, I = wl.n_layers, wl.hidden, wl.n_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim, wl.intermediate
+            trd = {"x_in": np.empty((L, H), np.float32), "q": np.empty((L, Q), np.float32),
+                   "k": np.empty((L, KV), np.float32), "v": np.empty((L, KV), np.float32),
+                   "o": np.empty((L, Q), np.float32), "x_mid": np.empty((L, H), np.float32),
+                   "a": np.empty((L, I), np.float32), "x_final": np.empty(H, np.float32)}
+            tr = Trace(*[trd[n].ctypes.data for n in ("x_in", "q", "k", "v", "o", "x_mid", "a", "x_final")])
+        rc = _load().orc_decode_step(ctypes.byref(self.cfg), ctypes.byref(self.w), self.kv.ctypes.data,
+                                     int(token), int(pos), logits.ctypes.data, ctypes.byref(am),
+                                     ctypes.byref(tr) if tr is not None else None)
+        if rc != 0:
+            raise ValueError("orc_decode_step failed with %d (token=%d pos=%d)" % (rc, token, pos))
+        return logits, int(am.value), trd
