@@ -1,0 +1,136 @@
+/*
+ * mbk.h -- C ABI of libmbk: one batch-1 decode step of a pre-norm Llama-style
+ * decoder, run on an AMD MI355X (gfx950) as ONE persistent cooperative kernel.
+ *
+ * What a step computes (MegaBake article, "What a megakernel is, and why
+ * small models want one": per layer RMSNorm, Q/K/V projections, RoPE,
+ * attention, output projection, residual add, RMSNorm, gate and up
+ * projections, SiLU, down projection, residual add; MegaBake README mirror,
+ * "Current status": the kernel also covers the embedding, the final norm, the
+ * vocabulary projection and the KV-cache update), followed by a greedy
+ * argmax of the logits.
+ *
+ * Conventions shared by every entry point
+ *  - All functions return an int status: MBK_OK (0) or one of MBK_ERR_*.
+ *    mbk_last_error() returns a thread-local message for the last failure.
+ *  - Device buffers (source weights, packed weights, KV cache, workspace,
+ *    logits, argmax) are owned by the caller and passed as raw device
+ *    pointers; the library never frees them and allocates no device memory
+ *    on the decode path.  Streams are hipStream_t passed as void*.
+ *  - Validation happens on the host before any HIP call: a call that returns
+ *    MBK_ERR_ARG / RANGE / SIZE / UNSUPPORTED / STATE has launched nothing.
+ *  - One handle per stream; calls on one handle are not reentrant.
+ *  - Like the README's strict default (section "The compilation path":
+ *    compilation errors rather than falling back), an unsupported shape is an
+ *    error, never a slower path.
+ */
+#ifndef MBK_H
+#define MBK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MBK_OK = 0,
+    MBK_ERR_ARG = 1,         /* NULL pointer, token outside [0, vocab), bad enum */
+    MBK_ERR_RANGE = 2,       /* position outside [0, kv_capacity) */
+    MBK_ERR_SIZE = 3,        /* caller buffer smaller than required */
+    MBK_ERR_UNSUPPORTED = 4, /* dimensions the kernels do not handle */
+    MBK_ERR_HIP = 5,         /* a HIP runtime call failed (message has the HIP error) */
+    MBK_ERR_TIMEOUT = 6,     /* a bounded grid-barrier wait expired on the device */
+    MBK_ERR_STATE = 7        /* call made before mbk_pack_weights / mbk_alloc_kv */
+};
+
+/* Pass as `token` to reuse the previous step's device-side argmax, so a greedy
+ * loop needs no host round trip (the README's "pipelined calls"). */
+#define MBK_TOKEN_PREV (-1)
+
+/* Decoder shape. Supported: head_dim in {16, 32, 64, 128}; n_heads a multiple
+ * of n_kv_heads with n_heads / n_kv_heads <= 8; hidden, n_heads*head_dim and
+ * intermediate multiples of 8 and <= 8192; kv_capacity <= 8192 (the README's
+ * bound on decode KV state, "Current status"). */
+typedef struct {
+    int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, kv_capacity;
+    int32_t qkv_bias; /* 0 or 1: bias added to the Q/K/V projections */
+    float rms_eps, rope_theta;
+} mbk_config;
+
+/* Source weights: bf16 device pointers in Hugging Face layout (row-major
+ * [out][in]).  Per-layer fields are HOST arrays of n_layers device pointers.
+ * The LM head is the tied embedding.  bq/bk/bv are read only if qkv_bias. */
+typedef struct {
+    const void *embed;      /* [vocab][hidden] */
+    const void *final_norm; /* [hidden] */
+    const void *const *attn_norm, *const *wq, *const *wk, *const *wv;
+    const void *const *bq, *const *bk, *const *bv;
+    const void *const *wo, *const *mlp_norm, *const *wgate, *const *wup, *const *wdown;
+} mbk_weights;
+
+typedef struct mbk_model mbk_model; /* opaque host handle */
+
+/* Validates the shape and creates a handle. No device work. */
+int mbk_create(const mbk_config *cfg, mbk_model **out);
+
+/* Frees the handle only (never caller memory). NULL is a no-op. */
+void mbk_destroy(mbk_model *m);
+
+/* Packs the weights into the streaming layout the kernels read.
+ * dst == NULL: writes the required size to *dst_bytes and returns.
+ * Otherwise packs device-to-device on `stream` into dst (>= *dst_bytes bytes,
+ * 256-byte aligned); the handle keeps dst, which the caller keeps alive.
+ * Every matrix is stored as tiles of RT rows in which each wave-wide 16-byte
+ * load reads 1 KiB of contiguous memory; the packed payload is exactly
+ * 2 bytes per parameter when no tile padding is needed (all the supported
+ * leaderboard shapes).  Also builds the fp32 RoPE table inside dst. */
+int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *dst_bytes, void *stream);
+
+/* Binds the KV cache and the workspace.
+ * kv == NULL or ws == NULL: writes the required sizes and returns.
+ * Otherwise zero-fills both on `stream` and keeps them.
+ * KV layout: bf16 [n_layers][2 (K, V)][n_kv_heads][kv_capacity][head_dim],
+ * keys stored after rotation; callers may pre-fill slots through this layout.
+ * Both buffers must be 256-byte aligned. */
+int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_bytes, void *stream);
+
+/* One decode step at position `pos` (0-based) for `token`, asynchronous on
+ * `stream`: writes KV slot `pos` of every layer, attends positions 0..pos,
+ * writes fp32 logits[vocab] (if logits != NULL) and the greedy argmax
+ * (lowest index among equal maxima) to argmax[0] (device int32).  Re-running
+ * a step at the same pos overwrites slot pos before reading it.
+ * One cooperative launch of one workgroup per CU. */
+int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream);
+
+/* Same bodies and results (bitwise), one kernel launch per barrier interval
+ * (the per-operator ablation).  use_graph = 1 replays the launches as a
+ * hipGraph instantiated once per handle. */
+int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax,
+                             int32_t use_graph, void *stream);
+
+/* Synchronises `stream` and reports device-side errors (MBK_ERR_TIMEOUT
+ * when a bounded barrier wait expired; the KV/workspace must then be re-bound
+ * with mbk_alloc_kv). */
+int mbk_check(mbk_model *m, void *stream);
+
+/* Grid-barrier microbenchmark: one cooperative launch running n barriers with
+ * empty bodies; *us_per_barrier = (t(n) - t(0)) / n from HIP events. */
+int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier);
+
+/* Number of barrier intervals (and ablation launches) per step. */
+int mbk_num_intervals(const mbk_model *m, int32_t *n);
+
+/* Test hook: limit every bounded barrier wait to `spin_limit` polls (0 =
+ * default) and make workgroup `skip_wg` (-1 = none) skip its arrival at
+ * interval `skip_interval`, so a test can force the watchdog from the host. */
+int mbk_set_debug(mbk_model *m, int32_t spin_limit, int32_t skip_wg, int32_t skip_interval);
+
+/* Message for the last non-zero status returned on this thread. */
+const char *mbk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MBK_H */

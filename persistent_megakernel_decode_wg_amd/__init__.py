@@ -1,0 +1,10 @@
+"""Python binding of libmbk, the batch-1 persistent-megakernel decoder for MI355X.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libmbk.so`` (see ``include/mbk.h``).  PyTorch provides device
+memory (tensors) and the current stream.  If the library has not been built
+the import of ``Decoder`` fails loudly; there is no fallback path.
+"""
+from .binding import (  # noqa: F401
+    MBK_ERR_ARG, MBK_ERR_HIP, MBK_ERR_RANGE, MBK_ERR_SIZE, MBK_ERR_STATE, MBK_ERR_TIMEOUT, MBK_ERR_UNSUPPORTED,
+    MBK_OK, MBK_TOKEN_PREV, Decoder, MbkError, lib, lib_path)

@@ -1,0 +1,119 @@
+// layout.h -- packed-weight geometry, interval table and workspace layout of libmbk.
+//
+// Shared by the host-side planner/packer and the device bodies, so both read
+// the same tile geometry.  Everything here is plain data and index arithmetic.
+#pragma once
+#include <stdint.h>
+
+#ifndef MBK_HD
+#define MBK_HD __host__ __device__ __forceinline__
+#endif
+
+namespace mbk {
+
+constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kGroups = 8;             // barrier groups: WG w belongs to group w % 8 (one per XCD
+                                       // under the round-robin dispatch of an 8-XCD part)
+constexpr int kMaxVec = 8192;          // largest GEMV input vector (floats) held in LDS
+constexpr int kMaxGqa = 8;             // query heads per KV head handled by one attention item
+constexpr int kAttnMinChunk = 64;      // fewest cached positions per attention split
+
+enum Op : int32_t { OP_QKV = 0, OP_ATTN = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4, OP_LMHEAD = 5 };
+enum MatKind : int32_t { MAT_PLAIN = 0, MAT_QKV = 1, MAT_GATEUP = 2 };
+
+// A packed bf16 matrix.  Rows (in packed order) are grouped in tiles of RT
+// rows; each row's K inputs are split in 8-element groups (16 bytes) spread
+// over L = 64 / RT lanes.  Chunk (tile t, step it, lane l) holds the 8 values
+//   packed row  t*RT + l / L,   input group  kg = (l % L) + it * L
+// and sits at byte  off + ((t * IT + it) * 64 + l) * 16,  IT = (K / 8) / L.
+// So every wave-wide 16-byte load of one step reads 1 KiB of contiguous memory.
+struct MatGeom {
+    uint64_t off;    // byte offset in the packed blob
+    int32_t rows;    // packed rows = ntiles * RT (rows >= logical rows)
+    int32_t K;
+    int32_t L, RT, IT;
+    int32_t ntiles;
+    int32_t kind;    // MatKind: how packed rows map to source rows
+    int32_t pad;
+};
+
+MBK_HD uint64_t chunk_offset(const MatGeom &g, int64_t tile, int it, int lane) {
+    return g.off + ((uint64_t)(tile * g.IT + it) * 64u + (uint64_t)lane) * 16u;
+}
+
+// Byte offset of the 16-byte group kg of packed row r.
+MBK_HD uint64_t row_group_offset(const MatGeom &g, int64_t r, int kg) {
+    int64_t t = r / g.RT;
+    int rr = (int)(r % g.RT);
+    int it = kg / g.L, kl = kg % g.L;
+    return chunk_offset(g, t, it, rr * g.L + kl);
+}
+
+// Geometry rule: L is the largest power of two <= 64 dividing K/8; operators
+// whose epilogue combines two adjacent packed rows (RoPE pairs, gate/up
+// pairs) need RT >= 2, so their L is capped at 32.
+MBK_HD void choose_lanes(int K, bool pairs, int *L, int *RT) {
+    int kg = K / 8, l = 1;
+    while (l < 64 && kg % (l * 2) == 0) l *= 2;
+    if (pairs && l > 32) l = 32;
+    *L = l;
+    *RT = 64 / l;
+}
+
+// Source of packed row r of a fused matrix.
+//  MAT_QKV: rows [0, nq*hd) are queries, then nkv*hd keys, then nkv*hd values.
+//    Inside each query or key head the rows are interleaved so that packed
+//    rows (2m, 2m+1) are head dims (m, m + hd/2): the pair RoPE rotates.
+//  MAT_GATEUP: packed row 2i is gate row i, 2i+1 is up row i.
+struct RowSrc {
+    int32_t which;   // QKV: 0 q, 1 k, 2 v; GATEUP: 0 gate, 1 up; PLAIN: 0
+    int32_t row;     // row inside that source matrix
+};
+
+MBK_HD RowSrc packed_row_source(int kind, int r, int hd, int nq_rows, int nkv_rows) {
+    RowSrc s{0, r};
+    if (kind == MAT_QKV) {
+        int which = 0, base = r;
+        if (r >= nq_rows + nkv_rows) { which = 2; base = r - nq_rows - nkv_rows; }
+        else if (r >= nq_rows) { which = 1; base = r - nq_rows; }
+        if (which < 2) {
+            int h = base / hd, i = base % hd;
+            base = h * hd + ((i & 1) ? (i >> 1) + hd / 2 : (i >> 1));
+        }
+        s.which = which;
+        s.row = base;
+    } else if (kind == MAT_GATEUP) {
+        s.which = r & 1;
+        s.row = r >> 1;
+    }
+    return s;
+}
+
+// One barrier interval of the static task list (a row of the phase table).
+struct Interval {
+    int32_t op;        // Op
+    int32_t layer;
+    int32_t n_items;   // GEMV: tiles; attention: n_kv_heads * max_splits
+    int32_t rot;       // item i runs on workgroup (i + rot) % n_wg
+    MatGeom mat;       // GEMV operators
+    uint64_t norm_off; // RMSNorm weight folded into this interval (bf16), or ~0
+    uint64_t bias_off; // Q/K/V bias (bf16, [q|k|v] natural order), or ~0
+};
+
+// Workspace layout (bytes).  Control words get their own 256-byte lines.
+struct WsLayout {
+    uint64_t ctrl;      // [0] error flag, [1] previous argmax token, [2] LM-head arrivals
+    uint64_t argkey;    // u64 argmax key
+    uint64_t bar_global;
+    uint64_t bar_group; // kGroups lines: arrival counters
+    uint64_t bar_rel;   // kGroups lines: release epochs
+    uint64_t merge_cnt; // n_kv lines: attention split arrivals
+    uint64_t x, q, o, a;
+    uint64_t part;      // attention partials [n_kv][max_splits][g][hd + 2]
+    uint64_t total;
+};
+
+MBK_HD uint64_t align256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+}  // namespace mbk

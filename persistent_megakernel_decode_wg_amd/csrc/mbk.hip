@@ -1,0 +1,561 @@
+// mbk.hip -- libmbk: kernels and the C ABI declared in include/mbk.h.
+//
+// Executors (MegaBake article, section "How a model gets in": phases grouped
+// into barrier intervals, a table-driven persistent loop that dispatches a
+// body per phase row and closes each interval with a counting grid barrier):
+//   k_persistent  one cooperative launch, one workgroup per CU, walks the
+//                 static interval table with a grid barrier between intervals;
+//   k_interval    the same bodies, one launch per interval (the ablation).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <cstdarg>
+#include <string>
+#include <vector>
+
+#include "../../include/mbk.h"
+#include "bodies.h"
+#include "layout.h"
+
+using namespace mbk;
+
+// ---- kernels ----------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
+    extern __shared__ float lds[];
+    __shared__ float red[kWaves];
+    for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
+        run_interval(p, ivi, lds, red);
+        if (ivi + 1 < p.last_iv) {
+            if (!grid_barrier(p, p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u, ivi)) return;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_interval(Params p, int ivi) {
+    extern __shared__ float lds[];
+    __shared__ float red[kWaves];
+    run_interval(p, ivi, lds, red);
+}
+
+__global__ __launch_bounds__(kThreads) void k_barrier_bench(Params p, int n) {
+    for (int i = 0; i < n; ++i)
+        if (!grid_barrier(p, p.epoch_base + (uint32_t)i + 1u, -1)) return;
+}
+
+// Packer: one thread per 16-byte chunk of the packed matrix.
+__global__ void k_pack(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16_t *s1, const uint16_t *s2, int hd,
+                       int nq_rows, int nkv_rows) {
+    const uint64_t n = (uint64_t)g.ntiles * g.IT * 64u;
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (uint64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(c % 64u);
+        const uint64_t rest = c / 64u;
+        const int it = (int)(rest % (uint64_t)g.IT);
+        const int64_t t = (int64_t)(rest / (uint64_t)g.IT);
+        const int64_t prow = t * g.RT + lane / g.L;
+        const int kg = (lane % g.L) + it * g.L;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (prow < g.rows) {
+            RowSrc s = packed_row_source(g.kind, (int)prow, hd, nq_rows, nkv_rows);
+            const uint16_t *src = s.which == 0 ? s0 : (s.which == 1 ? s1 : s2);
+            v = *(const u32x4 *)(src + (uint64_t)s.row * g.K + (uint64_t)kg * 8u);
+        }
+        *(u32x4 *)(dst + g.off + c * 16u) = v;
+    }
+}
+
+// ---- host side --------------------------------------------------------------------------------------
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIPCHK(call)                                                                              \
+    do {                                                                                          \
+        hipError_t e_ = (call);                                                                   \
+        if (e_ != hipSuccess) return fail(MBK_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+struct LayerPlan {
+    MatGeom qkv, o, gu, down;
+    uint64_t attn_norm, mlp_norm, bias;  // bias = ~0 when absent
+};
+
+struct Plan {
+    std::vector<LayerPlan> layers;
+    MatGeom embed;
+    uint64_t final_norm = 0, rope = 0, table = 0, total = 0;
+    std::vector<Interval> iv;
+    int max_splits = 1;
+    size_t lds_bytes = 0;
+    WsLayout ws{};
+};
+
+}  // namespace
+
+struct mbk_model {
+    mbk_config c;
+    int n_wg = 0;
+    int device = -1;
+    bool planned = false;
+    Plan plan;
+    std::vector<float> rope_host;
+    uint8_t *blob = nullptr;
+    uint16_t *kv = nullptr;
+    uint8_t *ws = nullptr;
+    uint32_t epoch = 0;
+    int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
+    // graph replay of the ablation
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t gexec = nullptr;
+    hipGraphNode_t node0 = nullptr;
+    float *g_logits = nullptr;
+    int32_t *g_argmax = nullptr;
+};
+
+namespace {
+
+MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind) {
+    MatGeom g{};
+    choose_lanes(K, pairs, &g.L, &g.RT);
+    g.K = K;
+    g.IT = (K / 8) / g.L;
+    g.rows = rows;
+    g.ntiles = (rows + g.RT - 1) / g.RT;
+    g.kind = kind;
+    g.off = cursor;
+    cursor = align256(cursor + (uint64_t)g.ntiles * g.IT * 1024u);
+    return g;
+}
+
+Interval gemv_interval(int op, int layer, const MatGeom &g, uint64_t norm, uint64_t bias) {
+    Interval v{};
+    v.op = op;
+    v.layer = layer;
+    v.n_items = g.ntiles;
+    v.rot = 0;
+    v.mat = g;
+    v.norm_off = norm;
+    v.bias_off = bias;
+    return v;
+}
+
+int ensure_device(mbk_model *m) {
+    if (m->n_wg > 0) return MBK_OK;
+    HIPCHK(hipGetDevice(&m->device));
+    int cus = 0;
+    HIPCHK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m->device));
+    if (cus <= 0) return fail(MBK_ERR_HIP, "device reports %d compute units", cus);
+    m->n_wg = cus;
+    return MBK_OK;
+}
+
+void build_plan(mbk_model *m) {
+    const mbk_config &c = m->c;
+    Plan &P = m->plan;
+    const int hd = c.head_dim, Q = c.n_heads * hd, KV = c.n_kv_heads * hd, G = c.n_heads / c.n_kv_heads;
+    uint64_t cur = 0;
+    P.layers.resize(c.n_layers);
+    for (int l = 0; l < c.n_layers; ++l) {
+        LayerPlan &L = P.layers[l];
+        L.qkv = make_geom(cur, Q + 2 * KV, c.hidden, true, MAT_QKV);
+        L.o = make_geom(cur, c.hidden, Q, false, MAT_PLAIN);
+        L.gu = make_geom(cur, 2 * c.intermediate, c.hidden, true, MAT_GATEUP);
+        L.down = make_geom(cur, c.hidden, c.intermediate, false, MAT_PLAIN);
+        L.attn_norm = cur;
+        cur = align256(cur + 2u * c.hidden);
+        L.mlp_norm = cur;
+        cur = align256(cur + 2u * c.hidden);
+        L.bias = ~(uint64_t)0;
+        if (c.qkv_bias) {
+            L.bias = cur;
+            cur = align256(cur + 2u * (Q + 2 * KV));
+        }
+    }
+    P.embed = make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN);
+    P.final_norm = cur;
+    cur = align256(cur + 2u * c.hidden);
+    P.rope = cur;
+    cur = align256(cur + (uint64_t)c.kv_capacity * (hd / 2) * 8u);
+
+    // attention split count: enough items to reach every CU, and every
+    // partial of one KV head must fit in LDS for the merge
+    const int stride = hd + 4;
+    const size_t attn_budget = 96 * 1024;
+    int ms = std::max(1, m->n_wg / c.n_kv_heads);
+    ms = std::min<int>(ms, (int)(attn_budget / ((size_t)G * stride * 4)));
+    ms = std::max(1, std::min(ms, 64));
+    P.max_splits = ms;
+    size_t lds = (size_t)std::max({c.hidden, Q, c.intermediate}) * 4;
+    lds = std::max(lds, (size_t)(G + kWaves * G) * stride * 4);
+    lds = std::max(lds, (size_t)ms * G * stride * 4);
+    P.lds_bytes = (lds + 15) & ~(size_t)15;
+
+    P.iv.clear();
+    for (int l = 0; l < c.n_layers; ++l) {
+        const LayerPlan &L = P.layers[l];
+        P.iv.push_back(gemv_interval(OP_QKV, l, L.qkv, L.attn_norm, L.bias));
+        Interval a{};
+        a.op = OP_ATTN;
+        a.layer = l;
+        a.n_items = c.n_kv_heads * ms;
+        a.rot = 0;
+        a.norm_off = a.bias_off = ~(uint64_t)0;
+        P.iv.push_back(a);
+        P.iv.push_back(gemv_interval(OP_O, l, L.o, ~(uint64_t)0, ~(uint64_t)0));
+        P.iv.push_back(gemv_interval(OP_GATEUP, l, L.gu, L.mlp_norm, ~(uint64_t)0));
+        P.iv.push_back(gemv_interval(OP_DOWN, l, L.down, ~(uint64_t)0, ~(uint64_t)0));
+    }
+    P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, ~(uint64_t)0));
+    P.table = cur;
+    cur = align256(cur + P.iv.size() * sizeof(Interval));
+    P.total = cur;
+
+    // workspace
+    WsLayout &W = P.ws;
+    uint64_t w = 0;
+    W.ctrl = w; w += 256;
+    W.argkey = w; w += 256;
+    W.bar_global = w; w += 256;
+    W.bar_group = w; w += 256 * kGroups;
+    W.bar_rel = w; w += 256 * kGroups;
+    W.merge_cnt = w; w += 256u * c.n_kv_heads;
+    W.x = w; w = align256(w + 4u * c.hidden);
+    W.q = w; w = align256(w + 4u * Q);
+    W.o = w; w = align256(w + 4u * Q);
+    W.a = w; w = align256(w + 4u * c.intermediate);
+    W.part = w; w = align256(w + 4u * (uint64_t)c.n_kv_heads * ms * G * stride);
+    W.total = w;
+
+    // RoPE table: angle pos * theta^(-2i/hd), evaluated in double, stored fp32
+    m->rope_host.assign((size_t)c.kv_capacity * (hd / 2) * 2, 0.f);
+    for (int pos = 0; pos < c.kv_capacity; ++pos)
+        for (int i = 0; i < hd / 2; ++i) {
+            const double ang = (double)pos * std::pow((double)c.rope_theta, -2.0 * i / (double)hd);
+            m->rope_host[((size_t)pos * (hd / 2) + i) * 2 + 0] = (float)std::cos(ang);
+            m->rope_host[((size_t)pos * (hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
+        }
+    m->planned = true;
+}
+
+int ensure_plan(mbk_model *m) {
+    if (m->planned) return MBK_OK;
+    int rc = ensure_device(m);
+    if (rc) return rc;
+    build_plan(m);
+    const size_t lds = m->plan.lds_bytes;
+    if (lds > 160 * 1024) return fail(MBK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", lds);
+    HIPCHK(hipFuncSetAttribute((const void *)k_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    HIPCHK(hipFuncSetAttribute((const void *)k_interval, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    return MBK_OK;
+}
+
+Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax) {
+    const mbk_config &c = m->c;
+    Params p{};
+    p.blob = m->blob;
+    p.iv = (const Interval *)(m->blob + m->plan.table);
+    p.kv = m->kv;
+    p.ws = m->ws;
+    p.wl = m->plan.ws;
+    p.logits = logits;
+    p.argmax_out = argmax;
+    p.rope = (const float *)(m->blob + m->plan.rope);
+    p.embed = m->plan.embed;
+    p.final_norm_off = m->plan.final_norm;
+    p.n_wg = m->n_wg;
+    p.n_intervals = (int)m->plan.iv.size();
+    p.H = c.hidden;
+    p.nq = c.n_heads;
+    p.nkv = c.n_kv_heads;
+    p.hd = c.head_dim;
+    p.I = c.intermediate;
+    p.V = c.vocab;
+    p.S = c.kv_capacity;
+    p.NL = c.n_layers;
+    p.max_splits = m->plan.max_splits;
+    p.gqa = c.n_heads / c.n_kv_heads;
+    p.eps = c.rms_eps;
+    p.scale = 1.0f / std::sqrt((float)c.head_dim);
+    p.token = token;
+    p.pos = pos;
+    p.step_from_ws = 0;
+    p.epoch_base = m->epoch;
+    p.spin_limit = m->spin_limit;
+    p.skip_wg = m->skip_wg;
+    p.skip_interval = m->skip_interval;
+    p.first_iv = 0;
+    p.last_iv = p.n_intervals;
+    return p;
+}
+
+int check_step_args(const mbk_model *m, int32_t token, int32_t pos, const int32_t *argmax) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    if (!m->blob || !m->kv || !m->ws) return fail(MBK_ERR_STATE, "weights not packed or KV/workspace not bound");
+    if (!argmax) return fail(MBK_ERR_ARG, "argmax output is null");
+    if (token != MBK_TOKEN_PREV && (token < 0 || token >= m->c.vocab))
+        return fail(MBK_ERR_ARG, "token %d outside [0, %d)", token, m->c.vocab);
+    if (pos < 0 || pos >= m->c.kv_capacity) return fail(MBK_ERR_RANGE, "pos %d outside [0, %d)", pos, m->c.kv_capacity);
+    return MBK_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int pack_matrix(mbk_model *m, const MatGeom &g, const void *s0, const void *s1, const void *s2, hipStream_t st) {
+    const int hd = m->c.head_dim;
+    const uint64_t n = (uint64_t)g.ntiles * g.IT * 64u;
+    const int threads = 256;
+    const int blocks = (int)std::min<uint64_t>((n + threads - 1) / threads, 65536);
+    hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(threads), 0, st, m->blob, g, (const uint16_t *)s0,
+                       (const uint16_t *)s1, (const uint16_t *)s2, hd, m->c.n_heads * hd, m->c.n_kv_heads * hd);
+    HIPCHK(hipGetLastError());
+    return MBK_OK;
+}
+
+void drop_graph(mbk_model *m) {
+    if (m->gexec) (void)hipGraphExecDestroy(m->gexec);
+    if (m->graph) (void)hipGraphDestroy(m->graph);
+    m->gexec = nullptr;
+    m->graph = nullptr;
+    m->node0 = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mbk_last_error(void) { return g_err.c_str(); }
+
+int mbk_create(const mbk_config *cfg, mbk_model **out) {
+    if (!cfg || !out) return fail(MBK_ERR_ARG, "null argument");
+    const mbk_config &c = *cfg;
+    if (c.n_layers <= 0 || c.hidden <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 ||
+        c.intermediate <= 0 || c.vocab <= 0 || c.kv_capacity <= 0)
+        return fail(MBK_ERR_ARG, "every dimension must be positive");
+    if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return fail(MBK_ERR_ARG, "rms_eps and rope_theta must be > 0");
+    if (c.qkv_bias != 0 && c.qkv_bias != 1) return fail(MBK_ERR_ARG, "qkv_bias must be 0 or 1");
+    if (c.head_dim != 16 && c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128)
+        return fail(MBK_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", c.head_dim);
+    if (c.n_heads % c.n_kv_heads != 0) return fail(MBK_ERR_UNSUPPORTED, "n_heads %% n_kv_heads != 0");
+    if (c.n_heads / c.n_kv_heads > kMaxGqa) return fail(MBK_ERR_UNSUPPORTED, "more than %d query heads per KV head", kMaxGqa);
+    const int Q = c.n_heads * c.head_dim;
+    if (c.hidden % 8 || Q % 8 || c.intermediate % 8) return fail(MBK_ERR_UNSUPPORTED, "hidden, heads*head_dim and intermediate must be multiples of 8");
+    if (c.hidden > kMaxVec || Q > kMaxVec || c.intermediate > kMaxVec)
+        return fail(MBK_ERR_UNSUPPORTED, "vectors longer than %d", kMaxVec);
+    if (c.kv_capacity > 8192) return fail(MBK_ERR_UNSUPPORTED, "kv_capacity %d > 8192", c.kv_capacity);
+    if ((int64_t)c.vocab * c.hidden > ((int64_t)1 << 33)) return fail(MBK_ERR_UNSUPPORTED, "embedding too large");
+    mbk_model *m = new mbk_model();
+    m->c = c;
+    *out = m;
+    return MBK_OK;
+}
+
+void mbk_destroy(mbk_model *m) {
+    if (!m) return;
+    drop_graph(m);
+    delete m;
+}
+
+int mbk_num_intervals(const mbk_model *m, int32_t *n) {
+    if (!m || !n) return fail(MBK_ERR_ARG, "null argument");
+    *n = 5 * m->c.n_layers + 1;
+    return MBK_OK;
+}
+
+int mbk_set_debug(mbk_model *m, int32_t spin_limit, int32_t skip_wg, int32_t skip_interval) {
+    if (!m || spin_limit < 0) return fail(MBK_ERR_ARG, "bad debug arguments");
+    m->spin_limit = spin_limit ? spin_limit : (1 << 22);
+    m->skip_wg = skip_wg;
+    m->skip_interval = skip_interval;
+    return MBK_OK;
+}
+
+int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *dst_bytes, void *stream) {
+    if (!m || !dst_bytes) return fail(MBK_ERR_ARG, "null argument");
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    const Plan &P = m->plan;
+    if (!dst) {
+        *dst_bytes = P.total;
+        return MBK_OK;
+    }
+    if (!src) return fail(MBK_ERR_ARG, "null weights");
+    if (*dst_bytes < P.total) return fail(MBK_ERR_SIZE, "packed buffer %zu < %llu bytes", *dst_bytes, (unsigned long long)P.total);
+    if (!aligned(dst, 256)) return fail(MBK_ERR_ARG, "packed buffer not 256-byte aligned");
+    const mbk_config &c = m->c;
+    auto ok16 = [](const void *p) { return p && aligned(p, 16); };
+    if (!ok16(src->embed) || !ok16(src->final_norm)) return fail(MBK_ERR_ARG, "embed/final_norm null or misaligned");
+    if (!src->attn_norm || !src->wq || !src->wk || !src->wv || !src->wo || !src->mlp_norm || !src->wgate ||
+        !src->wup || !src->wdown || (c.qkv_bias && (!src->bq || !src->bk || !src->bv)))
+        return fail(MBK_ERR_ARG, "null per-layer weight array");
+    for (int l = 0; l < c.n_layers; ++l) {
+        const void *ps[] = {src->attn_norm[l], src->wq[l], src->wk[l], src->wv[l], src->wo[l], src->mlp_norm[l],
+                            src->wgate[l], src->wup[l], src->wdown[l]};
+        for (const void *p : ps)
+            if (!ok16(p)) return fail(MBK_ERR_ARG, "layer %d: weight pointer null or not 16-byte aligned", l);
+        if (c.qkv_bias && (!src->bq[l] || !src->bk[l] || !src->bv[l])) return fail(MBK_ERR_ARG, "layer %d: null bias", l);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    drop_graph(m);
+    m->blob = (uint8_t *)dst;
+    const int hd = c.head_dim, Q = c.n_heads * hd, KV = c.n_kv_heads * hd;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const LayerPlan &L = P.layers[l];
+        if ((rc = pack_matrix(m, L.qkv, src->wq[l], src->wk[l], src->wv[l], st))) return rc;
+        if ((rc = pack_matrix(m, L.o, src->wo[l], nullptr, nullptr, st))) return rc;
+        if ((rc = pack_matrix(m, L.gu, src->wgate[l], src->wup[l], nullptr, st))) return rc;
+        if ((rc = pack_matrix(m, L.down, src->wdown[l], nullptr, nullptr, st))) return rc;
+        HIPCHK(hipMemcpyAsync(m->blob + L.attn_norm, src->attn_norm[l], 2u * c.hidden, hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpyAsync(m->blob + L.mlp_norm, src->mlp_norm[l], 2u * c.hidden, hipMemcpyDeviceToDevice, st));
+        if (c.qkv_bias) {
+            HIPCHK(hipMemcpyAsync(m->blob + L.bias, src->bq[l], 2u * Q, hipMemcpyDeviceToDevice, st));
+            HIPCHK(hipMemcpyAsync(m->blob + L.bias + 2u * Q, src->bk[l], 2u * KV, hipMemcpyDeviceToDevice, st));
+            HIPCHK(hipMemcpyAsync(m->blob + L.bias + 2u * (Q + KV), src->bv[l], 2u * KV, hipMemcpyDeviceToDevice, st));
+        }
+    }
+    if ((rc = pack_matrix(m, P.embed, src->embed, nullptr, nullptr, st))) return rc;
+    HIPCHK(hipMemcpyAsync(m->blob + P.final_norm, src->final_norm, 2u * c.hidden, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(m->blob + P.rope, m->rope_host.data(), m->rope_host.size() * 4, hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(m->blob + P.table, P.iv.data(), P.iv.size() * sizeof(Interval), hipMemcpyHostToDevice, st));
+    HIPCHK(hipStreamSynchronize(st));  // host-side sources above must outlive the copies
+    return MBK_OK;
+}
+
+int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_bytes, void *stream) {
+    if (!m || !kv_bytes || !ws_bytes) return fail(MBK_ERR_ARG, "null argument");
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    const mbk_config &c = m->c;
+    const size_t need_kv = (size_t)c.n_layers * 2 * c.n_kv_heads * c.kv_capacity * c.head_dim * 2;
+    const size_t need_ws = m->plan.ws.total;
+    if (!kv || !ws) {
+        *kv_bytes = need_kv;
+        *ws_bytes = need_ws;
+        return MBK_OK;
+    }
+    if (*kv_bytes < need_kv || *ws_bytes < need_ws)
+        return fail(MBK_ERR_SIZE, "KV %zu < %zu or workspace %zu < %zu bytes", *kv_bytes, need_kv, *ws_bytes, need_ws);
+    if (!aligned(kv, 256) || !aligned(ws, 256)) return fail(MBK_ERR_ARG, "KV/workspace not 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    HIPCHK(hipMemsetAsync(kv, 0, need_kv, st));
+    HIPCHK(hipMemsetAsync(ws, 0, need_ws, st));
+    drop_graph(m);
+    m->kv = (uint16_t *)kv;
+    m->ws = (uint8_t *)ws;
+    m->epoch = 0;
+    return MBK_OK;
+}
+
+int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream) {
+    int rc = check_step_args(m, token, pos, argmax);
+    if (rc) return rc;
+    Params p = make_params(m, token, pos, logits, argmax);
+    void *args[] = {&p};
+    HIPCHK(hipLaunchCooperativeKernel((const void *)k_persistent, dim3(m->n_wg), dim3(kThreads), args,
+                                      (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
+    m->epoch += (uint32_t)(p.n_intervals - 1);
+    return MBK_OK;
+}
+
+int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax,
+                             int32_t use_graph, void *stream) {
+    int rc = check_step_args(m, token, pos, argmax);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    Params p = make_params(m, token, pos, logits, argmax);
+    const unsigned lds = (unsigned)m->plan.lds_bytes;
+    if (!use_graph) {
+        for (int i = 0; i < p.n_intervals; ++i)
+            hipLaunchKernelGGL(k_interval, dim3(m->n_wg), dim3(kThreads), lds, st, p, i);
+        HIPCHK(hipGetLastError());
+        return MBK_OK;
+    }
+    if (m->gexec && (m->g_logits != logits || m->g_argmax != argmax)) drop_graph(m);
+    if (!m->gexec) {
+        HIPCHK(hipGraphCreate(&m->graph, 0));
+        hipGraphNode_t prev = nullptr;
+        std::vector<Params> ps(p.n_intervals, p);
+        std::vector<int> idx(p.n_intervals);
+        for (int i = 0; i < p.n_intervals; ++i) {
+            ps[i].step_from_ws = i == 0 ? 0 : 1;
+            idx[i] = i;
+            void *kargs[] = {&ps[i], &idx[i]};
+            hipKernelNodeParams kp{};
+            kp.func = (void *)k_interval;
+            kp.gridDim = dim3(m->n_wg);
+            kp.blockDim = dim3(kThreads);
+            kp.sharedMemBytes = lds;
+            kp.kernelParams = kargs;
+            hipGraphNode_t node;
+            HIPCHK(hipGraphAddKernelNode(&node, m->graph, prev ? &prev : nullptr, prev ? 1 : 0, &kp));
+            if (i == 0) m->node0 = node;
+            prev = node;
+        }
+        HIPCHK(hipGraphInstantiate(&m->gexec, m->graph, nullptr, nullptr, 0));
+        m->g_logits = logits;
+        m->g_argmax = argmax;
+    }
+    int zero = 0;
+    void *kargs[] = {&p, &zero};
+    hipKernelNodeParams kp{};
+    kp.func = (void *)k_interval;
+    kp.gridDim = dim3(m->n_wg);
+    kp.blockDim = dim3(kThreads);
+    kp.sharedMemBytes = lds;
+    kp.kernelParams = kargs;
+    HIPCHK(hipGraphExecKernelNodeSetParams(m->gexec, m->node0, &kp));
+    HIPCHK(hipGraphLaunch(m->gexec, st));
+    return MBK_OK;
+}
+
+int mbk_check(mbk_model *m, void *stream) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+    if (!m->ws) return MBK_OK;
+    uint32_t err = 0;
+    HIPCHK(hipMemcpy(&err, m->ws + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));
+    if (err) return fail(MBK_ERR_TIMEOUT, "a grid-barrier wait expired on the device; re-bind KV/workspace");
+    return MBK_OK;
+}
+
+int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier) {
+    if (!m || !us_per_barrier || n <= 0) return fail(MBK_ERR_ARG, "bad arguments");
+    if (!m->ws || !m->blob) return fail(MBK_ERR_STATE, "workspace not bound");
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t e0, e1;
+    HIPCHK(hipEventCreate(&e0));
+    HIPCHK(hipEventCreate(&e1));
+    float t[2] = {0, 0};
+    const int counts[2] = {0, n};
+    for (int k = 0; k < 2; ++k) {
+        Params p = make_params(m, 0, 0, nullptr, nullptr);
+        int cnt = counts[k];
+        void *args[] = {&p, &cnt};
+        HIPCHK(hipEventRecord(e0, st));
+        HIPCHK(hipLaunchCooperativeKernel((const void *)k_barrier_bench, dim3(m->n_wg), dim3(kThreads), args, 0, st));
+        HIPCHK(hipEventRecord(e1, st));
+        HIPCHK(hipEventSynchronize(e1));
+        HIPCHK(hipEventElapsedTime(&t[k], e0, e1));
+        m->epoch += (uint32_t)cnt;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    *us_per_barrier = (t[1] - t[0]) * 1000.f / (float)n;
+    return MBK_OK;
+}
+
+}  // extern "C"

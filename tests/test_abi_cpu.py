@@ -1,0 +1,87 @@
+"""C ABI checks that need no GPU: exported symbols and host-side validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from persistent_megakernel_decode_wg_amd import build as mbk_build
+    mbk_build.ensure_built()
+    import persistent_megakernel_decode_wg_amd as pkg
+    return pkg.lib()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "mbk.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mbk_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert "mbk_decode_step" in names and "mbk_pack_weights" in names and "mbk_alloc_kv" in names
+    for n in names:
+        assert hasattr(L, n), "libmbk.so does not export %s" % n
+
+
+def _create(cfg):
+    from persistent_megakernel_decode_wg_amd.binding import make_config
+    c = make_config(cfg)
+    h = ctypes.c_void_p()
+    import persistent_megakernel_decode_wg_amd as pkg
+    rc = pkg.lib().mbk_create(ctypes.byref(c), ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(head_dim=48), 4), (dict(n_heads=9, n_kv_heads=2), 4), (dict(n_heads=18, n_kv_heads=2), 4),
+    (dict(hidden=100), 4), (dict(kv_capacity=16384), 4), (dict(intermediate=16384), 4),
+    (dict(n_layers=0), 1), (dict(vocab=-5), 1), (dict(rms_eps=0.0), 1), (dict(qkv_bias=2), 1),
+])
+def test_create_rejects_unsupported_or_bad_shapes(L, change, code):
+    wl = synth.get("tiny-2L-h64-kv32").replace(**change)
+    rc, h = _create(wl)
+    assert rc == code, L.mbk_last_error()
+    assert L.mbk_last_error()
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_create_accepts_every_workload_and_counts_intervals(L, name):
+    wl = synth.get(name)
+    rc, h = _create(wl)
+    assert rc == 0, L.mbk_last_error()
+    n = ctypes.c_int32()
+    assert L.mbk_num_intervals(h, ctypes.byref(n)) == 0
+    assert n.value == 5 * wl.n_layers + 1
+    L.mbk_destroy(h)
+
+
+def test_step_before_pack_is_a_state_error_and_args_are_checked(L):
+    rc, h = _create(synth.get("tiny-2L-h64-kv32"))
+    assert rc == 0
+    am = ctypes.c_int32()
+    assert L.mbk_decode_step(h, 1, 0, None, ctypes.byref(am), None) == 7           # MBK_ERR_STATE
+    assert L.mbk_decode_step(None, 1, 0, None, ctypes.byref(am), None) == 1        # MBK_ERR_ARG
+    assert L.mbk_decode_step_ablation(h, 1, 0, None, ctypes.byref(am), 0, None) == 7
+    assert L.mbk_set_debug(h, -1, 0, 0) == 1
+    assert L.mbk_pack_weights(h, None, None, None, None) == 1
+    L.mbk_destroy(h)
+    L.mbk_destroy(None)
+
+
+def test_no_device_is_reported_as_hip_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, h = _create(synth.get("tiny-2L-h64-kv32"))
+    n = ctypes.c_size_t()
+    assert L.mbk_pack_weights(h, None, None, ctypes.byref(n), None) == 5          # MBK_ERR_HIP
+    L.mbk_destroy(h)

@@ -1,0 +1,120 @@
+"""Parity of the HIP decode step (through the C ABI) with the CPU oracle, on the GPU."""
+import numpy as np
+import pytest
+
+import synth
+
+from gpu_util import LOGIT_TOL, MARGIN, Pair, compare, log, teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return Pair(synth.get("tiny-2L-h64-kv32"))
+
+
+def test_tiny_full_schedule_teacher_forced(tiny):
+    wl = tiny.wl
+    log("tiny: prompt %d + %d greedy steps" % (wl.n_prompt, wl.n_decode))
+    worst = teacher_forced(tiny, synth.decode_schedule(wl), list(synth.prompt_tokens(wl)), label="tiny")
+    log("tiny worst max|dlogit|/std = %.3g" % worst)
+
+
+@pytest.mark.parametrize("mode", ["ablation", "graph"])
+def test_tiny_ablation_is_bitwise_equal(tiny, mode):
+    wl = tiny.wl
+    prompt = list(synth.prompt_tokens(wl))
+    for pos in range(12):
+        tok = prompt[pos % len(prompt)]
+        a, ia = tiny.gpu_step(tok, pos, "mega")
+        b, ib = tiny.gpu_step(tok, pos, mode)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, "pos %d" % pos
+
+
+def test_tiny_rerun_same_position_is_idempotent_and_deterministic(tiny):
+    wl = tiny.wl
+    prompt = list(synth.prompt_tokens(wl))
+    for pos in range(6):
+        tiny.gpu_step(prompt[pos], pos)
+    a, ia = tiny.gpu_step(prompt[5], 5)
+    b, ib = tiny.gpu_step(prompt[5], 5)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib
+
+
+def test_tiny_edge_tokens_and_last_slot():
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = Pair(wl)
+    toks = [0, wl.vocab - 1] + [int(t) for t in synth.tokens(5, "edge", wl.kv_capacity - 2, wl.vocab)]
+    # positions 0 .. capacity-1: the last step fills the final slot
+    teacher_forced(p, list(range(wl.kv_capacity)), toks, check_every=1, label="tiny-edge")
+
+
+def test_tiny_pipelined_previous_token_matches_oracle_greedy():
+    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = Pair(wl)
+    prompt = list(synth.prompt_tokens(wl))
+    tok = None
+    for pos in synth.decode_schedule(wl):
+        t_gpu = prompt[pos] if pos < len(prompt) else MBK_TOKEN_PREV
+        t_ref = prompt[pos] if pos < len(prompt) else tok
+        lg, am = p.gpu_step(t_gpu, pos)
+        lo, ao, _ = p.ref.step(t_ref, pos)
+        rel, margin, ok = compare(lg, am, lo, ao)
+        assert rel <= LOGIT_TOL
+        if am != ao:
+            assert margin <= MARGIN, "free-running greedy diverged at pos %d with margin %.3g" % (pos, margin)
+            break
+        tok = ao
+
+
+def test_zero_projections_closed_form_on_gpu():
+    """W_o = W_down = 0 keeps the residual at E[t]: argmax must be t and logits E (w_f * E_t / rms)."""
+    wl = synth.get("tiny-2L-h64-kv32")
+    W = synth.make_weights(wl)
+    for L in W["layers"]:
+        L["wo"] = np.zeros_like(L["wo"])
+        L["wdown"] = np.zeros_like(L["wdown"])
+    p = Pair(wl, W)
+    for t in [3, 321, 511]:
+        lg, am = p.gpu_step(t, 0)
+        assert am == t
+        E = synth.bf16_to_f32(W["embed"]).astype(np.float64)
+        e = E[t]
+        want = E @ (e / np.sqrt(np.mean(e * e) + wl.rms_eps) * synth.bf16_to_f32(W["final_norm"]))
+        np.testing.assert_allclose(lg, want, rtol=1e-4, atol=1e-4 * np.abs(want).max())
+
+
+def test_smollm135m_kv128_full_schedule():
+    wl = synth.get("smollm135m-kv128")
+    p = Pair(wl)
+    log("smollm135m-kv128: %d steps" % len(synth.decode_schedule(wl)))
+    worst = teacher_forced(p, synth.decode_schedule(wl), list(synth.prompt_tokens(wl)), label="smollm135m")
+    log("smollm135m-kv128 worst max|dlogit|/std = %.3g" % worst)
+
+
+def test_smollm135m_kv4096_prefilled_long_context():
+    wl = synth.get("smollm135m-kv4096")
+    p = Pair(wl, kv_prefix=synth.kv_prefill(wl))
+    positions = synth.decode_schedule(wl)
+    log("smollm135m-kv4096: positions %d..%d" % (positions[0], positions[-1]))
+    # first 8 steps and the final step (which fills the last slot)
+    worst = teacher_forced(p, positions[:8], [synth.first_token(wl)], label="smollm135m-4k")
+    log("smollm135m-kv4096 worst max|dlogit|/std = %.3g" % worst)
+
+
+def test_qwen2_0p5b_bias_kv128():
+    wl = synth.get("qwen2-0.5b-kv128")
+    p = Pair(wl)
+    positions = synth.decode_schedule(wl)
+    worst = teacher_forced(p, positions[:72], list(synth.prompt_tokens(wl)), check_every=4, label="qwen2")
+    log("qwen2-0.5b-kv128 worst max|dlogit|/std = %.3g" % worst)
+
+
+def test_smollm1p7b_kv4096_prefilled():
+    wl = synth.get("smollm1.7b-kv4096")
+    p = Pair(wl, kv_prefix=synth.kv_prefill(wl))
+    positions = synth.decode_schedule(wl)
+    worst = teacher_forced(p, positions[:3], [synth.first_token(wl)], label="smollm1.7b-4k")
+    log("smollm1.7b-kv4096 worst max|dlogit|/std = %.3g" % worst)
