@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Batch-1 decode benchmark of the persistent megakernel on one MI355X.
+
+Workload: the SmolLM-135M-shaped decoder (30 layers, hidden 576, 9/3 heads of
+64, SwiGLU 1536, vocabulary 49152, tied embeddings) with seeded random bf16
+weights and a static 128-slot KV cache: the 64 prompt tokens are stepped at
+positions 0..63 (setup), then greedy steps run at positions 64..127 with the
+token fed back on the device (MBK_TOKEN_PREV), cycling over that range.
+One timed step = one cooperative launch = the whole decode step.
+
+Prints ONE JSON line (rank 0).  `value` is tok/s over the K timed steps.
+`roofline.achieved` = algorithmic bytes per step / mean kernel duration from
+HIP events recorded on the launch stream.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_bytes(wl, pos: int) -> int:
+    """Bytes one step must move: every weight once (tied embedding once), the embedding row,
+    the KV read over 0..pos and the append at pos, the fp32 logits, and the RoPE table row."""
+    kv_pos = wl.n_layers * 2 * wl.n_kv_heads * wl.head_dim * 2
+    return (2 * wl.param_count() + 2 * wl.hidden + (pos + 1) * kv_pos + kv_pos + 4 * wl.vocab + 4 * wl.head_dim)
+
+
+OPS = ["qkv", "attn", "o", "gateup", "down"]
+
+
+def phase_breakdown(dec, wl, positions, logits, am, steps=8, dump=""):
+    """Per-operator means (us) from the device phase timer: inputs = start->inputs loaded (median WG),
+    body = interval start->last WG done, sync = last WG done->first WG starting the next interval."""
+    import numpy as np
+    import torch
+    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV
+    tr = dec.set_phase_trace(True)
+    acc = {}
+    raw = []
+    for i in range(steps):
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+        torch.cuda.synchronize()
+        t = tr.cpu().numpy().astype(np.int64)          # [iv][wg][4], 100 MHz ticks
+        raw.append(t.copy())
+        n_iv = t.shape[0]
+        for iv in range(n_iv):
+            op = "lmhead" if iv == n_iv - 1 else OPS[iv % 5]
+            st, inp, end = t[iv, :, 0], t[iv, :, 1], t[iv, :, 2]
+            body = (end.max() - st.min()) * 0.01
+            has = inp > 0
+            inputs = float(np.median(inp[has] - st[has])) * 0.01 if has.any() else 0.0
+            sync = (t[iv + 1, :, 0].min() - end.max()) * 0.01 if iv + 1 < n_iv else 0.0
+            a = acc.setdefault(op, [0.0, 0.0, 0.0, 0])
+            a[0] += inputs; a[1] += body; a[2] += sync; a[3] += 1
+        tr.zero_()
+    dec.set_phase_trace(False)
+    if dump:
+        np.save(dump, np.stack(raw))
+    out = {op: {"inputs_us": round(a[0] / a[3], 3), "body_us": round(a[1] / a[3], 3), "sync_us": round(a[2] / a[3], 3),
+                "count_per_step": a[3] // steps} for op, a in acc.items()}
+    print("phase breakdown (us, mean per interval): " + json.dumps(out), file=sys.stderr, flush=True)
+    return out
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(q * (len(xs) - 1) + 0.5))]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="smollm135m-kv128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--phase", action="store_true", help="print a per-operator phase-timer breakdown to stderr")
+    ap.add_argument("--phase-dump", default="", help="also save the raw phase-timer arrays (.npy) to this path")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV, Decoder
+    from persistent_megakernel_decode_wg_amd import build as mbk_build
+
+    mbk_build.ensure_built()
+    torch.cuda.set_device(0)
+    wl = synth.get(args.workload)
+    W = synth.make_weights(wl)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    Wt = {"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
+          "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]}
+    dec = Decoder(wl)
+    dec.pack_weights(Wt)
+    dec.alloc_kv()
+    stream = torch.cuda.current_stream()
+    logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    # setup: prefill prompt (or the N(0,1) KV prefix) -> state at the first greedy position
+    if wl.kv_prefill:
+        pre = synth.kv_prefill(wl)
+        dec.kv[:, :, :, :wl.kv_prefill, :] = torch.from_numpy(pre.view(np.int16)).cuda()
+        dec.decode_step(synth.first_token(wl), wl.kv_prefill, logits, am)
+    else:
+        for p, t in enumerate(synth.prompt_tokens(wl)):
+            dec.decode_step(int(t), p, logits, am)
+    dec.check()
+    g0 = wl.greedy_start if not wl.kv_prefill else wl.kv_prefill + 1
+    g1 = wl.greedy_start + wl.n_decode          # exclusive
+    span = g1 - g0
+    positions = lambda i: g0 + (i % span)
+
+    for i in range(args.warmup):
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+    dec.check()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec.check()
+    kern_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    mean_kern_us = sum(kern_us) / K
+    bytes_mean = sum(algorithmic_bytes(wl, positions(i)) for i in range(K)) / K
+    achieved = bytes_mean / (mean_kern_us * 1e-6) / 1e9
+
+    # complete synchronized call (host + GPU), as the pages' leaderboard measures
+    call_us = []
+    for i in range(min(64, K)):
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+        torch.cuda.synchronize()
+        call_us.append((time.perf_counter() - c0) * 1e6)
+
+    extra = {
+        "us_per_token_p10": round(pct(kern_us, 0.1), 2), "us_per_token_p50": round(pct(kern_us, 0.5), 2),
+        "us_per_token_p90": round(pct(kern_us, 0.9), 2), "complete_call_us_p50": round(pct(call_us, 0.5), 2),
+        "bytes_per_token": int(bytes_mean), "intervals_per_step": dec.num_intervals(),
+    }
+    if not args.no_ablation:
+        for mode, use_graph in (("ablation_plain", False), ("ablation_graph", True)):
+            n = min(K, 128)
+            for i in range(8):
+                dec.decode_step_ablation(MBK_TOKEN_PREV, positions(i), logits, am, use_graph=use_graph)
+            torch.cuda.synchronize()
+            s0 = time.perf_counter()
+            for i in range(n):
+                dec.decode_step_ablation(MBK_TOKEN_PREV, positions(i), logits, am, use_graph=use_graph)
+            torch.cuda.synchronize()
+            extra[mode + "_us_per_token"] = round((time.perf_counter() - s0) / n * 1e6, 2)
+        extra["ablation_launches_per_token"] = dec.num_intervals()
+        extra["barrier_us"] = round(dec.barrier_bench(10000), 3)
+        dec.check()
+
+    if args.phase:
+        extra["phase"] = phase_breakdown(dec, wl, positions, logits, am, dump=args.phase_dump)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ref = oracle.Model(wl, W)
+        if wl.kv_prefill:
+            ref.prefill_kv(synth.kv_prefill(wl))
+            tok = synth.first_token(wl)
+            _, tok, _ = ref.step(tok, wl.kv_prefill)
+        else:
+            tok = 0
+            for p, t in enumerate(synth.prompt_tokens(wl)):
+                _, tok, _ = ref.step(int(t), p)
+        n, c0 = 0, time.perf_counter()
+        while time.perf_counter() - c0 < args.cpu_seconds and n < span:
+            _, tok, _ = ref.step(tok, positions(n))
+            n += 1
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d greedy steps at positions %d..%d after the %s setup, fp64-accumulating C oracle" % (
+                   n, g0, g0 + n - 1, "prefill" if wl.kv_prefill else "64-token prompt")}
+
+    out = {
+        "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",
+        "value": round(K / elapsed, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights)",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": wl.n_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "intermediate": wl.intermediate,
+                   "vocab": wl.vocab, "kv_capacity": wl.kv_capacity, "batch": 1,
+                   "positions": "%d-%d" % (g0, g1 - 1), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "us_per_token": round(mean_kern_us, 2),
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    dec.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -127,6 +127,19 @@ int mbk_num_intervals(const mbk_model *m, int32_t *n);
  * interval `skip_interval`, so a test can force the watchdog from the host. */
 int mbk_set_debug(mbk_model *m, int32_t spin_limit, int32_t skip_wg, int32_t skip_interval);
 
+/* Phase timer (the README's per-barrier-interval timer, section "Current
+ * performance"): when buf != NULL, every workgroup of every following launch
+ * writes the device wall clock (100 MHz) into buf as uint64
+ * [interval][workgroup][4]: [0] interval start (after the barrier), [1] inputs
+ * loaded, [2] body done, [3] unused.  buf must hold n_intervals * n_CUs * 32
+ * bytes; NULL switches the timer off. */
+int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
+
+/* Attention split policy: each split of the cached context covers at least
+ * min_positions positions (default 128); contexts up to that length run
+ * unsplit, one workgroup per KV head. */
+int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
+
 /* Message for the last non-zero status returned on this thread. */
 const char *mbk_last_error(void);
 

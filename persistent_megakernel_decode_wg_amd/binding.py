@@ -57,10 +57,13 @@ def lib():
         L.mbk_barrier_bench.argtypes = [vp, i32, vp, P(ctypes.c_float)]
         L.mbk_num_intervals.argtypes = [vp, P(i32)]
         L.mbk_set_debug.argtypes = [vp, i32, i32, i32]
+        L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
+        L.mbk_set_attention_split.argtypes = [vp, i32]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
-                  "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug"):
+                  "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
+                  "mbk_set_attention_split"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,3 +187,18 @@ class Decoder:
 
     def set_debug(self, spin_limit: int = 0, skip_wg: int = -1, skip_interval: int = -1) -> None:
         _chk(lib().mbk_set_debug(self.h, spin_limit, skip_wg, skip_interval))
+
+    def set_attention_split(self, min_positions: int) -> None:
+        _chk(lib().mbk_set_attention_split(self.h, int(min_positions)))
+
+    def set_phase_trace(self, enable: bool = True):
+        """Returns the int64 [intervals][n_wg][4] trace tensor (device wall clock) or None."""
+        import torch
+        if not enable:
+            _chk(lib().mbk_set_phase_trace(self.h, None, 0))
+            return None
+        n_wg = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        buf = torch.zeros((self.num_intervals(), n_wg, 4), dtype=torch.int64, device="cuda")
+        _chk(lib().mbk_set_phase_trace(self.h, ctypes.c_void_p(buf.data_ptr()), buf.numel() * 8))
+        self._trace = buf
+        return buf

@@ -12,6 +12,16 @@
 // memory side.  Weights and the RoPE table never change while a kernel runs
 // and are read with streaming (nt) loads.  A workgroup waits for its own
 // stores (s_waitcnt) before announcing completion.
+//
+// Latency.  At batch 1 an interval moves little data, so its cost is the
+// chain of dependent memory round trips.  While wave 0 waits at the grid
+// barrier, waves 1-3 copy the next interval's weight tiles (or the keys and
+// values already in the cache) into an LDS staging area -- weight streaming
+// across barrier intervals, the MegaBake article's roadmap item ("Checking
+// the 5.5x": prefetch of the next GEMM's weights while a block waits).  After
+// the barrier every input load of the interval is issued at once; tiles that
+// did not fit in LDS stream from HBM through two register buffers used in
+// turn, so the next chunk is in flight while the current one is consumed.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,6 +31,12 @@
 namespace mbk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKvB = 4;     // attention: positions per lane loaded per HBM batch (2 for G >= 5, see kv_batch)
+
+// Positions per lane per attention batch: fewer for large query groups, whose
+// per-head state already takes most of the registers.
+template <int G> constexpr int kv_batch() { return G >= 5 ? 2 : kKvB; }
 
 // Per-launch parameters (kernel argument, passed by value).
 struct Params {
@@ -32,11 +48,13 @@ struct Params {
     float *logits;            // [V] or null
     int32_t *argmax_out;      // device int32
     const float *rope;        // [S][hd/2][2] (cos, sin)
+    uint64_t *trace;          // phase timer [n_intervals][n_wg][4] or null
     MatGeom embed;            // packed tied embedding / LM head
-    uint64_t final_norm_off;
     int32_t n_wg, n_intervals;
     int32_t H, nq, nkv, hd, I, V, S, NL;
-    int32_t max_splits, gqa;
+    int32_t max_splits, gqa, attn_min_chunk;
+    int32_t lds_tab, lds_rope, lds_xs, lds_xres, lds_bias, lds_ys, lds_pf;  // LDS offsets (floats)
+    int32_t pf_bytes;         // size of the LDS staging area
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
     int32_t token, pos;       // token < 0: previous device argmax
     int32_t step_from_ws;     // 1: read token/pos from the workspace (graph replay)
@@ -73,10 +91,8 @@ MBK_DEV uint32_t atom_add(uint32_t *p, uint32_t v) {
 MBK_DEV auto rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
 }
-// 16-byte device-coherent load (sc1) at byte offset off from base.
-MBK_DEV u32x4 ldc16(const void *base, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), off, 0, 16);
-}
+// 16-byte device-coherent load / store (sc1) at byte offset off from base.
+MBK_DEV u32x4 ldc16(const void *base, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), off, 0, 16); }
 MBK_DEV void stc16(void *base, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), off, 0, 16); }
 MBK_DEV void stc_b16(void *base, uint32_t off, uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16((short)v, rsrc(base), off, 0, 16);
@@ -87,6 +103,12 @@ template <class T> MBK_DEV T *ws_ptr(const Params &p, uint64_t off) { return (T 
 MBK_DEV uint32_t ord_key(float f) {
     uint32_t b = __float_as_uint(f);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Phase timer: thread 0 of every workgroup stamps the device wall clock.
+MBK_DEV void stamp(const Params &p, int ivi, int k) {
+    if (p.trace && threadIdx.x == 0 && ivi >= 0)
+        p.trace[((size_t)ivi * p.n_wg + blockIdx.x) * 4 + k] = wall_clock64();
 }
 
 // ---- grid barrier ---------------------------------------------------------------------------------
@@ -105,29 +127,40 @@ MBK_DEV bool spin_until(const uint32_t *p, uint32_t target, int limit) {
     return true;
 }
 
-MBK_DEV bool grid_barrier(const Params &p, uint32_t epoch, int ivi) {
-    __shared__ int ok_s;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+// Arrival: every wave's stores must be complete first (on gfx9 loads and
+// stores share one counter, so this also drains outstanding loads; the next
+// interval's prefetch is therefore issued between arrival and waiting).
+// Returns 1 in thread 0 when this workgroup arrived last in its group.
+MBK_DEV int barrier_arrive(const Params &p, uint32_t epoch, int ivi) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    int last = 0;
     if (threadIdx.x == 0) {
         const int w = blockIdx.x, grp = w % kGroups;
-        const int ngroups = p.n_wg < kGroups ? p.n_wg : kGroups;
         const uint32_t members = (uint32_t)((p.n_wg - grp + kGroups - 1) / kGroups);
-        uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.bar_group + 256u * grp);
-        uint32_t *rel = ws_ptr<uint32_t>(p, p.wl.bar_rel + 256u * grp);
-        uint32_t *glob = ws_ptr<uint32_t>(p, p.wl.bar_global);
-        bool ok;
-        if (w == p.skip_wg && ivi == p.skip_interval) {
-            ok = spin_until(rel, epoch, p.spin_limit);  // never arrives: the group waits in vain
-        } else {
-            uint32_t old = atom_add(cnt, 1u);
+        if (!(w == p.skip_wg && ivi == p.skip_interval)) {  // a skipped arrival leaves the group waiting in vain
+            const uint32_t old = atom_add(ws_ptr<uint32_t>(p, p.wl.bar_group + 256u * grp), 1u);
             if (old == epoch * members - 1u) {
-                atom_add(glob, 1u);
-                ok = spin_until(glob, epoch * (uint32_t)ngroups, p.spin_limit);
-                if (ok) stc_u(rel, epoch);
-            } else {
-                ok = spin_until(rel, epoch, p.spin_limit);
+                atom_add(ws_ptr<uint32_t>(p, p.wl.bar_global), 1u);
+                last = 1;
             }
+        }
+    }
+    return last;
+}
+
+MBK_DEV bool barrier_wait(const Params &p, uint32_t epoch, int last) {
+    __shared__ int ok_s;
+    if (threadIdx.x == 0) {
+        const int grp = blockIdx.x % kGroups;
+        const int ngroups = p.n_wg < kGroups ? p.n_wg : kGroups;
+        uint32_t *rel = ws_ptr<uint32_t>(p, p.wl.bar_rel + 256u * grp);
+        bool ok;
+        if (last) {
+            ok = spin_until(ws_ptr<uint32_t>(p, p.wl.bar_global), epoch * (uint32_t)ngroups, p.spin_limit);
+            if (ok) stc_u(rel, epoch);
+        } else {
+            ok = spin_until(rel, epoch, p.spin_limit);
         }
         if (!ok) stc_u(ws_ptr<uint32_t>(p, p.wl.ctrl), 1u);
         ok_s = ok;
@@ -136,13 +169,56 @@ MBK_DEV bool grid_barrier(const Params &p, uint32_t epoch, int ivi) {
     return ok_s != 0;
 }
 
-// ---- reductions ----------------------------------------------------------------------------------
+MBK_DEV bool grid_barrier(const Params &p, uint32_t epoch, int ivi) {
+    return barrier_wait(p, epoch, barrier_arrive(p, epoch, ivi));
+}
 
-MBK_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+// ---- reductions ----------------------------------------------------------------------------------
+// Butterfly sums over groups of N consecutive lanes.  Steps inside 16 lanes
+// use DPP moves: after the xor-1 and xor-2 steps every quad is uniform, so a
+// half-row mirror (lane i <-> 7-i) pairs quad 0 with quad 1, and after that a
+// row mirror (i <-> 15-i) pairs the two halves of a 16-lane row.  The 16- and
+// 32-lane steps go through the LDS crossbar.
+
+template <int CTRL> MBK_DEV float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int N> MBK_DEV float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if constexpr (N >= 16) v += dpp<0x140>(v);  // row_mirror
+    if constexpr (N >= 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32);
     return v;
 }
+
+MBK_DEV float group_sum_n(float v, int n) {
+    switch (n) {
+        case 1: return v;
+        case 2: return group_sum<2>(v);
+        case 4: return group_sum<4>(v);
+        case 8: return group_sum<8>(v);
+        case 16: return group_sum<16>(v);
+        case 32: return group_sum<32>(v);
+        default: return group_sum<64>(v);
+    }
+}
+
+// Value of the lane `n` positions away (lane ^ n) when every group of n
+// consecutive lanes holds one uniform value (as after group_sum<n>).
+MBK_DEV float group_swap(float v, int n) {
+    switch (n) {
+        case 1: return dpp<0xB1>(v);
+        case 2: return dpp<0x4E>(v);
+        case 4: return dpp<0x141>(v);
+        case 8: return dpp<0x140>(v);
+        default: return __shfl_xor(v, n);
+    }
+}
+
+MBK_DEV float wave_sum(float v) { return group_sum<64>(v); }
 
 // Sum over the workgroup in a fixed order; every thread gets the result.
 MBK_DEV float block_sum(float v, float *red) {
@@ -157,7 +233,7 @@ MBK_DEV float block_sum(float v, float *red) {
     return s;
 }
 
-// ---- input vectors ---------------------------------------------------------------------------------
+// ---- step inputs ---------------------------------------------------------------------------------
 
 MBK_DEV int step_token(const Params &p) {
     int t = p.step_from_ws ? (int)ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 3) : p.token;
@@ -168,128 +244,326 @@ MBK_DEV int step_pos(const Params &p) {
     return p.step_from_ws ? (int)ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 4) : p.pos;
 }
 
-// Element r of the embedding row of `token` (bf16 -> fp32), read from the packed LM head.
-MBK_DEV float embed_elem(const Params &p, int token, int r) {
-    const uint8_t *c = p.blob + row_group_offset(p.embed, token, r >> 3);
-    return bf16f(((const uint16_t *)c)[r & 7]);
+MBK_DEV int first_item(const Params &p, const Interval &iv) {
+    const uint32_t nwg = (uint32_t)p.n_wg;
+    return (int)((blockIdx.x + nwg - (uint32_t)(iv.rot % p.n_wg)) % nwg);
 }
 
-// xs[0..K) <- residual stream (embedding row of `token` for layer 0), optionally
-// RMS-normalised with the bf16 weight at blob offset norm_off.
-MBK_DEV void load_residual(const Params &p, float *xs, float *red, bool from_embed, int token, uint64_t norm_off) {
-    const int K = p.H;
+// Rounds (one tile per wave each) needed to cover the interval's tiles.
+MBK_DEV int gemv_rounds(const Params &p, const Interval &iv) {
+    return (iv.n_items + kWaves * p.n_wg - 1) / (kWaves * p.n_wg);
+}
+
+// ---- input vectors (all loads of an interval issued together) ------------------------------------
+
+// GEMV input vectors live in LDS as bf16 pairs: each 8-element group g is 32
+// bytes, [hi pairs | lo pairs] with hi = bf16(x), lo = bf16(x - hi), so that
+// hi + lo carries ~17 significant bits and the bf16 dot-product instruction
+// (fp32 accumulation) consumes weights and activations without conversions.
+
+MBK_DEV uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+MBK_DEV void split8(const float *v, u32x4 &h, u32x4 &l) {
+    uint16_t hb[8], lb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hb[e] = to_bf16(v[e]);
+        lb[e] = to_bf16(v[e] - bf16f(hb[e]));
+    }
+    h = (u32x4){pack2(hb[0], hb[1]), pack2(hb[2], hb[3]), pack2(hb[4], hb[5]), pack2(hb[6], hb[7])};
+    l = (u32x4){pack2(lb[0], lb[1]), pack2(lb[2], lb[3]), pack2(lb[4], lb[5]), pack2(lb[6], lb[7])};
+}
+
+MBK_DEV void unpack8(const u32x4 &w, float *v) {
+    v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+    v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+}
+
+// xs <- hi/lo pairs of RMSNorm(v) * w, v the residual stream (or the embedding
+// row of `token`), w the bf16 weight at blob offset norm_off.  Pass 1 stores
+// v * w (fp32) and accumulates v^2; pass 2 scales and splits in place.
+MBK_DEV void load_normed(const Params &p, float *xs, float *red, bool from_embed, int token, uint64_t norm_off, int K) {
+    const int ng = K / 8;
     float ss = 0.f;
-    if (from_embed) {
-        for (int g = threadIdx.x; g < K / 8; g += kThreads) {
-            u32x4 w = *(const u32x4 *)(p.blob + row_group_offset(p.embed, token, g));
-            float v[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { xs[g * 8 + e] = v[e]; ss += v[e] * v[e]; }
+#pragma unroll 2
+    for (int g = threadIdx.x; g < ng; g += kThreads) {
+        float v[8], w[8];
+        if (from_embed) {
+            unpack8(*(const u32x4 *)(p.blob + row_group_offset(p.embed, token, g)), v);
+        } else {
+            const u32x4 a = ldc16(p.ws, (uint32_t)(p.wl.x + 32u * g)), b = ldc16(p.ws, (uint32_t)(p.wl.x + 32u * g + 16u));
+            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
         }
-    } else {
-        for (int g = threadIdx.x; g < K / 4; g += kThreads) {
-            u32x4 w = ldc16(p.ws, (uint32_t)(p.wl.x + 16u * g));
-            float v[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+        unpack8(*(const u32x4 *)(p.blob + norm_off + 16u * g), w);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { xs[g * 4 + e] = v[e]; ss += v[e] * v[e]; }
-        }
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        *(float4 *)(xs + 8 * g) = make_float4(v[0] * w[0], v[1] * w[1], v[2] * w[2], v[3] * w[3]);
+        *(float4 *)(xs + 8 * g + 4) = make_float4(v[4] * w[4], v[5] * w[5], v[6] * w[6], v[7] * w[7]);
     }
-    if (norm_off != ~(uint64_t)0) {
-        float tot = block_sum(ss, red);  // contains the barrier that makes xs visible
-        float r = rsqrtf(tot / (float)K + p.eps);
-        const uint16_t *nw = (const uint16_t *)(p.blob + norm_off);
-        for (int k = threadIdx.x; k < K; k += kThreads) xs[k] = xs[k] * r * bf16f(nw[k]);
+    const float r = rsqrtf(block_sum(ss, red) / (float)K + p.eps);
+    for (int g = threadIdx.x; g < ng; g += kThreads) {
+        float v[8];
+        const float4 a = *(const float4 *)(xs + 8 * g), b = *(const float4 *)(xs + 8 * g + 4);
+        v[0] = a.x * r; v[1] = a.y * r; v[2] = a.z * r; v[3] = a.w * r;
+        v[4] = b.x * r; v[5] = b.y * r; v[6] = b.z * r; v[7] = b.w * r;
+        u32x4 h, l;
+        split8(v, h, l);
+        *(u32x4 *)(xs + 8 * g) = h;
+        *(u32x4 *)(xs + 8 * g + 4) = l;
     }
-    __syncthreads();
 }
 
-// xs[0..K) <- fp32 workspace vector at byte offset off.
-MBK_DEV void load_vec(const Params &p, float *xs, uint64_t off, int K) {
-    for (int g = threadIdx.x; g < K / 4; g += kThreads) {
-        u32x4 w = ldc16(p.ws, (uint32_t)(off + 16u * g));
-        *(u32x4 *)(xs + 4 * g) = w;
+// xs <- hi/lo pairs of the fp32 workspace vector at byte offset off.
+MBK_DEV void load_ws_split(const Params &p, float *xs, uint64_t off, int K) {
+#pragma unroll 2
+    for (int g = threadIdx.x; g < K / 8; g += kThreads) {
+        const u32x4 a = ldc16(p.ws, (uint32_t)(off + 32u * g)), b = ldc16(p.ws, (uint32_t)(off + 32u * g + 16u));
+        const float v[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
+                            __uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
+        u32x4 h, l;
+        split8(v, h, l);
+        *(u32x4 *)(xs + 8 * g) = h;
+        *(u32x4 *)(xs + 8 * g + 4) = l;
     }
-    __syncthreads();
 }
 
-// ---- GEMV ------------------------------------------------------------------------------------------
-// Dot products of the RT rows of packed tile t with xs (fp32 in LDS).  Lane l
-// covers row l / L and input groups (l % L) + it * L; the row sum is reduced
-// over its L lanes, so every lane of the row ends up holding it.
-MBK_DEV float gemv_tile(const uint8_t *blob, const MatGeom &g, int64_t t, const float *xs, int lane) {
-    const int L = g.L, IT = g.IT, kl = lane & (L - 1);
+// dst[0..K) <- fp32 workspace vector at byte offset off (coherent loads).
+MBK_DEV void load_ws_vec(const Params &p, float *dst, uint64_t off, int K) {
+#pragma unroll 2
+    for (int g = threadIdx.x; g < K / 4; g += kThreads) *(u32x4 *)(dst + 4 * g) = ldc16(p.ws, (uint32_t)(off + 16u * g));
+}
+
+// dst[0..K) <- embedding row of `token` (fp32).
+MBK_DEV void load_embed_row(const Params &p, float *dst, int token, int K) {
+#pragma unroll 2
+    for (int g = threadIdx.x; g < K / 8; g += kThreads) {
+        float v[8];
+        unpack8(*(const u32x4 *)(p.blob + row_group_offset(p.embed, token, g)), v);
+        *(float4 *)(dst + 8 * g) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(dst + 8 * g + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+// ---- GEMV --------------------------------------------------------------------------------------------
+// A wave owns tiles first + wave*n_wg, + 4*n_wg, ... (round r holds one tile
+// per wave).  The first rounds come from the LDS staging area; the rest are
+// read from HBM in chunks of kCh steps (16-byte loads per lane; steps past IT
+// re-read the last one, so every chunk issues exactly kCh loads and the
+// compiler's in-order load counting keeps the next chunk in flight while the
+// current one is consumed).  Lane l covers row l / L and input groups
+// (l % L) + it * L; the row sum is reduced over its L lanes.  Row sums go to
+// LDS (ys); the operator's epilogue then runs as a short loop over them, so
+// the streaming loop exists once in the kernel's code (the instruction cache
+// is far smaller than the kernel).
+
+constexpr int kCh = 8;
+
+// Rounds of tiles of this interval held in the staging area.
+MBK_DEV int gemv_pf_rounds(const Params &p, const Interval &iv) {
+    const int per_round = kWaves * iv.mat.IT * 1024;
+    const int fit = p.pf_bytes / per_round;
+    return min(fit, gemv_rounds(p, iv));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+MBK_DEV float dot2(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+// a += 8 weights (one 16-byte chunk) times input group xv (hi/lo pairs).
+MBK_DEV void fma16(const u32x4 &w, const float *xv, float *a) {
+    const u32x4 h = *(const u32x4 *)xv, l = *(const u32x4 *)(xv + 4);
+    a[0] = dot2(w.x, h.x, a[0]);
+    a[1] = dot2(w.y, h.y, a[1]);
+    a[2] = dot2(w.z, h.z, a[2]);
+    a[3] = dot2(w.w, h.w, a[3]);
+    a[0] = dot2(w.x, l.x, a[0]);
+    a[1] = dot2(w.y, l.y, a[1]);
+    a[2] = dot2(w.z, l.z, a[2]);
+    a[3] = dot2(w.w, l.w, a[3]);
+}
+
+MBK_DEV void load_chunk(const uint8_t *blob, const MatGeom &g, int64_t t, int c, int lane, u32x4 *w) {
     const uint8_t *base = blob + chunk_offset(g, t, 0, lane);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int it0 = 0; it0 < IT; it0 += 8) {
-        u32x4 w[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (it0 + u < IT) w[u] = ld_stream(base + (size_t)(it0 + u) * 1024u);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (it0 + u < IT) {
-                const float *xv = xs + (kl + (it0 + u) * L) * 8;
-                const float4 xa = *(const float4 *)xv, xb = *(const float4 *)(xv + 4);
-                a0 = fmaf(bf_lo(w[u].x), xa.x, a0);
-                a1 = fmaf(bf_hi(w[u].x), xa.y, a1);
-                a2 = fmaf(bf_lo(w[u].y), xa.z, a2);
-                a3 = fmaf(bf_hi(w[u].y), xa.w, a3);
-                a0 = fmaf(bf_lo(w[u].z), xb.x, a0);
-                a1 = fmaf(bf_hi(w[u].z), xb.y, a1);
-                a2 = fmaf(bf_lo(w[u].w), xb.z, a2);
-                a3 = fmaf(bf_hi(w[u].w), xb.w, a3);
-            }
-        }
-    }
-    float acc = (a0 + a1) + (a2 + a3);
-    for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m);
-    return acc;
-}
-
-// Runs fn(tile, row_sum, lane) for every tile of the interval owned by this
-// workgroup: item i goes to workgroup (i + rot) % n_wg, and the workgroup's
-// items are dealt to its waves in turn.
-template <class Fn>
-MBK_DEV void for_my_tiles(const Params &p, const Interval &iv, const float *xs, Fn &&fn) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nwg = p.n_wg;
-    const int first = (int)((blockIdx.x + (uint32_t)nwg - (uint32_t)(iv.rot % nwg)) % (uint32_t)nwg);
-    for (int64_t t = first + (int64_t)wave * nwg; t < iv.n_items; t += (int64_t)kWaves * nwg) {
-        float y = gemv_tile(p.blob, iv.mat, t, xs, lane);
-        fn(t, y, lane);
+    for (int u = 0; u < kCh; ++u) {
+        const int it = min(c * kCh + u, g.IT - 1);
+        w[u] = ld_stream(base + (size_t)it * 1024u);
     }
 }
 
-// ---- operators -------------------------------------------------------------------------------------
+MBK_DEV void fma_chunk(const MatGeom &g, int c, int kl, const float *xs, const u32x4 *w, float *a) {
+#pragma unroll
+    for (int u = 0; u < kCh; ++u) {
+        const int it = c * kCh + u;
+        if (it < g.IT) fma16(w[u], xs + (kl + it * g.L) * 8, a);
+    }
+}
 
-// Q/K/V projection (+bias), RoPE on query/key pairs, KV append.
-MBK_DEV void op_qkv(const Params &p, const Interval &iv, float *xs, float *red) {
-    const int token = iv.layer == 0 ? step_token(p) : 0, pos = step_pos(p);
-    load_residual(p, xs, red, iv.layer == 0, token, iv.norm_off);
-    const int hd = p.hd, Q = p.nq * hd, KVr = p.nkv * hd, half = hd / 2;
+// Stores the row sum of the wave's k-th tile: ys[(k * kWaves + wave) * RT + row].
+MBK_DEV void finish_row(float *a, const MatGeom &g, int k, int lane, int wave, float *ys) {
+    const float acc = group_sum_n((a[0] + a[1]) + (a[2] + a[3]), g.L);
+    a[0] = a[1] = a[2] = a[3] = 0.f;
+    if ((lane & (g.L - 1)) == 0) ys[((k * kWaves + wave) << g.lrt) + (lane >> (6 - g.lrt))] = acc;
+}
+
+// Copies this workgroup's first rounds of tiles into the staging area, using
+// threads [tid, nthreads) of the workgroup.
+MBK_DEV void stage_gemv(const Params &p, const Interval &iv, uint8_t *pf, int tid, int nthreads) {
     const MatGeom &g = iv.mat;
-    const uint16_t *bias = iv.bias_off != ~(uint64_t)0 ? (const uint16_t *)(p.blob + iv.bias_off) : nullptr;
-    const float2 *rope = (const float2 *)p.rope + (size_t)pos * half;
+    const int npf = gemv_pf_rounds(p, iv);
+    const int first = first_item(p, iv);
+    const int per_slot = g.IT * 64;
+    const int units = npf * kWaves * per_slot;
+    constexpr int U = 8;
+    for (int u0 = tid; u0 < units; u0 += U * nthreads) {
+        u32x4 v[U];
+        bool ok[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = u0 + k * nthreads;
+            const int slot = u / per_slot, rem = u % per_slot;
+            const int64_t t = first + (int64_t)slot * p.n_wg;  // slot = round * kWaves + wave
+            ok[k] = u < units && t < iv.n_items;
+            if (ok[k]) v[k] = ld_stream(p.blob + chunk_offset(g, t, rem / 64, rem % 64));
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (ok[k]) *(u32x4 *)(pf + (size_t)(u0 + k * nthreads) * 16u) = v[k];
+    }
+}
+
+// Row sums of all this workgroup's tiles of the interval into ys.
+// A (kCh registers) holds chunk 0 of the wave's first HBM tile when
+// hbm_first < n_items (issued by gemv_start before the input loads).
+MBK_DEV void gemv_rows(const Params &p, const Interval &iv, const float *xs, const uint8_t *pf, u32x4 *A, float *ys) {
+    const MatGeom &g = iv.mat;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kl = lane & (g.L - 1);
+    const int first = first_item(p, iv);
+    const int npf = gemv_pf_rounds(p, iv);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < npf; ++r) {
+        if (first + (int64_t)(wave + kWaves * r) * p.n_wg >= iv.n_items) break;
+        const u32x4 *w = (const u32x4 *)(pf + (size_t)(r * kWaves + wave) * g.IT * 1024u) + lane;
+        for (int it0 = 0; it0 < g.IT; it0 += kCh) {
+#pragma unroll
+            for (int u = 0; u < kCh; ++u)
+                if (it0 + u < g.IT) fma16(w[(it0 + u) * 64], xs + (kl + (it0 + u) * g.L) * 8, a);
+        }
+        finish_row(a, g, r, lane, wave, ys);
+    }
+    int k = npf;
+    int64_t t = first + (int64_t)(wave + kWaves * k) * p.n_wg;
+    if (t >= iv.n_items) return;
+    const int64_t T = (int64_t)kWaves * p.n_wg;
+    const int nch = (g.IT + kCh - 1) / kCh;
+    u32x4 B[kCh];
+    int c = 0;
+    for (;;) {
+        int64_t tn = t;
+        int cn = c + 1;
+        if (cn == nch) { cn = 0; tn += T; }
+        bool more = tn < iv.n_items;
+        load_chunk(p.blob, g, more ? tn : t, more ? cn : c, lane, B);
+        fma_chunk(g, c, kl, xs, A, a);
+        if (c == nch - 1) finish_row(a, g, k++, lane, wave, ys);
+        if (!more) return;
+        t = tn;
+        c = cn;
+        tn = t;
+        cn = c + 1;
+        if (cn == nch) { cn = 0; tn += T; }
+        more = tn < iv.n_items;
+        load_chunk(p.blob, g, more ? tn : t, more ? cn : c, lane, A);
+        fma_chunk(g, c, kl, xs, B, a);
+        if (c == nch - 1) finish_row(a, g, k++, lane, wave, ys);
+        if (!more) return;
+        t = tn;
+        c = cn;
+    }
+}
+
+// Issues chunk 0 of this wave's first HBM tile into A.
+MBK_DEV void gemv_start(const Params &p, const Interval &iv, u32x4 *A) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = first_item(p, iv) + (int64_t)(wave + kWaves * gemv_pf_rounds(p, iv)) * p.n_wg;
+    if (t < iv.n_items) load_chunk(p.blob, iv.mat, t, 0, lane, A);
+}
+
+// Packed row of local row index i (ys index), or -1 if that slot holds no row.
+MBK_DEV int local_row(const Params &p, const Interval &iv, int i) {
+    const MatGeom &g = iv.mat;
+    const int slot = i >> g.lrt;  // (round * kWaves + wave)
+    const int64_t t = first_item(p, iv) + (int64_t)slot * p.n_wg;
+    if (t >= iv.n_items) return -1;
+    const int64_t r = (t << g.lrt) + (i & (g.RT - 1));
+    return r < g.rows ? (int)r : -1;
+}
+
+MBK_DEV int local_rows(const Params &p, const Interval &iv) { return gemv_rounds(p, iv) * kWaves * iv.mat.RT; }
+
+// ---- GEMV operators ------------------------------------------------------------------------------------
+
+MBK_DEV uint8_t *staging(const Params &p, float *lds) { return (uint8_t *)(lds + p.lds_pf); }
+
+// The interval's input vector into xs (and the residual stream into xres).
+MBK_DEV void gemv_inputs(const Params &p, const Interval &iv, float *lds, float *red) {
+    float *xs = lds + p.lds_xs, *xres = lds + p.lds_xres;
+    switch (iv.op) {
+        case OP_QKV: {
+            if (iv.bias_off != ~(uint64_t)0) {
+                const uint16_t *b = (const uint16_t *)(p.blob + iv.bias_off);
+                float *bias = lds + p.lds_bias;
+                for (int i = threadIdx.x; i < (p.nq + 2 * p.nkv) * p.hd; i += kThreads) bias[i] = bf16f(b[i]);
+            }
+            load_normed(p, xs, red, iv.layer == 0, iv.layer == 0 ? step_token(p) : 0, iv.norm_off, p.H);
+            break;
+        }
+        case OP_O:
+            load_ws_split(p, xs, p.wl.o, p.nq * p.hd);
+            if (iv.layer == 0) load_embed_row(p, xres, step_token(p), p.H);
+            else load_ws_vec(p, xres, p.wl.x, p.H);
+            break;
+        case OP_DOWN:
+            load_ws_split(p, xs, p.wl.a, p.I);
+            load_ws_vec(p, xres, p.wl.x, p.H);
+            break;
+        default:  // gate/up and LM head: RMS-normalised residual stream
+            load_normed(p, xs, red, false, 0, iv.norm_off, p.H);
+            break;
+    }
+    __syncthreads();
+}
+
+// Q/K/V: bias, RoPE on query/key pairs, query to the workspace, key/value
+// appended to the cache at slot pos.
+MBK_DEV void epi_qkv(const Params &p, const Interval &iv, const float *lds, const float *ys) {
+    const int pos = step_pos(p), hd = p.hd, Q = p.nq * hd, KVr = p.nkv * hd, half = hd / 2;
+    const bool has_bias = iv.bias_off != ~(uint64_t)0;
+    const float *bias = lds + p.lds_bias;
+    const float2 *rope = (const float2 *)(lds + p.lds_rope);
     float *q = ws_ptr<float>(p, p.wl.q);
     uint16_t *kc = p.kv + ((size_t)iv.layer * 2 + 0) * p.nkv * p.S * hd;
     uint16_t *vc = p.kv + ((size_t)iv.layer * 2 + 1) * p.nkv * p.S * hd;
-    for_my_tiles(p, iv, xs, [&](int64_t t, float y, int lane) {
-        const float partner = __shfl_xor(y, g.L);
-        if ((lane & (g.L - 1)) != 0) return;
-        const int rr = lane / g.L, prow = (int)(t * g.RT) + rr;
-        if (prow >= g.rows) return;
-        RowSrc s = packed_row_source(MAT_QKV, prow, hd, Q, KVr);
-        if (s.which == 2) {  // value row: its own epilogue
-            float v = y + (bias ? bf16f(bias[Q + KVr + s.row]) : 0.f);
+    const int n = local_rows(p, iv);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int prow = local_row(p, iv, i);
+        if (prow < 0) continue;
+        const RowSrc s = packed_row_source(MAT_QKV, prow, hd, Q, KVr);
+        if (s.which == 2) {
+            const float v = ys[i] + (has_bias ? bias[Q + KVr + s.row] : 0.f);
             const int j = s.row / hd, d = s.row % hd;
             stc_b16(vc, (uint32_t)((((size_t)j * p.S + pos) * hd + d) * 2u), to_bf16(v));
-            return;
+            continue;
         }
-        if (rr & 1) return;  // odd rows are the partner of the pair handled below
+        if (prow & 1) continue;  // the odd row is the partner of this pair
         const int boff = s.which == 0 ? 0 : Q;
         const int h = s.row / hd, m = s.row % hd;  // m < hd/2
-        float u = y, w = partner;
-        if (bias) { u += bf16f(bias[boff + s.row]); w += bf16f(bias[boff + s.row + half]); }
+        float u = ys[i], w = ys[i + 1];
+        if (has_bias) { u += bias[boff + s.row]; w += bias[boff + s.row + half]; }
         const float2 cs = rope[m];
         const float r0 = u * cs.x - w * cs.y, r1 = w * cs.x + u * cs.y;
         if (s.which == 0) {
@@ -300,70 +574,46 @@ MBK_DEV void op_qkv(const Params &p, const Interval &iv, float *xs, float *red) 
             stc_b16(kc, (uint32_t)((base + m) * 2u), to_bf16(r0));
             stc_b16(kc, (uint32_t)((base + m + half) * 2u), to_bf16(r1));
         }
-    });
+    }
 }
 
-// x += W_o o (residual add in the epilogue).
-MBK_DEV void op_o(const Params &p, const Interval &iv, float *xs) {
-    load_vec(p, xs, p.wl.o, p.nq * p.hd);
-    const int token = iv.layer == 0 ? step_token(p) : 0;
+// x[r] = residual[r] + y[r] (output and down projections).
+MBK_DEV void epi_residual(const Params &p, const Interval &iv, const float *lds, const float *ys) {
+    const float *xres = lds + p.lds_xres;
     float *x = ws_ptr<float>(p, p.wl.x);
-    const MatGeom &g = iv.mat;
-    const bool first = iv.layer == 0;
-    for_my_tiles(p, iv, xs, [&](int64_t t, float y, int lane) {
-        if ((lane & (g.L - 1)) != 0) return;
-        const int r = (int)(t * g.RT) + lane / g.L;
-        if (r >= g.rows) return;
-        const float xin = first ? embed_elem(p, token, r) : ldc(x + r);
-        stc(x + r, xin + y);
-    });
+    const int n = local_rows(p, iv);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int r = local_row(p, iv, i);
+        if (r >= 0) stc(x + r, xres[r] + ys[i]);
+    }
 }
 
-// a = silu(W_gate xn) * (W_up xn), xn = RMSNorm(x).
-MBK_DEV void op_gateup(const Params &p, const Interval &iv, float *xs, float *red) {
-    load_residual(p, xs, red, false, 0, iv.norm_off);
+// a = silu(gate) * up over the interleaved gate/up rows.
+MBK_DEV void epi_swiglu(const Params &p, const Interval &iv, const float *ys) {
     float *a = ws_ptr<float>(p, p.wl.a);
-    const MatGeom &g = iv.mat;
-    for_my_tiles(p, iv, xs, [&](int64_t t, float y, int lane) {
-        const float up = __shfl_xor(y, g.L);
-        if ((lane & (g.L - 1)) != 0) return;
-        const int rr = lane / g.L, prow = (int)(t * g.RT) + rr;
-        if ((rr & 1) || prow >= g.rows) return;
-        const float gt = y;
-        stc(a + (prow >> 1), gt / (1.f + __expf(-gt)) * up);
-    });
+    const int n = local_rows(p, iv);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int r = local_row(p, iv, i);
+        if (r < 0 || (r & 1)) continue;
+        const float g = ys[i];
+        stc(a + (r >> 1), __fdividef(g, 1.f + __expf(-g)) * ys[i + 1]);
+    }
 }
 
-// x += W_down a.
-MBK_DEV void op_down(const Params &p, const Interval &iv, float *xs) {
-    load_vec(p, xs, p.wl.a, p.I);
-    float *x = ws_ptr<float>(p, p.wl.x);
-    const MatGeom &g = iv.mat;
-    for_my_tiles(p, iv, xs, [&](int64_t t, float y, int lane) {
-        if ((lane & (g.L - 1)) != 0) return;
-        const int r = (int)(t * g.RT) + lane / g.L;
-        if (r >= g.rows) return;
-        stc(x + r, ldc(x + r) + y);
-    });
-}
-
-// logits = E RMSNorm(x); greedy argmax through one 64-bit atomic max per
-// workgroup; the last workgroup to finish publishes the index.
-MBK_DEV void op_lmhead(const Params &p, const Interval &iv, float *xs, float *red) {
-    load_residual(p, xs, red, false, 0, iv.norm_off);
-    const MatGeom &g = iv.mat;
+// Logits out; greedy argmax through one 64-bit atomic max per workgroup, the
+// last workgroup to finish publishes the index.
+MBK_DEV void epi_lmhead(const Params &p, const Interval &iv, const float *ys) {
     uint64_t best = 0;
-    for_my_tiles(p, iv, xs, [&](int64_t t, float y, int lane) {
-        if ((lane & (g.L - 1)) != 0) return;
-        const int r = (int)(t * g.RT) + lane / g.L;
-        if (r >= g.rows) return;
-        if (p.logits) p.logits[r] = y;
-        const uint64_t key = ((uint64_t)ord_key(y) << 32) | (uint64_t)(0xffffffffu - (uint32_t)r);
+    const int n = local_rows(p, iv);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int r = local_row(p, iv, i);
+        if (r < 0) continue;
+        if (p.logits) p.logits[r] = ys[i];
+        const uint64_t key = ((uint64_t)ord_key(ys[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)r);
         best = key > best ? key : best;
-    });
-    // workgroup max
+    }
     for (int m = 1; m < 64; m <<= 1) {
-        uint64_t o = ((uint64_t)__shfl_xor((uint32_t)(best >> 32), m) << 32) | __shfl_xor((uint32_t)best, m);
+        const uint64_t o = ((uint64_t)__shfl_xor((uint32_t)(best >> 32), m) << 32) | __shfl_xor((uint32_t)best, m);
         best = o > best ? o : best;
     }
     __shared__ uint64_t wbest[kWaves];
@@ -386,14 +636,54 @@ MBK_DEV void op_lmhead(const Params &p, const Interval &iv, float *xs, float *re
     }
 }
 
+// One GEMV interval: first HBM chunk, inputs, streamed row sums, epilogue.
+MBK_DEV void op_gemv(const Params &p, const Interval &iv, int ivi, float *lds, float *red) {
+    u32x4 A[kCh];
+    gemv_start(p, iv, A);
+    gemv_inputs(p, iv, lds, red);
+    stamp(p, ivi, 1);
+    float *ys = lds + p.lds_ys;
+    gemv_rows(p, iv, lds + p.lds_xs, staging(p, lds), A, ys);
+    __syncthreads();
+    switch (iv.op) {
+        case OP_QKV: epi_qkv(p, iv, lds, ys); break;
+        case OP_O:
+        case OP_DOWN: epi_residual(p, iv, lds, ys); break;
+        case OP_GATEUP: epi_swiglu(p, iv, ys); break;
+        default: epi_lmhead(p, iv, ys); break;
+    }
+}
+
 // ---- attention ---------------------------------------------------------------------------------------
 // Decode attention for KV head j over cached positions [t0, t1), the G query
 // heads of the group packed together so each key and value is read once
 // (README mirror, "Current status": flash decoding, query heads sharing a KV
 // head packed at long context).  LP = hd/8 lanes share one position; a wave
-// covers 64/LP positions per step.  Online softmax per lane group, then a
-// log-sum-exp merge across lane groups (shuffles) and across waves (LDS).
-// Result: per head (m, l, acc[hd]) in LDS `out` ([G][hd + 4] floats).
+// covers 64/LP positions per step and the workgroup 4x that.  Positions
+// before the current one that fit are staged in LDS before the barrier; the
+// rest (always including the slot written this step) come from memory in
+// batches through two register buffers.  Online softmax per lane group, then
+// a log-sum-exp merge across lane groups (shuffles) and across waves (LDS).
+// Result: per head (m, l, acc[hd]) in `out`.
+
+struct Split { int nsplit, t0, t1; };
+
+MBK_DEV Split split_range(const Params &p, int s, int pos) {
+    const int Lc = pos + 1;
+    int chunk = (Lc + p.max_splits - 1) / p.max_splits;
+    if (chunk < p.attn_min_chunk) chunk = p.attn_min_chunk;
+    Split r;
+    r.nsplit = (Lc + chunk - 1) / chunk;
+    r.t0 = s * chunk;
+    r.t1 = min(Lc, r.t0 + chunk);
+    return r;
+}
+
+// End of the staged range [t0, end): positions before `pos` that fit.
+MBK_DEV int attn_stage_end(const Params &p, const Split &sp, int pos) {
+    const int cap = p.pf_bytes / (4 * p.hd);
+    return max(sp.t0, min(min(sp.t1, pos), sp.t0 + cap));
+}
 
 MBK_DEV void lse_merge(float &m, float &l, float *acc, float m2, float l2, const float *acc2, int n) {
     const float mn = fmaxf(m, m2);
@@ -404,91 +694,175 @@ MBK_DEV void lse_merge(float &m, float &l, float *acc, float m2, float l2, const
     m = mn;
 }
 
+MBK_DEV const uint16_t *kv_block(const Params &p, int layer, int which, int j) {
+    return p.kv + (((size_t)layer * 2 + which) * p.nkv + j) * p.S * p.hd;
+}
+
+// Copies the staged positions of this workgroup's first attention item to LDS
+// (K rows then V rows, hd bf16 each), using threads [tid, nthreads).
+MBK_DEV void stage_attn(const Params &p, const Interval &iv, uint8_t *pf, int tid, int nthreads) {
+    const int item = first_item(p, iv);
+    if (item >= iv.n_items) return;
+    const int pos = step_pos(p), j = item / p.max_splits, s = item % p.max_splits;
+    const Split sp = split_range(p, s, pos);
+    if (s >= sp.nsplit) return;
+    const int npos = attn_stage_end(p, sp, pos) - sp.t0, row16 = p.hd / 8;
+    const int half_units = npos * row16, units = 2 * half_units;
+    const uint16_t *Kb = kv_block(p, iv.layer, 0, j), *Vb = kv_block(p, iv.layer, 1, j);
+    constexpr int U = 8;
+    for (int u0 = tid; u0 < units; u0 += U * nthreads) {
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = u0 + k * nthreads;
+            if (u < units) {
+                const int which = u >= half_units, rem = u - which * half_units;
+                v[k] = ldc16(which ? Vb : Kb, (uint32_t)((size_t)(sp.t0 + rem / row16) * p.hd * 2 + (rem % row16) * 16));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (u0 + k * nthreads < units) *(u32x4 *)(pf + (size_t)(u0 + k * nthreads) * 16u) = v[k];
+    }
+}
+
+
+
+// Attention over positions [t0, t1) for the G query heads of KV head j.
+// Lane (slot, dl) handles positions t0 + wave*PPW + slot + i*4*PPW and head
+// dims dl*8..dl*8+7.  Positions come in blocks of KB steps; per block each
+// lane rescales its running (m, l, acc) once, so a position costs one
+// exponential per head.  At the end every lane rescales to the workgroup-wide
+// maximum of each head, so slots and waves combine by plain sums in LDS.
+// Result: per head {M, L, acc[hd]} in out ([G][hd + 4], acc unnormalised).
 template <int G>
-MBK_DEV void attend_range(const Params &p, int layer, int j, int t0, int t1, float *out) {
-    const int hd = p.hd, LP = hd / 8, PPW = 64 / LP;
+MBK_DEV void attend_range(const Params &p, int layer, int j, const Split &sp, int pos, bool staged, const uint8_t *pf,
+                          float *out) {
+    constexpr int KB = kv_batch<G>();
+    const int hd = p.hd, LP = hd / 8, PPW = 64 / LP, per_it = kWaves * PPW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane / LP, dl = lane % LP;
-    const float *q = ws_ptr<float>(p, p.wl.q);
+    const int dl = lane % LP, slot = lane / LP;
+    const int t0 = sp.t0, t1 = sp.t1;
+    const int tend = staged ? attn_stage_end(p, sp, pos) : t0;  // [t0, tend) is in LDS
+    const int npos = tend - t0;
+    const uint16_t *Kb = kv_block(p, layer, 0, j), *Vb = kv_block(p, layer, 1, j);
     float qf[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        u32x4 a = ldc16(p.ws, (uint32_t)(p.wl.q + ((size_t)(j * G + h) * hd + dl * 8) * 4u));
-        u32x4 b = ldc16(p.ws, (uint32_t)(p.wl.q + ((size_t)(j * G + h) * hd + dl * 8 + 4) * 4u));
+        const uint32_t qo = (uint32_t)(p.wl.q + ((size_t)(j * G + h) * hd + dl * 8) * 4u);
+        const u32x4 a = ldc16(p.ws, qo), b = ldc16(p.ws, qo + 16u);
         qf[h][0] = __uint_as_float(a.x) * p.scale; qf[h][1] = __uint_as_float(a.y) * p.scale;
         qf[h][2] = __uint_as_float(a.z) * p.scale; qf[h][3] = __uint_as_float(a.w) * p.scale;
         qf[h][4] = __uint_as_float(b.x) * p.scale; qf[h][5] = __uint_as_float(b.y) * p.scale;
         qf[h][6] = __uint_as_float(b.z) * p.scale; qf[h][7] = __uint_as_float(b.w) * p.scale;
     }
-    (void)q;
     float m[G], l[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY; l[h] = 0.f;
+        m[h] = -INFINITY;
+        l[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
-    const uint16_t *Kb = p.kv + (((size_t)layer * 2 + 0) * p.nkv + j) * p.S * hd;
-    const uint16_t *Vb = p.kv + (((size_t)layer * 2 + 1) * p.nkv + j) * p.S * hd;
-    for (int base = t0 + wave * PPW; base < t1; base += kWaves * PPW) {
-        const int t = base + slot;
-        const bool valid = t < t1;
-        u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-        if (valid) {
-            kw = ldc16(Kb, (uint32_t)(((size_t)t * hd + dl * 8) * 2u));
-            vw = ldc16(Vb, (uint32_t)(((size_t)t * hd + dl * 8) * 2u));
+    const int n_it = (t1 - t0 + per_it - 1) / per_it;
+    for (int b = 0; b < n_it; b += KB) {
+        u32x4 kw[KB], vw[KB];
+        bool val[KB];
+        // staged positions from LDS
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int t = t0 + wave * PPW + slot + (b + u) * per_it;
+            val[u] = t < t1;
+            const int q = t < tend ? t - t0 : 0;
+            kw[u] = npos > 0 ? *(const u32x4 *)(pf + ((size_t)q * hd + dl * 8) * 2u) : (u32x4){0u, 0u, 0u, 0u};
+            vw[u] = npos > 0 ? *(const u32x4 *)(pf + ((size_t)(npos + q) * hd + dl * 8) * 2u) : (u32x4){0u, 0u, 0u, 0u};
         }
-        const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y), bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
-        const float vf[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y), bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+        // the rest (always including the slot appended this step) from memory
+        if (t0 + wave * PPW + PPW - 1 + (b + KB - 1) * per_it >= tend) {
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                const int t = t0 + wave * PPW + slot + (b + u) * per_it;
+                if (t >= tend && t < t1) {
+                    const uint32_t off = (uint32_t)(((size_t)t * hd + dl * 8) * 2u);
+                    kw[u] = ldc16(Kb, off);
+                    vw[u] = ldc16(Vb, off);
+                }
+            }
+        }
+        float sc[KB][G];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            float kf[8];
+            unpack8(kw[u], kf);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
+                sc[u][h] = val[u] ? group_sum_n(d, LP) : -INFINITY;
+            }
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float d = 0.f;
+            float bm = sc[0][h];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
-            for (int msk = 1; msk < LP; msk <<= 1) d += __shfl_xor(d, msk);
-            if (valid) {
-                const float mn = fmaxf(m[h], d);
-                const float c = __expf(m[h] - mn), pw = __expf(d - mn);
-                l[h] = l[h] * c + pw;
+            for (int u = 1; u < KB; ++u) bm = fmaxf(bm, sc[u][h]);
+            const float mn = fmaxf(m[h], bm);
+            if (mn != -INFINITY && mn != m[h]) {
+                const float c = __expf(m[h] - mn);
+                l[h] *= c;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw, vf[e], acc[h][e] * c);
+                for (int e = 0; e < 8; ++e) acc[h][e] *= c;
                 m[h] = mn;
             }
         }
-    }
-    // merge the position slots of this wave
-    for (int msk = LP; msk < 64; msk <<= 1) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float a2[8];
-            const float m2 = __shfl_xor(m[h], msk), l2 = __shfl_xor(l[h], msk);
+        for (int u = 0; u < KB; ++u) {
+            float vf[8];
+            unpack8(vw[u], vf);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[h][e], msk);
-            lse_merge(m[h], l[h], acc[h], m2, l2, a2, 8);
+            for (int h = 0; h < G; ++h) {
+                const float pw = val[u] ? __expf(sc[u][h] - m[h]) : 0.f;
+                l[h] += pw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw, vf[e], acc[h][e]);
+            }
         }
     }
-    // merge the waves through LDS: scratch [wave][G][hd + 4]
-    float *scr = out + G * (hd + 4);
+    // workgroup-wide maximum per head: slots of the wave, then waves (LDS)
     const int stride = hd + 4;
-    if (slot == 0) {
+    float *wmax = out + G * stride;                      // [kWaves][G]
+    float *part = wmax + kWaves * G;                     // [kWaves * PPW][G][stride]
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float *r = scr + ((size_t)wave * G + h) * stride;
-            if (dl == 0) { r[0] = m[h]; r[1] = l[h]; }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r[4 + dl * 8 + e] = acc[h][e];
-        }
+    for (int h = 0; h < G; ++h) {
+        float mm = m[h];
+        for (int msk = LP; msk < 64; msk <<= 1) mm = fmaxf(mm, __shfl_xor(mm, msk));
+        if (lane == 0) wmax[wave * G + h] = mm;
     }
     __syncthreads();
+    const int contrib = wave * PPW + slot;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float M = wmax[h];
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w * G + h]);
+        const float f = m[h] == -INFINITY ? 0.f : __expf(m[h] - M);
+        float *r = part + ((size_t)contrib * G + h) * stride;
+        if (dl == 0) { r[0] = M; r[1] = l[h] * f; }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[4 + dl * 8 + e] = acc[h][e] * f;
+    }
+    __syncthreads();
+    const int nc = kWaves * PPW;
     for (int idx = threadIdx.x; idx < G * hd; idx += kThreads) {
         const int h = idx / hd, e = idx % hd;
-        float mm = -INFINITY, ll = 0.f, aa = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float *r = scr + ((size_t)w * G + h) * stride;
-            lse_merge(mm, ll, &aa, r[0], r[1], &r[4 + e], 1);
+        float ll = 0.f, aa = 0.f;
+        for (int c = 0; c < nc; ++c) {
+            const float *r = part + ((size_t)c * G + h) * stride;
+            ll += r[1];
+            aa += r[4 + e];
         }
         float *o = out + (size_t)h * stride;
-        if (e == 0) { o[0] = mm; o[1] = ll; }
+        if (e == 0) { o[0] = part[h * stride]; o[1] = ll; }
         o[4 + e] = aa;
     }
     __syncthreads();
@@ -499,17 +873,14 @@ MBK_DEV void attend_range(const Params &p, int layer, int j, int t0, int t1, flo
 // the last split to arrive (one atomic per split) merges all partials in
 // split order, so the result does not depend on arrival order.
 template <int G>
-MBK_DEV void attention_item(const Params &p, int layer, int j, int s, float *lds) {
-    const int pos = step_pos(p), Lc = pos + 1, hd = p.hd, stride = hd + 4;
-    int chunk = (Lc + p.max_splits - 1) / p.max_splits;
-    if (chunk < kAttnMinChunk) chunk = kAttnMinChunk;
-    const int nsplit = (Lc + chunk - 1) / chunk;
-    if (s >= nsplit) return;
-    const int t0 = s * chunk, t1 = min(Lc, t0 + chunk);
-    float *res = lds;  // [G][stride]
-    attend_range<G>(p, layer, j, t0, t1, res);
+MBK_DEV void attention_item(const Params &p, int layer, int j, int s, bool staged, float *lds) {
+    const int pos = step_pos(p), hd = p.hd, stride = hd + 4;
+    const Split sp = split_range(p, s, pos);
+    if (s >= sp.nsplit) return;
+    float *res = lds + p.lds_xs;  // [G][stride] + scratch
+    attend_range<G>(p, layer, j, sp, pos, staged, staging(p, lds), res);
     float *o = ws_ptr<float>(p, p.wl.o);
-    if (nsplit == 1) {
+    if (sp.nsplit == 1) {
         for (int idx = threadIdx.x; idx < G * hd; idx += kThreads) {
             const int h = idx / hd, e = idx % hd;
             const float *r = res + (size_t)h * stride;
@@ -526,23 +897,23 @@ MBK_DEV void attention_item(const Params &p, int layer, int j, int s, float *lds
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.merge_cnt + 256u * j);
-        const bool last = atom_add(cnt, 1u) == (uint32_t)nsplit - 1u;
+        const bool last = atom_add(cnt, 1u) == (uint32_t)sp.nsplit - 1u;
         if (last) stc_u(cnt, 0u);
         last_s = last;
     }
     __syncthreads();
     if (!last_s) return;
     // load every partial of head group j into LDS, then merge in split order
-    float *all = lds;  // [nsplit][G][stride]
+    float *all = res;  // [nsplit][G][stride]
     const uint64_t gbase = p.wl.part + ((uint64_t)(j * p.max_splits) * G) * stride * 4u;
-    const int n16 = nsplit * G * stride / 4;
+    const int n16 = sp.nsplit * G * stride / 4;
     for (int idx = threadIdx.x; idx < n16; idx += kThreads)
         *(u32x4 *)(all + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * hd; idx += kThreads) {
         const int h = idx / hd, e = idx % hd;
         float mm = -INFINITY, ll = 0.f, aa = 0.f;
-        for (int q = 0; q < nsplit; ++q) {
+        for (int q = 0; q < sp.nsplit; ++q) {
             const float *r = all + ((size_t)q * G + h) * stride;
             lse_merge(mm, ll, &aa, r[0], r[1], &r[4 + e], 1);
         }
@@ -550,29 +921,53 @@ MBK_DEV void attention_item(const Params &p, int layer, int j, int s, float *lds
     }
 }
 
-MBK_DEV void op_attention(const Params &p, const Interval &iv, float *lds) {
-    const int nwg = p.n_wg;
-    const int first = (int)((blockIdx.x + (uint32_t)nwg - (uint32_t)(iv.rot % nwg)) % (uint32_t)nwg);
-    for (int i = first; i < iv.n_items; i += nwg) {
-        const int j = i / p.max_splits, s = i % p.max_splits;
-        switch (p.gqa) {
-            case 1: attention_item<1>(p, iv.layer, j, s, lds); break;
-            case 2: attention_item<2>(p, iv.layer, j, s, lds); break;
-            case 3: attention_item<3>(p, iv.layer, j, s, lds); break;
-            case 4: attention_item<4>(p, iv.layer, j, s, lds); break;
-            case 5: attention_item<5>(p, iv.layer, j, s, lds); break;
-            case 6: attention_item<6>(p, iv.layer, j, s, lds); break;
-            case 7: attention_item<7>(p, iv.layer, j, s, lds); break;
-            default: attention_item<8>(p, iv.layer, j, s, lds); break;
-        }
+template <int G>
+MBK_DEV void op_attention(const Params &p, const Interval &iv, int ivi, float *lds) {
+    stamp(p, ivi, 1);
+    const int first = first_item(p, iv);
+    for (int i = first; i < iv.n_items; i += p.n_wg) {
+        attention_item<G>(p, iv.layer, i / p.max_splits, i % p.max_splits, i == first, lds);
         __syncthreads();
     }
 }
 
 // ---- interval dispatch -------------------------------------------------------------------------------
 
+// One-time per launch: the interval table and this step's RoPE row go to LDS.
+MBK_DEV void load_static(const Params &p, float *lds) {
+    const uint32_t *src = (const uint32_t *)p.iv;
+    uint32_t *dst = (uint32_t *)(lds + p.lds_tab);
+    const int nw = p.n_intervals * (int)(sizeof(Interval) / 4);
+    for (int i = threadIdx.x; i < nw; i += kThreads) dst[i] = src[i];
+    const int pos = step_pos(p), half = p.hd / 2;
+    for (int i = threadIdx.x; i < 2 * half; i += kThreads) lds[p.lds_rope + i] = p.rope[(size_t)pos * 2 * half + i];
+    __syncthreads();
+}
+
+// Descriptor of interval ivi from the LDS copy, forced into scalar registers.
+MBK_DEV Interval interval_at(const Params &p, const float *lds, int ivi) {
+    constexpr int nw = (int)(sizeof(Interval) / 4);
+    const uint32_t *src = (const uint32_t *)(lds + p.lds_tab) + ivi * nw;
+    uint32_t w[nw];
+#pragma unroll
+    for (int i = 0; i < nw; ++i) w[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    Interval v;
+    __builtin_memcpy(&v, w, sizeof v);
+    return v;
+}
+
+// Stages what interval ivi reads that does not depend on the previous
+// interval's results, using threads [tid, nthreads) of the workgroup.
+MBK_DEV void stage(const Params &p, float *lds, int ivi, int tid, int nthreads) {
+    const Interval iv = interval_at(p, lds, ivi);
+    if (iv.op == OP_ATTN) stage_attn(p, iv, staging(p, lds), tid, nthreads);
+    else stage_gemv(p, iv, staging(p, lds), tid, nthreads);
+}
+
+template <int G>
 MBK_DEV void run_interval(const Params &p, int ivi, float *lds, float *red) {
-    const Interval iv = p.iv[ivi];
+    const Interval iv = interval_at(p, lds, ivi);
+    stamp(p, ivi, 0);
     if (ivi == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
         __hip_atomic_store(ws_ptr<uint64_t>(p, p.wl.argkey), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (!p.step_from_ws) {  // publish this step's token/pos for launches that read them from the workspace
@@ -581,15 +976,9 @@ MBK_DEV void run_interval(const Params &p, int ivi, float *lds, float *red) {
             stc_u(ctrl + 4, (uint32_t)p.pos);
         }
     }
-    switch (iv.op) {
-        case OP_QKV: op_qkv(p, iv, lds, red); break;
-        case OP_ATTN: op_attention(p, iv, lds); break;
-        case OP_O: op_o(p, iv, lds); break;
-        case OP_GATEUP: op_gateup(p, iv, lds, red); break;
-        case OP_DOWN: op_down(p, iv, lds); break;
-        case OP_LMHEAD: op_lmhead(p, iv, lds, red); break;
-        default: break;
-    }
+    if (iv.op == OP_ATTN) op_attention<G>(p, iv, ivi, lds);
+    else op_gemv(p, iv, ivi, lds, red);
+    stamp(p, ivi, 2);
 }
 
 }  // namespace mbk

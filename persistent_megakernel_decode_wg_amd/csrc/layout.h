@@ -35,7 +35,7 @@ struct MatGeom {
     int32_t L, RT, IT;
     int32_t ntiles;
     int32_t kind;    // MatKind: how packed rows map to source rows
-    int32_t pad;
+    int32_t lrt;     // log2(RT)
 };
 
 MBK_HD uint64_t chunk_offset(const MatGeom &g, int64_t tile, int it, int lane) {
@@ -96,21 +96,31 @@ struct Interval {
     int32_t layer;
     int32_t n_items;   // GEMV: tiles; attention: n_kv_heads * max_splits
     int32_t rot;       // item i runs on workgroup (i + rot) % n_wg
+    int32_t x_src;     // interval that wrote the residual-stream version read here (-1: embedding row)
+    int32_t pad;
     MatGeom mat;       // GEMV operators
     uint64_t norm_off; // RMSNorm weight folded into this interval (bf16), or ~0
     uint64_t bias_off; // Q/K/V bias (bf16, [q|k|v] natural order), or ~0
 };
 
 // Workspace layout (bytes).  Control words get their own 256-byte lines.
+// Activations handed between intervals are vectors of tagged 8-byte entries
+// {fp32 value, u32 tag}: the tag names the (step, interval) that wrote the
+// value, so a reader polls for exactly the version it needs.
 struct WsLayout {
-    uint64_t ctrl;      // [0] error flag, [1] previous argmax token, [2] LM-head arrivals
+    uint64_t ctrl;      // [0] error flag, [1] previous argmax token, [2] LM-head arrivals,
+                        // [3] token, [4] pos, [5] step sequence (for launches reading them here)
     uint64_t argkey;    // u64 argmax key
     uint64_t bar_global;
     uint64_t bar_group; // kGroups lines: arrival counters
     uint64_t bar_rel;   // kGroups lines: release epochs
     uint64_t merge_cnt; // n_kv lines: attention split arrivals
-    uint64_t x, q, o, a;
-    uint64_t part;      // attention partials [n_kv][max_splits][g][hd + 2]
+    uint64_t x;         // [hidden] residual stream
+    uint64_t q;         // [n_heads * hd] rotated queries
+    uint64_t k, v;      // [n_kv * hd] this step's rotated keys / values (fp32)
+    uint64_t o;         // [n_heads * hd] attention output
+    uint64_t a;         // [intermediate] silu(gate) * up
+    uint64_t part;      // attention partials [n_kv][max_splits][g][hd + 4] (fp32)
     uint64_t total;
 };
 

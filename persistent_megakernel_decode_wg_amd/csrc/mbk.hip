@@ -24,22 +24,42 @@ using namespace mbk;
 
 // ---- kernels ----------------------------------------------------------------------------------------
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
     extern __shared__ float lds[];
     __shared__ float red[kWaves];
+    load_static(p, lds);
+    stage(p, lds, p.first_iv, threadIdx.x, kThreads);
+    __syncthreads();
     for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
-        run_interval(p, ivi, lds, red);
+        run_interval<G>(p, ivi, lds, red);
         if (ivi + 1 < p.last_iv) {
-            if (!grid_barrier(p, p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u, ivi)) return;
+            const uint32_t epoch = p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u;
+            const int last = barrier_arrive(p, epoch, ivi);
+            // wave 0 waits at the barrier; waves 1-3 stage the next interval meanwhile
+            if (threadIdx.x >= 64) stage(p, lds, ivi + 1, threadIdx.x - 64, kThreads - 64);
+            if (!barrier_wait(p, epoch, last)) return;
         }
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void k_interval(Params p, int ivi) {
     extern __shared__ float lds[];
     __shared__ float red[kWaves];
-    run_interval(p, ivi, lds, red);
+    load_static(p, lds);
+    stage(p, lds, ivi, threadIdx.x, kThreads);
+    __syncthreads();
+    run_interval<G>(p, ivi, lds, red);
 }
+
+// One instance per query-group size G (query heads per KV head).
+typedef void (*persistent_fn)(Params);
+typedef void (*interval_fn)(Params, int);
+static const persistent_fn kPersistent[kMaxGqa] = {k_persistent<1>, k_persistent<2>, k_persistent<3>, k_persistent<4>,
+                                                   k_persistent<5>, k_persistent<6>, k_persistent<7>, k_persistent<8>};
+static const interval_fn kInterval[kMaxGqa] = {k_interval<1>, k_interval<2>, k_interval<3>, k_interval<4>,
+                                               k_interval<5>, k_interval<6>, k_interval<7>, k_interval<8>};
 
 __global__ __launch_bounds__(kThreads) void k_barrier_bench(Params p, int n) {
     for (int i = 0; i < n; ++i)
@@ -101,6 +121,7 @@ struct Plan {
     uint64_t final_norm = 0, rope = 0, table = 0, total = 0;
     std::vector<Interval> iv;
     int max_splits = 1;
+    int lds_tab = 0, lds_rope = 0, lds_xres = 0, lds_bias = 0, lds_xs = 0, lds_ys = 0, lds_pf = 0, pf_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
 };
@@ -119,6 +140,8 @@ struct mbk_model {
     uint8_t *ws = nullptr;
     uint32_t epoch = 0;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
+    int32_t attn_min_chunk = 128;
+    uint64_t *trace = nullptr;
     // graph replay of the ablation
     hipGraph_t graph = nullptr;
     hipGraphExec_t gexec = nullptr;
@@ -137,6 +160,8 @@ MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind) {
     g.rows = rows;
     g.ntiles = (rows + g.RT - 1) / g.RT;
     g.kind = kind;
+    g.lrt = 0;
+    while ((1 << g.lrt) < g.RT) ++g.lrt;
     g.off = cursor;
     cursor = align256(cursor + (uint64_t)g.ntiles * g.IT * 1024u);
     return g;
@@ -195,16 +220,42 @@ void build_plan(mbk_model *m) {
     // attention split count: enough items to reach every CU, and every
     // partial of one KV head must fit in LDS for the merge
     const int stride = hd + 4;
-    const size_t attn_budget = 96 * 1024;
+    const size_t attn_budget = 48 * 1024;
     int ms = std::max(1, m->n_wg / c.n_kv_heads);
     ms = std::min<int>(ms, (int)(attn_budget / ((size_t)G * stride * 4)));
     ms = std::max(1, std::min(ms, 64));
     P.max_splits = ms;
-    size_t lds = (size_t)std::max({c.hidden, Q, c.intermediate}) * 4;
-    lds = std::max(lds, (size_t)(G + kWaves * G) * stride * 4);
-    lds = std::max(lds, (size_t)ms * G * stride * 4);
-    P.lds_bytes = (lds + 15) & ~(size_t)15;
-
+    // LDS (floats): interval table | RoPE row | residual x | Q/K/V bias | GEMV input or attention scratch
+    const int n_iv = 5 * c.n_layers + 1;
+    int off = 0;
+    P.lds_tab = off;
+    off += (int)((n_iv * sizeof(Interval) + 15) / 16 * 4);
+    P.lds_rope = off;
+    off += (hd + 3) / 4 * 4;
+    P.lds_xres = off;
+    off += (c.hidden + 3) / 4 * 4;
+    P.lds_bias = off;
+    if (c.qkv_bias) off += (Q + 2 * KV + 3) / 4 * 4;
+    // row sums of this workgroup's tiles: rounds (one tile per wave) * 4 waves * RT rows, per interval max
+    int ys = 0;
+    for (int l = 0; l < c.n_layers; ++l)
+        for (const MatGeom *g : {&P.layers[l].qkv, &P.layers[l].o, &P.layers[l].gu, &P.layers[l].down})
+            ys = std::max(ys, (g->ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * g->RT);
+    ys = std::max(ys, (P.embed.ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * P.embed.RT);
+    P.lds_ys = off;
+    off += (ys + 3) / 4 * 4;
+    P.lds_xs = off;
+    size_t work = (size_t)std::max({c.hidden, Q, c.intermediate});
+    // attention: result [G][stride], per-wave maxima [kWaves][G], per-slot partials [kWaves * 512/hd][G][stride]
+    work = std::max(work, (size_t)G * stride + kWaves * G + (size_t)kWaves * (512 / hd) * G * stride);
+    work = std::max(work, (size_t)ms * G * stride);
+    off += (int)((work + 3) / 4 * 4);
+    // staging area for the next interval's weights / cached keys and values
+    P.lds_pf = off;
+    const size_t lds_max = 160 * 1024;
+    const size_t used = (size_t)off * 4 + 256;  // + static LDS of the kernels
+    P.pf_bytes = (int)std::min<size_t>(64 * 1024, used < lds_max ? (lds_max - used) / 1024 * 1024 : 0);
+    P.lds_bytes = (size_t)off * 4 + P.pf_bytes;
     P.iv.clear();
     for (int l = 0; l < c.n_layers; ++l) {
         const LayerPlan &L = P.layers[l];
@@ -259,8 +310,9 @@ int ensure_plan(mbk_model *m) {
     build_plan(m);
     const size_t lds = m->plan.lds_bytes;
     if (lds > 160 * 1024) return fail(MBK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", lds);
-    HIPCHK(hipFuncSetAttribute((const void *)k_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    HIPCHK(hipFuncSetAttribute((const void *)k_interval, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    const int G = m->c.n_heads / m->c.n_kv_heads;
+    HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     return MBK_OK;
 }
 
@@ -276,7 +328,6 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.argmax_out = argmax;
     p.rope = (const float *)(m->blob + m->plan.rope);
     p.embed = m->plan.embed;
-    p.final_norm_off = m->plan.final_norm;
     p.n_wg = m->n_wg;
     p.n_intervals = (int)m->plan.iv.size();
     p.H = c.hidden;
@@ -289,6 +340,16 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.NL = c.n_layers;
     p.max_splits = m->plan.max_splits;
     p.gqa = c.n_heads / c.n_kv_heads;
+    p.attn_min_chunk = m->attn_min_chunk;
+    p.lds_tab = m->plan.lds_tab;
+    p.lds_rope = m->plan.lds_rope;
+    p.lds_xs = m->plan.lds_xs;
+    p.lds_xres = m->plan.lds_xres;
+    p.lds_bias = m->plan.lds_bias;
+    p.lds_ys = m->plan.lds_ys;
+    p.lds_pf = m->plan.lds_pf;
+    p.pf_bytes = m->plan.pf_bytes;
+    p.trace = m->trace;
     p.eps = c.rms_eps;
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
     p.token = token;
@@ -465,7 +526,7 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
     if (rc) return rc;
     Params p = make_params(m, token, pos, logits, argmax);
     void *args[] = {&p};
-    HIPCHK(hipLaunchCooperativeKernel((const void *)k_persistent, dim3(m->n_wg), dim3(kThreads), args,
+    HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
                                       (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
     m->epoch += (uint32_t)(p.n_intervals - 1);
     return MBK_OK;
@@ -480,7 +541,7 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
     const unsigned lds = (unsigned)m->plan.lds_bytes;
     if (!use_graph) {
         for (int i = 0; i < p.n_intervals; ++i)
-            hipLaunchKernelGGL(k_interval, dim3(m->n_wg), dim3(kThreads), lds, st, p, i);
+            hipLaunchKernelGGL(kInterval[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), lds, st, p, i);
         HIPCHK(hipGetLastError());
         return MBK_OK;
     }
@@ -495,7 +556,7 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
             idx[i] = i;
             void *kargs[] = {&ps[i], &idx[i]};
             hipKernelNodeParams kp{};
-            kp.func = (void *)k_interval;
+            kp.func = (void *)kInterval[p.gqa - 1];
             kp.gridDim = dim3(m->n_wg);
             kp.blockDim = dim3(kThreads);
             kp.sharedMemBytes = lds;
@@ -512,7 +573,7 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
     int zero = 0;
     void *kargs[] = {&p, &zero};
     hipKernelNodeParams kp{};
-    kp.func = (void *)k_interval;
+    kp.func = (void *)kInterval[p.gqa - 1];
     kp.gridDim = dim3(m->n_wg);
     kp.blockDim = dim3(kThreads);
     kp.sharedMemBytes = lds;
@@ -529,6 +590,29 @@ int mbk_check(mbk_model *m, void *stream) {
     uint32_t err = 0;
     HIPCHK(hipMemcpy(&err, m->ws + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));
     if (err) return fail(MBK_ERR_TIMEOUT, "a grid-barrier wait expired on the device; re-bind KV/workspace");
+    return MBK_OK;
+}
+
+int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    if (!buf) {
+        m->trace = nullptr;
+        return MBK_OK;
+    }
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    const size_t need = m->plan.iv.size() * (size_t)m->n_wg * 4 * sizeof(uint64_t);
+    if (bytes < need) return fail(MBK_ERR_SIZE, "phase trace buffer %zu < %zu bytes", bytes, need);
+    if (!aligned(buf, 8)) return fail(MBK_ERR_ARG, "phase trace buffer not 8-byte aligned");
+    drop_graph(m);
+    m->trace = (uint64_t *)buf;
+    return MBK_OK;
+}
+
+int mbk_set_attention_split(mbk_model *m, int32_t min_positions) {
+    if (!m || min_positions < 1) return fail(MBK_ERR_ARG, "min_positions must be >= 1");
+    drop_graph(m);
+    m->attn_min_chunk = min_positions;
     return MBK_OK;
 }
 
