@@ -35,8 +35,11 @@ OPS = ["qkv", "attn", "o", "gateup", "down"]
 
 
 def phase_breakdown(dec, wl, positions, logits, am, steps=8, dump=""):
-    """Per-operator means (us) from the device phase timer: inputs = start->inputs loaded (median WG),
-    body = interval start->last WG done, sync = last WG done->first WG starting the next interval."""
+    """Per-operator means (us) from the device phase timer (100 MHz wall clock; stamps [0] interval start,
+    [1] inputs loaded -- only on workgroups with work --, [2] body done).  Per interval: done = last working
+    workgroup's [2]; span = done - previous interval's done (the step's critical path); wait = median
+    working workgroup's [1] - previous done (input hand-over latency); comp = median [2] - [1] over working
+    workgroups and comp_max its maximum; n_work = working workgroups."""
     import numpy as np
     import torch
     from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV
@@ -44,26 +47,30 @@ def phase_breakdown(dec, wl, positions, logits, am, steps=8, dump=""):
     acc = {}
     raw = []
     for i in range(steps):
+        tr.zero_()
         dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
         torch.cuda.synchronize()
-        t = tr.cpu().numpy().astype(np.int64)          # [iv][wg][4], 100 MHz ticks
+        t = tr.cpu().numpy().astype(np.int64)          # [iv][wg][4]
         raw.append(t.copy())
         n_iv = t.shape[0]
+        prev_done = t[0, :, 0].min()
         for iv in range(n_iv):
             op = "lmhead" if iv == n_iv - 1 else OPS[iv % 5]
-            st, inp, end = t[iv, :, 0], t[iv, :, 1], t[iv, :, 2]
-            body = (end.max() - st.min()) * 0.01
-            has = inp > 0
-            inputs = float(np.median(inp[has] - st[has])) * 0.01 if has.any() else 0.0
-            sync = (t[iv + 1, :, 0].min() - end.max()) * 0.01 if iv + 1 < n_iv else 0.0
-            a = acc.setdefault(op, [0.0, 0.0, 0.0, 0])
-            a[0] += inputs; a[1] += body; a[2] += sync; a[3] += 1
-        tr.zero_()
+            work = t[iv, :, 1] > 0
+            if not work.any():
+                continue
+            t1, t2 = t[iv, work, 1], t[iv, work, 2]
+            done = t2.max()
+            a = acc.setdefault(op, np.zeros(6))
+            a += [(done - prev_done) * 0.01, (np.median(t1) - prev_done) * 0.01, np.median(t2 - t1) * 0.01,
+                  (t2 - t1).max() * 0.01, work.sum(), 1]
+            prev_done = done
     dec.set_phase_trace(False)
     if dump:
         np.save(dump, np.stack(raw))
-    out = {op: {"inputs_us": round(a[0] / a[3], 3), "body_us": round(a[1] / a[3], 3), "sync_us": round(a[2] / a[3], 3),
-                "count_per_step": a[3] // steps} for op, a in acc.items()}
+    out = {op: {"span_us": round(a[0] / a[5], 3), "wait_us": round(a[1] / a[5], 3), "comp_us": round(a[2] / a[5], 3),
+                "comp_max_us": round(a[3] / a[5], 3), "n_work": int(a[4] / a[5]),
+                "count_per_step": int(a[5]) // steps} for op, a in acc.items()}
     print("phase breakdown (us, mean per interval): " + json.dumps(out), file=sys.stderr, flush=True)
     return out
 
@@ -82,6 +89,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sync", choices=["dataflow", "barrier"], default="dataflow",
+                    help="interval ordering of the persistent kernel (the other mode is timed as an extra)")
     ap.add_argument("--phase", action="store_true", help="print a per-operator phase-timer breakdown to stderr")
     ap.add_argument("--phase-dump", default="", help="also save the raw phase-timer arrays (.npy) to this path")
     args = ap.parse_args()
@@ -94,7 +103,7 @@ def main():
     import torch
 
     import synth
-    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV, Decoder
+    from persistent_megakernel_decode_wg_amd import MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV, Decoder
     from persistent_megakernel_decode_wg_amd import build as mbk_build
 
     mbk_build.ensure_built()
@@ -107,6 +116,8 @@ def main():
     dec = Decoder(wl)
     dec.pack_weights(Wt)
     dec.alloc_kv()
+    sync_modes = {"dataflow": MBK_SYNC_DATAFLOW, "barrier": MBK_SYNC_BARRIER}
+    dec.set_sync_mode(sync_modes[args.sync])
     stream = torch.cuda.current_stream()
     logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
     am = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -159,6 +170,22 @@ def main():
         "us_per_token_p90": round(pct(kern_us, 0.9), 2), "complete_call_us_p50": round(pct(call_us, 0.5), 2),
         "bytes_per_token": int(bytes_mean), "intervals_per_step": dec.num_intervals(),
     }
+    # the other interval ordering of the same persistent kernel
+    other = "barrier" if args.sync == "dataflow" else "dataflow"
+    dec.set_sync_mode(sync_modes[other])
+    for i in range(8):
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(128)]
+    for i in range(128):
+        ev2[i][0].record(stream)
+        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+        ev2[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec.check()
+    extra["sync_mode"] = args.sync
+    extra[other + "_mode_us_per_token"] = round(sum(a.elapsed_time(b) for a, b in ev2) / 128 * 1e3, 2)
+    dec.set_sync_mode(sync_modes[args.sync])
+
     if not args.no_ablation:
         for mode, use_graph in (("ablation_plain", False), ("ablation_graph", True)):
             n = min(K, 128)

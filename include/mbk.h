@@ -41,13 +41,22 @@ enum {
     MBK_ERR_SIZE = 3,        /* caller buffer smaller than required */
     MBK_ERR_UNSUPPORTED = 4, /* dimensions the kernels do not handle */
     MBK_ERR_HIP = 5,         /* a HIP runtime call failed (message has the HIP error) */
-    MBK_ERR_TIMEOUT = 6,     /* a bounded grid-barrier wait expired on the device */
+    MBK_ERR_TIMEOUT = 6,     /* a bounded wait (input poll or grid barrier) expired on the device */
     MBK_ERR_STATE = 7        /* call made before mbk_pack_weights / mbk_alloc_kv */
 };
 
 /* Pass as `token` to reuse the previous step's device-side argmax, so a greedy
  * loop needs no host round trip (the README's "pipelined calls"). */
 #define MBK_TOKEN_PREV (-1)
+
+/* How the intervals of the persistent kernel are ordered (mbk_set_sync_mode).
+ * DATAFLOW (default): every activation handed between intervals is written as
+ *   8-byte {value, tag} entries and each workgroup polls exactly the entries
+ *   it reads, without grid barriers (the MegaBake article's roadmap, section
+ *   "Checking the 5.5x": per-phase event counters instead of grid barriers).
+ * BARRIER: a counting grid barrier closes every interval (the article's
+ *   "How a model gets in" executor).  Both give bitwise identical results. */
+enum { MBK_SYNC_DATAFLOW = 0, MBK_SYNC_BARRIER = 1 };
 
 /* Decoder shape. Supported: head_dim in {16, 32, 64, 128}; n_heads a multiple
  * of n_kv_heads with n_heads / n_kv_heads <= 8; hidden, n_heads*head_dim and
@@ -104,41 +113,48 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
  * One cooperative launch of one workgroup per CU. */
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream);
 
-/* Same bodies and results (bitwise), one kernel launch per barrier interval
+/* Same bodies and results (bitwise), one kernel launch per interval
  * (the per-operator ablation).  use_graph = 1 replays the launches as a
  * hipGraph instantiated once per handle. */
 int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax,
                              int32_t use_graph, void *stream);
 
 /* Synchronises `stream` and reports device-side errors (MBK_ERR_TIMEOUT
- * when a bounded barrier wait expired; the KV/workspace must then be re-bound
- * with mbk_alloc_kv). */
+ * when a bounded wait expired; the KV/workspace must then be re-bound with
+ * mbk_alloc_kv). */
 int mbk_check(mbk_model *m, void *stream);
 
 /* Grid-barrier microbenchmark: one cooperative launch running n barriers with
  * empty bodies; *us_per_barrier = (t(n) - t(0)) / n from HIP events. */
 int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier);
 
-/* Number of barrier intervals (and ablation launches) per step. */
+/* Number of intervals (and ablation launches) per step: 5 per layer + 1. */
 int mbk_num_intervals(const mbk_model *m, int32_t *n);
 
-/* Test hook: limit every bounded barrier wait to `spin_limit` polls (0 =
- * default) and make workgroup `skip_wg` (-1 = none) skip its arrival at
- * interval `skip_interval`, so a test can force the watchdog from the host. */
+/* Test hook: limit every bounded wait to `spin_limit` polls (0 = default,
+ * 2^22) and make workgroup `skip_wg` (-1 = none) of the persistent kernel
+ * leave at interval `skip_interval` without running it, so a test can force
+ * the watchdog from the host: the waits of the workgroups that need its
+ * results (or its barrier arrival) expire and the step reports
+ * MBK_ERR_TIMEOUT through mbk_check. */
 int mbk_set_debug(mbk_model *m, int32_t spin_limit, int32_t skip_wg, int32_t skip_interval);
 
 /* Phase timer (the README's per-barrier-interval timer, section "Current
  * performance"): when buf != NULL, every workgroup of every following launch
  * writes the device wall clock (100 MHz) into buf as uint64
- * [interval][workgroup][4]: [0] interval start (after the barrier), [1] inputs
- * loaded, [2] body done, [3] unused.  buf must hold n_intervals * n_CUs * 32
- * bytes; NULL switches the timer off. */
+ * [interval][workgroup][4]: [0] interval start, [1] inputs loaded (written only by
+ * workgroups with work in the interval), [2] body
+ * done, [3] grid barrier passed (barrier mode only).  buf must hold
+ * n_intervals * n_CUs * 32 bytes; NULL switches the timer off. */
 int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
 
 /* Attention split policy: each split of the cached context covers at least
  * min_positions positions (default 128); contexts up to that length run
  * unsplit, one workgroup per KV head. */
 int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
+
+/* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */
+int mbk_set_sync_mode(mbk_model *m, int32_t mode);
 
 /* Message for the last non-zero status returned on this thread. */
 const char *mbk_last_error(void);

@@ -11,6 +11,8 @@ lib_path = os.path.join(_HERE, "libmbk.so")
 MBK_OK, MBK_ERR_ARG, MBK_ERR_RANGE, MBK_ERR_SIZE, MBK_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 MBK_ERR_HIP, MBK_ERR_TIMEOUT, MBK_ERR_STATE = 5, 6, 7
 MBK_TOKEN_PREV = -1
+MBK_SYNC_DATAFLOW = 0
+MBK_SYNC_BARRIER = 1
 
 
 class MbkError(RuntimeError):
@@ -59,11 +61,12 @@ def lib():
         L.mbk_set_debug.argtypes = [vp, i32, i32, i32]
         L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
         L.mbk_set_attention_split.argtypes = [vp, i32]
+        L.mbk_set_sync_mode.argtypes = [vp, i32]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
                   "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
-                  "mbk_set_attention_split"):
+                  "mbk_set_attention_split", "mbk_set_sync_mode"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +190,10 @@ class Decoder:
 
     def set_debug(self, spin_limit: int = 0, skip_wg: int = -1, skip_interval: int = -1) -> None:
         _chk(lib().mbk_set_debug(self.h, spin_limit, skip_wg, skip_interval))
+
+    def set_sync_mode(self, mode: int) -> None:
+        """MBK_SYNC_DATAFLOW (0, default) or MBK_SYNC_BARRIER (1)."""
+        _chk(lib().mbk_set_sync_mode(self.h, int(mode)))
 
     def set_attention_split(self, min_positions: int) -> None:
         _chk(lib().mbk_set_attention_split(self.h, int(min_positions)))

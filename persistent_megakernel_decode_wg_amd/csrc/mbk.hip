@@ -2,9 +2,11 @@
 //
 // Executors (MegaBake article, section "How a model gets in": phases grouped
 // into barrier intervals, a table-driven persistent loop that dispatches a
-// body per phase row and closes each interval with a counting grid barrier):
+// body per phase row):
 //   k_persistent  one cooperative launch, one workgroup per CU, walks the
-//                 static interval table with a grid barrier between intervals;
+//                 static interval table; intervals hand activations over as
+//                 tagged entries (dataflow), or -- in barrier mode -- close
+//                 with a counting grid barrier as in the article;
 //   k_interval    the same bodies, one launch per interval (the ablation).
 #include <hip/hip_runtime.h>
 
@@ -24,6 +26,9 @@ using namespace mbk;
 
 // ---- kernels ----------------------------------------------------------------------------------------
 
+// Every workgroup leaves the loop after the last interval or at its first
+// failed (expired) wait; the debug switch skip_wg/skip_interval makes one
+// workgroup leave early so that the others' waits expire.
 template <int G>
 __global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
     extern __shared__ float lds[];
@@ -32,13 +37,21 @@ __global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
     stage(p, lds, p.first_iv, threadIdx.x, kThreads);
     __syncthreads();
     for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
-        run_interval<G>(p, ivi, lds, red);
-        if (ivi + 1 < p.last_iv) {
+        if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return;
+        const bool more = ivi + 1 < p.last_iv;
+        if (!p.barrier) {
+            // dataflow: waves 2-3 stage the next interval while waves 0-1 wait for inputs
+            if (!run_interval<G>(p, ivi, more ? ivi + 1 : -1, lds, red)) return;
+            continue;
+        }
+        if (!run_interval<G>(p, ivi, -1, lds, red)) return;
+        if (more) {
             const uint32_t epoch = p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u;
-            const int last = barrier_arrive(p, epoch, ivi);
+            const int last = barrier_arrive(p, epoch);
             // wave 0 waits at the barrier; waves 1-3 stage the next interval meanwhile
             if (threadIdx.x >= 64) stage(p, lds, ivi + 1, threadIdx.x - 64, kThreads - 64);
             if (!barrier_wait(p, epoch, last)) return;
+            stamp(p, ivi, 3);
         }
     }
 }
@@ -50,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void k_interval(Params p, int ivi) {
     load_static(p, lds);
     stage(p, lds, ivi, threadIdx.x, kThreads);
     __syncthreads();
-    run_interval<G>(p, ivi, lds, red);
+    (void)run_interval<G>(p, ivi, -1, lds, red);
 }
 
 // One instance per query-group size G (query heads per KV head).
@@ -63,7 +76,7 @@ static const interval_fn kInterval[kMaxGqa] = {k_interval<1>, k_interval<2>, k_i
 
 __global__ __launch_bounds__(kThreads) void k_barrier_bench(Params p, int n) {
     for (int i = 0; i < n; ++i)
-        if (!grid_barrier(p, p.epoch_base + (uint32_t)i + 1u, -1)) return;
+        if (!grid_barrier(p, p.epoch_base + (uint32_t)i + 1u)) return;
 }
 
 // Packer: one thread per 16-byte chunk of the packed matrix.
@@ -138,7 +151,9 @@ struct mbk_model {
     uint8_t *blob = nullptr;
     uint16_t *kv = nullptr;
     uint8_t *ws = nullptr;
-    uint32_t epoch = 0;
+    uint32_t epoch = 0;   // grid barriers completed on the bound workspace
+    uint32_t seq = 0;     // decode steps run on the bound workspace (activation tags)
+    int32_t sync_mode = MBK_SYNC_DATAFLOW;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
     int32_t attn_min_chunk = 128;
     uint64_t *trace = nullptr;
@@ -167,12 +182,13 @@ MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind) {
     return g;
 }
 
-Interval gemv_interval(int op, int layer, const MatGeom &g, uint64_t norm, uint64_t bias) {
+Interval gemv_interval(int op, int layer, const MatGeom &g, uint64_t norm, uint64_t bias, int x_src) {
     Interval v{};
     v.op = op;
     v.layer = layer;
     v.n_items = g.ntiles;
     v.rot = 0;
+    v.x_src = x_src;
     v.mat = g;
     v.norm_off = norm;
     v.bias_off = bias;
@@ -220,28 +236,29 @@ void build_plan(mbk_model *m) {
     // attention split count: enough items to reach every CU, and every
     // partial of one KV head must fit in LDS for the merge
     const int stride = hd + 4;
-    const size_t attn_budget = 48 * 1024;
+    const size_t attn_budget = 32 * 1024;
     int ms = std::max(1, m->n_wg / c.n_kv_heads);
     ms = std::min<int>(ms, (int)(attn_budget / ((size_t)G * stride * 4)));
     ms = std::max(1, std::min(ms, 64));
     P.max_splits = ms;
-    // LDS (floats): interval table | RoPE row | residual x | Q/K/V bias | GEMV input or attention scratch
+    // LDS (floats): interval table | RoPE row | residual rows or attention inputs | Q/K/V bias |
+    // row sums | GEMV input or attention scratch | two staging buffers
     const int n_iv = 5 * c.n_layers + 1;
-    int off = 0;
-    P.lds_tab = off;
-    off += (int)((n_iv * sizeof(Interval) + 15) / 16 * 4);
-    P.lds_rope = off;
-    off += (hd + 3) / 4 * 4;
-    P.lds_xres = off;
-    off += (c.hidden + 3) / 4 * 4;
-    P.lds_bias = off;
-    if (c.qkv_bias) off += (Q + 2 * KV + 3) / 4 * 4;
     // row sums of this workgroup's tiles: rounds (one tile per wave) * 4 waves * RT rows, per interval max
     int ys = 0;
     for (int l = 0; l < c.n_layers; ++l)
         for (const MatGeom *g : {&P.layers[l].qkv, &P.layers[l].o, &P.layers[l].gu, &P.layers[l].down})
             ys = std::max(ys, (g->ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * g->RT);
     ys = std::max(ys, (P.embed.ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * P.embed.RT);
+    int off = 0;
+    P.lds_tab = off;
+    off += (int)((n_iv * sizeof(Interval) + 15) / 16 * 4);
+    P.lds_rope = off;
+    off += (hd + 3) / 4 * 4;
+    P.lds_xres = off;
+    off += (std::max(ys, (G + 2) * hd) + 3) / 4 * 4;
+    P.lds_bias = off;
+    if (c.qkv_bias) off += (Q + 2 * KV + 3) / 4 * 4;
     P.lds_ys = off;
     off += (ys + 3) / 4 * 4;
     P.lds_xs = off;
@@ -250,28 +267,33 @@ void build_plan(mbk_model *m) {
     work = std::max(work, (size_t)G * stride + kWaves * G + (size_t)kWaves * (512 / hd) * G * stride);
     work = std::max(work, (size_t)ms * G * stride);
     off += (int)((work + 3) / 4 * 4);
-    // staging area for the next interval's weights / cached keys and values
+    // two staging buffers for the next interval's weights / cached keys and values
     P.lds_pf = off;
     const size_t lds_max = 160 * 1024;
     const size_t used = (size_t)off * 4 + 256;  // + static LDS of the kernels
-    P.pf_bytes = (int)std::min<size_t>(64 * 1024, used < lds_max ? (lds_max - used) / 1024 * 1024 : 0);
-    P.lds_bytes = (size_t)off * 4 + P.pf_bytes;
+    P.pf_bytes = (int)std::min<size_t>(64 * 1024, used < lds_max ? (lds_max - used) / 2 / 1024 * 1024 : 0);
+    P.lds_bytes = (size_t)off * 4 + 2 * (size_t)P.pf_bytes;
     P.iv.clear();
+    // x_src: the interval whose residual-stream version an interval reads
+    // (the previous layer's down projection; -1: the embedding row)
+    const uint64_t none = ~(uint64_t)0;
     for (int l = 0; l < c.n_layers; ++l) {
         const LayerPlan &L = P.layers[l];
-        P.iv.push_back(gemv_interval(OP_QKV, l, L.qkv, L.attn_norm, L.bias));
+        const int base = 5 * l, prev_down = l == 0 ? -1 : base - 1;
+        P.iv.push_back(gemv_interval(OP_QKV, l, L.qkv, L.attn_norm, L.bias, prev_down));
         Interval a{};
         a.op = OP_ATTN;
         a.layer = l;
         a.n_items = c.n_kv_heads * ms;
         a.rot = 0;
-        a.norm_off = a.bias_off = ~(uint64_t)0;
+        a.x_src = -1;
+        a.norm_off = a.bias_off = none;
         P.iv.push_back(a);
-        P.iv.push_back(gemv_interval(OP_O, l, L.o, ~(uint64_t)0, ~(uint64_t)0));
-        P.iv.push_back(gemv_interval(OP_GATEUP, l, L.gu, L.mlp_norm, ~(uint64_t)0));
-        P.iv.push_back(gemv_interval(OP_DOWN, l, L.down, ~(uint64_t)0, ~(uint64_t)0));
+        P.iv.push_back(gemv_interval(OP_O, l, L.o, none, none, prev_down));
+        P.iv.push_back(gemv_interval(OP_GATEUP, l, L.gu, L.mlp_norm, none, base + 2));
+        P.iv.push_back(gemv_interval(OP_DOWN, l, L.down, none, none, base + 2));
     }
-    P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, ~(uint64_t)0));
+    P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, none, 5 * c.n_layers - 1));
     P.table = cur;
     cur = align256(cur + P.iv.size() * sizeof(Interval));
     P.total = cur;
@@ -285,10 +307,13 @@ void build_plan(mbk_model *m) {
     W.bar_group = w; w += 256 * kGroups;
     W.bar_rel = w; w += 256 * kGroups;
     W.merge_cnt = w; w += 256u * c.n_kv_heads;
-    W.x = w; w = align256(w + 4u * c.hidden);
-    W.q = w; w = align256(w + 4u * Q);
-    W.o = w; w = align256(w + 4u * Q);
-    W.a = w; w = align256(w + 4u * c.intermediate);
+    // tagged activations: 8 bytes per entry
+    W.x = w; w = align256(w + 8u * c.hidden);
+    W.q = w; w = align256(w + 8u * Q);
+    W.k = w; w = align256(w + 8u * KV);
+    W.v = w; w = align256(w + 8u * KV);
+    W.o = w; w = align256(w + 8u * Q);
+    W.a = w; w = align256(w + 8u * c.intermediate);
     W.part = w; w = align256(w + 4u * (uint64_t)c.n_kv_heads * ms * G * stride);
     W.total = w;
 
@@ -314,6 +339,13 @@ int ensure_plan(mbk_model *m) {
     HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     return MBK_OK;
+}
+
+// Next step number: tags seq * n_intervals + i + 1 must stay below 2^32.
+uint32_t next_seq(mbk_model *m) {
+    const uint32_t n = (uint32_t)m->plan.iv.size();
+    m->seq = (m->seq + 1u >= 0xffffffffu / n - 1u) ? 1u : m->seq + 1u;
+    return m->seq;
 }
 
 Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax) {
@@ -354,7 +386,9 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
     p.token = token;
     p.pos = pos;
+    p.seq = m->seq;
     p.step_from_ws = 0;
+    p.barrier = m->sync_mode == MBK_SYNC_BARRIER;
     p.epoch_base = m->epoch;
     p.spin_limit = m->spin_limit;
     p.skip_wg = m->skip_wg;
@@ -518,17 +552,19 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
     m->kv = (uint16_t *)kv;
     m->ws = (uint8_t *)ws;
     m->epoch = 0;
+    m->seq = 0;
     return MBK_OK;
 }
 
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream) {
     int rc = check_step_args(m, token, pos, argmax);
     if (rc) return rc;
+    next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
     void *args[] = {&p};
     HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
                                       (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
-    m->epoch += (uint32_t)(p.n_intervals - 1);
+    if (p.barrier) m->epoch += (uint32_t)(p.n_intervals - 1);
     return MBK_OK;
 }
 
@@ -537,7 +573,9 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
     int rc = check_step_args(m, token, pos, argmax);
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
+    next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
+    p.barrier = 0;
     const unsigned lds = (unsigned)m->plan.lds_bytes;
     if (!use_graph) {
         for (int i = 0; i < p.n_intervals; ++i)
@@ -589,7 +627,7 @@ int mbk_check(mbk_model *m, void *stream) {
     if (!m->ws) return MBK_OK;
     uint32_t err = 0;
     HIPCHK(hipMemcpy(&err, m->ws + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));
-    if (err) return fail(MBK_ERR_TIMEOUT, "a grid-barrier wait expired on the device; re-bind KV/workspace");
+    if (err) return fail(MBK_ERR_TIMEOUT, "a bounded device wait expired; re-bind KV/workspace");
     return MBK_OK;
 }
 
@@ -606,6 +644,13 @@ int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes) {
     if (!aligned(buf, 8)) return fail(MBK_ERR_ARG, "phase trace buffer not 8-byte aligned");
     drop_graph(m);
     m->trace = (uint64_t *)buf;
+    return MBK_OK;
+}
+
+int mbk_set_sync_mode(mbk_model *m, int32_t mode) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    if (mode != MBK_SYNC_DATAFLOW && mode != MBK_SYNC_BARRIER) return fail(MBK_ERR_ARG, "unknown sync mode %d", mode);
+    m->sync_mode = mode;
     return MBK_OK;
 }
 

@@ -52,8 +52,16 @@ class Pair:
         torch.cuda.synchronize()
 
     def gpu_step(self, token, pos, mode="mega"):
+        """mode: mega (persistent kernel, dataflow), barrier (persistent kernel, grid barriers),
+        ablation (one launch per interval) or graph (the ablation replayed as a hipGraph)."""
         if mode == "mega":
             self.dec.decode_step(token, pos, self.logits, self.am)
+        elif mode == "barrier":
+            self.dec.set_sync_mode(1)
+            try:
+                self.dec.decode_step(token, pos, self.logits, self.am)
+            finally:
+                self.dec.set_sync_mode(0)
         elif mode == "ablation":
             self.dec.decode_step_ablation(token, pos, self.logits, self.am, use_graph=False)
         else:

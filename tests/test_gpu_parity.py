@@ -21,8 +21,8 @@ def test_tiny_full_schedule_teacher_forced(tiny):
     log("tiny worst max|dlogit|/std = %.3g" % worst)
 
 
-@pytest.mark.parametrize("mode", ["ablation", "graph"])
-def test_tiny_ablation_is_bitwise_equal(tiny, mode):
+@pytest.mark.parametrize("mode", ["barrier", "ablation", "graph"])
+def test_tiny_executors_are_bitwise_equal(tiny, mode):
     wl = tiny.wl
     prompt = list(synth.prompt_tokens(wl))
     for pos in range(12):
@@ -99,9 +99,33 @@ def test_smollm135m_kv4096_prefilled_long_context():
     p = Pair(wl, kv_prefix=synth.kv_prefill(wl))
     positions = synth.decode_schedule(wl)
     log("smollm135m-kv4096: positions %d..%d" % (positions[0], positions[-1]))
-    # first 8 steps and the final step (which fills the last slot)
     worst = teacher_forced(p, positions[:8], [synth.first_token(wl)], label="smollm135m-4k")
     log("smollm135m-kv4096 worst max|dlogit|/std = %.3g" % worst)
+    # split-context attention with the cross-workgroup merge: every executor gives the same bits
+    pos = positions[8]
+    tok = synth.first_token(wl)
+    a, ia = p.gpu_step(tok, pos, "mega")
+    for mode in ("barrier", "ablation"):
+        b, ib = p.gpu_step(tok, pos, mode)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
+
+
+@pytest.mark.parametrize("mode", ["mega", "barrier"])
+def test_watchdog_expires_and_recovers(mode):
+    """Workgroup 0 leaves the persistent kernel before interval 0 (host-set debug switch, tiny spin
+    limit): the waits that need its results expire, every workgroup exits, the step reports
+    MBK_ERR_TIMEOUT, and after re-binding the workspace the next step is correct again."""
+    from persistent_megakernel_decode_wg_amd import MBK_ERR_TIMEOUT, MbkError
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = Pair(wl)
+    tok = int(synth.prompt_tokens(wl)[0])
+    p.dec.set_debug(spin_limit=1 << 14, skip_wg=0, skip_interval=0)
+    with pytest.raises(MbkError) as e:
+        p.gpu_step(tok, 0, mode)
+    assert e.value.code == MBK_ERR_TIMEOUT
+    p.dec.set_debug(0, -1, -1)
+    p.dec.rebind()
+    teacher_forced(p, [0, 1, 2], list(synth.prompt_tokens(wl)), mode=mode, label="after-watchdog")
 
 
 def test_qwen2_0p5b_bias_kv128():
