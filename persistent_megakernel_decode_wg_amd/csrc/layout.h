@@ -11,13 +11,15 @@
 
 namespace mbk {
 
-constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
+constexpr int kThreads = 384;          // threads per workgroup (6 wave64)
 constexpr int kWaves = kThreads / 64;
+constexpr int kCW = 4;                 // compute waves (0 .. kCW-1): poll inputs, compute, publish
+constexpr int kLW = kWaves - kCW;      // loader waves: stream this workgroup's future weights into LDS
 constexpr int kGroups = 8;             // barrier groups: WG w belongs to group w % 8 (one per XCD
                                        // under the round-robin dispatch of an 8-XCD part)
 constexpr int kMaxVec = 8192;          // largest GEMV input vector (floats) held in LDS
 constexpr int kMaxGqa = 8;             // query heads per KV head handled by one attention item
-constexpr int kAttnMinChunk = 64;      // fewest cached positions per attention split
+constexpr int kChunk = 1024;           // bytes one wave moves with one 16-byte-per-lane load
 
 enum Op : int32_t { OP_QKV = 0, OP_ATTN = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4, OP_LMHEAD = 5 };
 enum MatKind : int32_t { MAT_PLAIN = 0, MAT_QKV = 1, MAT_GATEUP = 2 };
@@ -90,18 +92,42 @@ MBK_HD RowSrc packed_row_source(int kind, int r, int hd, int nq_rows, int nkv_ro
     return s;
 }
 
-// One barrier interval of the static task list (a row of the phase table).
+// One barrier interval of the static schedule (a row of the phase table).
+// Its items (GEMV tiles, attention items) run on the nwg workgroups
+// (wg0 + k) % n_wg, k < nwg.  GEMV: participant k owns the contiguous tile
+// block [k * ntiles / nwg, (k + 1) * ntiles / nwg).  Attention: participant k
+// owns items k, k + nwg, ...
 struct Interval {
     int32_t op;        // Op
     int32_t layer;
     int32_t n_items;   // GEMV: tiles; attention: n_kv_heads * max_splits
-    int32_t rot;       // item i runs on workgroup (i + rot) % n_wg
     int32_t x_src;     // interval that wrote the residual-stream version read here (-1: embedding row)
-    int32_t pad;
+    int32_t wg0, nwg;  // participating workgroups
     MatGeom mat;       // GEMV operators
     uint64_t norm_off; // RMSNorm weight folded into this interval (bf16), or ~0
     uint64_t bias_off; // Q/K/V bias (bf16, [q|k|v] natural order), or ~0
 };
+
+// One entry of a workgroup's task list: a contiguous run of GEMV tiles, or
+// one attention item, of one interval.  A workgroup's tasks are stored in
+// interval order; its loader waves stream the weights of every task into an
+// LDS ring in that order, and its compute waves consume them in that order.
+enum TaskFlag : int32_t { TASK_FIRST = 1, TASK_LAST = 2 };
+struct Task {
+    int32_t iv;     // interval
+    int32_t a;      // GEMV: first tile; attention: item
+    int32_t n;      // GEMV: tiles; attention: 1
+    int32_t flags;  // TASK_FIRST: first task of this workgroup in iv; TASK_LAST: last one
+};
+
+// Block of tiles of participant k out of nwg over ntiles tiles.
+MBK_HD int block_begin(int64_t ntiles, int k, int nwg) { return (int)(ntiles * k / nwg); }
+
+// Participant index of workgroup w in an interval, or -1.
+MBK_HD int participant(const Interval &iv, int w, int n_wg) {
+    const int k = (w - iv.wg0 % n_wg + n_wg) % n_wg;
+    return k < iv.nwg ? k : -1;
+}
 
 // Workspace layout (bytes).  Control words get their own 256-byte lines.
 // Activations handed between intervals are vectors of tagged 8-byte entries

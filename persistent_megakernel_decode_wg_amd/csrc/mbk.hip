@@ -26,44 +26,21 @@ using namespace mbk;
 
 // ---- kernels ----------------------------------------------------------------------------------------
 
-// Every workgroup leaves the loop after the last interval or at its first
+// Both executors run the same step body (run_step): the persistent kernel
+// over every interval of the step, the ablation kernel over one interval per
+// launch.  Every workgroup leaves after its last interval or at its first
 // failed (expired) wait; the debug switch skip_wg/skip_interval makes one
 // workgroup leave early so that the others' waits expire.
 template <int G>
 __global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
-    extern __shared__ float lds[];
-    __shared__ float red[kWaves];
-    load_static(p, lds);
-    stage(p, lds, p.first_iv, threadIdx.x, kThreads);
-    __syncthreads();
-    for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
-        if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return;
-        const bool more = ivi + 1 < p.last_iv;
-        if (!p.barrier) {
-            // dataflow: waves 2-3 stage the next interval while waves 0-1 wait for inputs
-            if (!run_interval<G>(p, ivi, more ? ivi + 1 : -1, lds, red)) return;
-            continue;
-        }
-        if (!run_interval<G>(p, ivi, -1, lds, red)) return;
-        if (more) {
-            const uint32_t epoch = p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u;
-            const int last = barrier_arrive(p, epoch);
-            // wave 0 waits at the barrier; waves 1-3 stage the next interval meanwhile
-            if (threadIdx.x >= 64) stage(p, lds, ivi + 1, threadIdx.x - 64, kThreads - 64);
-            if (!barrier_wait(p, epoch, last)) return;
-            stamp(p, ivi, 3);
-        }
-    }
+    run_step<G>(p);
 }
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void k_interval(Params p, int ivi) {
-    extern __shared__ float lds[];
-    __shared__ float red[kWaves];
-    load_static(p, lds);
-    stage(p, lds, ivi, threadIdx.x, kThreads);
-    __syncthreads();
-    (void)run_interval<G>(p, ivi, -1, lds, red);
+    p.first_iv = ivi;
+    p.last_iv = ivi + 1;
+    run_step<G>(p);
 }
 
 // One instance per query-group size G (query heads per KV head).
@@ -131,10 +108,14 @@ struct LayerPlan {
 struct Plan {
     std::vector<LayerPlan> layers;
     MatGeom embed;
-    uint64_t final_norm = 0, rope = 0, table = 0, total = 0;
+    uint64_t final_norm = 0, rope = 0, table = 0, tasks = 0, task_idx = 0, total = 0;
     std::vector<Interval> iv;
-    int max_splits = 1;
-    int lds_tab = 0, lds_rope = 0, lds_xres = 0, lds_bias = 0, lds_xs = 0, lds_ys = 0, lds_pf = 0, pf_bytes = 0;
+    std::vector<Task> task_list;       // all workgroups' tasks, workgroup-major
+    std::vector<int32_t> task_index;   // [n_wg][n_iv + 1]
+    int max_splits = 1, piece_pos = 1, max_tasks = 0;
+    // LDS layout (bytes of the dynamic area)
+    int lds_ivtab = 0, lds_tasks = 0, lds_trace = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
+        lds_xres = 0, lds_attn = 0, lds_ring = 0, ring_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
 };
@@ -187,7 +168,6 @@ Interval gemv_interval(int op, int layer, const MatGeom &g, uint64_t norm, uint6
     v.op = op;
     v.layer = layer;
     v.n_items = g.ntiles;
-    v.rot = 0;
     v.x_src = x_src;
     v.mat = g;
     v.norm_off = norm;
@@ -205,9 +185,19 @@ int ensure_device(mbk_model *m) {
     return MBK_OK;
 }
 
-void build_plan(mbk_model *m) {
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr size_t kLdsStatic = 512;      // Ctl and the other static LDS words of the kernels
+constexpr int kMinRing = 16 * 1024;
+
+size_t a16(size_t v) { return (v + 15) / 16 * 16; }
+
+// Builds the packed-blob layout, the interval table, every workgroup's task
+// list and the LDS layout.  Returns an empty string or the reason the shape
+// cannot be planned.
+std::string build_plan(mbk_model *m) {
     const mbk_config &c = m->c;
     Plan &P = m->plan;
+    const int n_wg = m->n_wg;
     const int hd = c.head_dim, Q = c.n_heads * hd, KV = c.n_kv_heads * hd, G = c.n_heads / c.n_kv_heads;
     uint64_t cur = 0;
     P.layers.resize(c.n_layers);
@@ -233,50 +223,18 @@ void build_plan(mbk_model *m) {
     P.rope = cur;
     cur = align256(cur + (uint64_t)c.kv_capacity * (hd / 2) * 8u);
 
-    // attention split count: enough items to reach every CU, and every
-    // partial of one KV head must fit in LDS for the merge
+    // attention splits: enough items to reach the CUs, and every partial of
+    // one KV head fits the LDS merge scratch
     const int stride = hd + 4;
-    const size_t attn_budget = 32 * 1024;
-    int ms = std::max(1, m->n_wg / c.n_kv_heads);
-    ms = std::min<int>(ms, (int)(attn_budget / ((size_t)G * stride * 4)));
+    const size_t merge_budget = 16 * 1024;
+    int ms = std::max(1, n_wg / c.n_kv_heads);
+    ms = std::min<int>(ms, (int)(merge_budget / ((size_t)G * stride * 4)));
     ms = std::max(1, std::min(ms, 64));
     P.max_splits = ms;
-    // LDS (floats): interval table | RoPE row | residual rows or attention inputs | Q/K/V bias |
-    // row sums | GEMV input or attention scratch | two staging buffers
-    const int n_iv = 5 * c.n_layers + 1;
-    // row sums of this workgroup's tiles: rounds (one tile per wave) * 4 waves * RT rows, per interval max
-    int ys = 0;
-    for (int l = 0; l < c.n_layers; ++l)
-        for (const MatGeom *g : {&P.layers[l].qkv, &P.layers[l].o, &P.layers[l].gu, &P.layers[l].down})
-            ys = std::max(ys, (g->ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * g->RT);
-    ys = std::max(ys, (P.embed.ntiles + kWaves * m->n_wg - 1) / (kWaves * m->n_wg) * kWaves * P.embed.RT);
-    int off = 0;
-    P.lds_tab = off;
-    off += (int)((n_iv * sizeof(Interval) + 15) / 16 * 4);
-    P.lds_rope = off;
-    off += (hd + 3) / 4 * 4;
-    P.lds_xres = off;
-    off += (std::max(ys, (G + 2) * hd) + 3) / 4 * 4;
-    P.lds_bias = off;
-    if (c.qkv_bias) off += (Q + 2 * KV + 3) / 4 * 4;
-    P.lds_ys = off;
-    off += (ys + 3) / 4 * 4;
-    P.lds_xs = off;
-    size_t work = (size_t)std::max({c.hidden, Q, c.intermediate});
-    // attention: result [G][stride], per-wave maxima [kWaves][G], per-slot partials [kWaves * 512/hd][G][stride]
-    work = std::max(work, (size_t)G * stride + kWaves * G + (size_t)kWaves * (512 / hd) * G * stride);
-    work = std::max(work, (size_t)ms * G * stride);
-    off += (int)((work + 3) / 4 * 4);
-    // two staging buffers for the next interval's weights / cached keys and values
-    P.lds_pf = off;
-    const size_t lds_max = 160 * 1024;
-    const size_t used = (size_t)off * 4 + 256;  // + static LDS of the kernels
-    P.pf_bytes = (int)std::min<size_t>(64 * 1024, used < lds_max ? (lds_max - used) / 2 / 1024 * 1024 : 0);
-    P.lds_bytes = (size_t)off * 4 + 2 * (size_t)P.pf_bytes;
-    P.iv.clear();
-    // x_src: the interval whose residual-stream version an interval reads
-    // (the previous layer's down projection; -1: the embedding row)
+
+    // intervals: participants rotate so that successive intervals start on different workgroups
     const uint64_t none = ~(uint64_t)0;
+    P.iv.clear();
     for (int l = 0; l < c.n_layers; ++l) {
         const LayerPlan &L = P.layers[l];
         const int base = 5 * l, prev_down = l == 0 ? -1 : base - 1;
@@ -285,7 +243,6 @@ void build_plan(mbk_model *m) {
         a.op = OP_ATTN;
         a.layer = l;
         a.n_items = c.n_kv_heads * ms;
-        a.rot = 0;
         a.x_src = -1;
         a.norm_off = a.bias_off = none;
         P.iv.push_back(a);
@@ -294,8 +251,111 @@ void build_plan(mbk_model *m) {
         P.iv.push_back(gemv_interval(OP_DOWN, l, L.down, none, none, base + 2));
     }
     P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, none, 5 * c.n_layers - 1));
+    const int n_iv = (int)P.iv.size();
+    int rot = 0;
+    for (Interval &v : P.iv) {
+        v.nwg = std::min(n_wg, v.n_items);
+        v.wg0 = rot;
+        rot = (rot + v.nwg) % n_wg;
+    }
+
+    // LDS layout (the ring takes what is left)
+    int max_rows = 1;
+    for (const Interval &v : P.iv)
+        if (v.op == OP_O || v.op == OP_DOWN)
+            for (int k = 0; k < v.nwg; ++k)
+                max_rows = std::max(max_rows, (block_begin(v.n_items, k + 1, v.nwg) - block_begin(v.n_items, k, v.nwg)) * v.mat.RT);
+    const int kmax = std::max({c.hidden, Q, c.intermediate});
+    size_t off = 0;
+    P.lds_ivtab = (int)off; off = a16(off + (size_t)n_iv * sizeof(Interval));
+    const size_t task_slot = off;
+    // tasks are laid out below, once their count is known; reserve after the fixed parts
+    P.lds_trace = 0; P.lds_rope = 0;
+    size_t fixed = 0;
+    fixed += a16((size_t)n_iv * 32);                               // trace
+    fixed += a16((size_t)4 * hd);                                  // RoPE row
+    fixed += a16((size_t)(G + 2) * hd * 4);                        // attention inputs
+    fixed += c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0;       // Q/K/V bias
+    fixed += a16((size_t)kmax * 4);                                // GEMV input (hi/lo pairs)
+    fixed += a16((size_t)max_rows * 4);                            // residual rows
+    fixed += a16((size_t)std::max(kCW, ms) * G * stride * 4);      // attention merge scratch
+
+    // tile runs of at most a quarter of the ring: first size the ring assuming a task
+    // list of 64 entries per workgroup, then build the lists and shrink the ring
+    // to what the lists leave.
+    size_t max_tile = 0;
+    for (const Interval &v : P.iv)
+        if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.IT * kChunk);
+    auto build_tasks = [&](size_t ring) {
+        const size_t max_alloc = ring / 4;
+        P.task_list.clear();
+        P.task_index.assign((size_t)n_wg * (n_iv + 1), 0);
+        int max_tasks = 0;
+        for (int w = 0; w < n_wg; ++w) {
+            const int start = (int)P.task_list.size();
+            for (int i = 0; i < n_iv; ++i) {
+                P.task_index[(size_t)w * (n_iv + 1) + i] = (int)P.task_list.size();
+                const Interval &v = P.iv[i];
+                const int k = participant(v, w, n_wg);
+                if (k < 0) continue;
+                const size_t first = P.task_list.size();
+                if (v.op == OP_ATTN) {
+                    for (int it = k; it < v.n_items; it += v.nwg) P.task_list.push_back(Task{i, it, 1, 0});
+                } else {
+                    const int b0 = block_begin(v.n_items, k, v.nwg), b1 = block_begin(v.n_items, k + 1, v.nwg);
+                    const int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
+                    for (int t = b0; t < b1; t += per) P.task_list.push_back(Task{i, t, std::min(per, b1 - t), 0});
+                }
+                if (P.task_list.size() > first) {
+                    P.task_list[first].flags |= TASK_FIRST;
+                    P.task_list.back().flags |= TASK_LAST;
+                }
+            }
+            P.task_index[(size_t)w * (n_iv + 1) + n_iv] = (int)P.task_list.size();
+            max_tasks = std::max(max_tasks, (int)P.task_list.size() - start);
+        }
+        P.max_tasks = max_tasks;
+    };
+    const size_t avail0 = kLdsMax - kLdsStatic - task_slot - fixed;
+    size_t ring = avail0 > (size_t)64 * 16 ? (avail0 - 64 * 16) / kChunk * kChunk : 0;
+    for (int iter = 0; iter < 4; ++iter) {
+        if (ring < (size_t)kMinRing || ring < 4 * max_tile) break;
+        build_tasks(ring);
+        const size_t need = task_slot + a16((size_t)P.max_tasks * 16) + fixed;
+        if (need + kLdsStatic + ring <= kLdsMax) break;
+        ring = need + kLdsStatic < kLdsMax ? (kLdsMax - kLdsStatic - need) / kChunk * kChunk : 0;
+    }
+    if (ring < (size_t)kMinRing || ring < 4 * max_tile)
+        return "not enough LDS for the weight ring (" + std::to_string(ring) + " bytes)";
+    build_tasks(ring);
+    off = task_slot;
+    P.lds_tasks = (int)off; off = a16(off + (size_t)P.max_tasks * 16);
+    P.lds_trace = (int)off; off = a16(off + (size_t)n_iv * 32);
+    P.lds_rope = (int)off; off = a16(off + (size_t)4 * hd);
+    P.lds_qkv = (int)off; off = a16(off + (size_t)(G + 2) * hd * 4);
+    P.lds_bias = (int)off; off = c.qkv_bias ? a16(off + (size_t)(Q + 2 * KV) * 4) : off;
+    P.lds_xs = (int)off; off = a16(off + (size_t)kmax * 4);
+    P.lds_xres = (int)off; off = a16(off + (size_t)max_rows * 4);
+    P.lds_attn = (int)off; off = a16(off + (size_t)std::max(kCW, ms) * G * stride * 4);
+    off = (off + kChunk - 1) / kChunk * kChunk;
+    P.lds_ring = (int)off;
+    if (off + ring + kLdsStatic > kLdsMax) ring = (kLdsMax - kLdsStatic - off) / kChunk * kChunk;
+    if (ring < (size_t)kMinRing || ring < 4 * max_tile) return "not enough LDS for the weight ring";
+    // task runs were cut for the ring size used by build_tasks; re-cut if the ring shrank
+    build_tasks(ring);
+    if (P.lds_tasks + (size_t)P.max_tasks * 16 > (size_t)P.lds_trace) return "task list does not fit its LDS slot";
+    P.ring_bytes = (int)ring;
+    P.lds_bytes = off + ring;
+    // attention pieces: at most a quarter of the ring, keys and values each rounded up to whole chunks
+    P.piece_pos = (int)((ring / 4 / 2) / kChunk * kChunk / ((size_t)hd * 2));
+    if (P.piece_pos < 1) return "attention piece too small";
+
     P.table = cur;
     cur = align256(cur + P.iv.size() * sizeof(Interval));
+    P.tasks = cur;
+    cur = align256(cur + P.task_list.size() * sizeof(Task));
+    P.task_idx = cur;
+    cur = align256(cur + P.task_index.size() * sizeof(int32_t));
     P.total = cur;
 
     // workspace
@@ -326,15 +386,17 @@ void build_plan(mbk_model *m) {
             m->rope_host[((size_t)pos * (hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
         }
     m->planned = true;
+    return "";
 }
 
 int ensure_plan(mbk_model *m) {
     if (m->planned) return MBK_OK;
     int rc = ensure_device(m);
     if (rc) return rc;
-    build_plan(m);
+    const std::string why = build_plan(m);
+    if (!why.empty()) return fail(MBK_ERR_UNSUPPORTED, "%s", why.c_str());
     const size_t lds = m->plan.lds_bytes;
-    if (lds > 160 * 1024) return fail(MBK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", lds);
+    if (lds + kLdsStatic > kLdsMax) return fail(MBK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", lds);
     const int G = m->c.n_heads / m->c.n_kv_heads;
     HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -350,18 +412,22 @@ uint32_t next_seq(mbk_model *m) {
 
 Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax) {
     const mbk_config &c = m->c;
+    const Plan &P = m->plan;
     Params p{};
     p.blob = m->blob;
-    p.iv = (const Interval *)(m->blob + m->plan.table);
+    p.iv = (const Interval *)(m->blob + P.table);
+    p.tasks = (const Task *)(m->blob + P.tasks);
+    p.task_idx = (const int32_t *)(m->blob + P.task_idx);
     p.kv = m->kv;
     p.ws = m->ws;
-    p.wl = m->plan.ws;
+    p.wl = P.ws;
     p.logits = logits;
     p.argmax_out = argmax;
-    p.rope = (const float *)(m->blob + m->plan.rope);
-    p.embed = m->plan.embed;
+    p.rope = (const float *)(m->blob + P.rope);
+    p.trace = m->trace;
+    p.embed = P.embed;
     p.n_wg = m->n_wg;
-    p.n_intervals = (int)m->plan.iv.size();
+    p.n_intervals = (int)P.iv.size();
     p.H = c.hidden;
     p.nq = c.n_heads;
     p.nkv = c.n_kv_heads;
@@ -370,18 +436,24 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.V = c.vocab;
     p.S = c.kv_capacity;
     p.NL = c.n_layers;
-    p.max_splits = m->plan.max_splits;
+    p.max_splits = P.max_splits;
     p.gqa = c.n_heads / c.n_kv_heads;
     p.attn_min_chunk = m->attn_min_chunk;
-    p.lds_tab = m->plan.lds_tab;
-    p.lds_rope = m->plan.lds_rope;
-    p.lds_xs = m->plan.lds_xs;
-    p.lds_xres = m->plan.lds_xres;
-    p.lds_bias = m->plan.lds_bias;
-    p.lds_ys = m->plan.lds_ys;
-    p.lds_pf = m->plan.lds_pf;
-    p.pf_bytes = m->plan.pf_bytes;
-    p.trace = m->trace;
+    p.piece_pos = P.piece_pos;
+    p.hd_shift = 0;
+    while ((1 << p.hd_shift) < c.head_dim) ++p.hd_shift;
+    p.lds_ivtab = P.lds_ivtab;
+    p.lds_tasks = P.lds_tasks;
+    p.lds_trace = P.lds_trace;
+    p.lds_rope = P.lds_rope;
+    p.lds_qkv = P.lds_qkv;
+    p.lds_bias = P.lds_bias;
+    p.lds_xs = P.lds_xs;
+    p.lds_xres = P.lds_xres;
+    p.lds_attn = P.lds_attn;
+    p.lds_ring = P.lds_ring;
+    p.ring_bytes = P.ring_bytes;
+    p.max_tasks = P.max_tasks;
     p.eps = c.rms_eps;
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
     p.token = token;
@@ -526,6 +598,9 @@ int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *ds
     HIPCHK(hipMemcpyAsync(m->blob + P.final_norm, src->final_norm, 2u * c.hidden, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(m->blob + P.rope, m->rope_host.data(), m->rope_host.size() * 4, hipMemcpyHostToDevice, st));
     HIPCHK(hipMemcpyAsync(m->blob + P.table, P.iv.data(), P.iv.size() * sizeof(Interval), hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(m->blob + P.tasks, P.task_list.data(), P.task_list.size() * sizeof(Task), hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(m->blob + P.task_idx, P.task_index.data(), P.task_index.size() * sizeof(int32_t),
+                          hipMemcpyHostToDevice, st));
     HIPCHK(hipStreamSynchronize(st));  // host-side sources above must outlive the copies
     return MBK_OK;
 }
