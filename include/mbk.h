@@ -156,6 +156,19 @@ int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */
 int mbk_set_sync_mode(mbk_model *m, int32_t mode);
 
+/* Number of workgroups of the persistent kernel (one per compute unit); n = 0
+ * (default) uses every compute unit of the current device.  Only before the
+ * schedule is planned (the first mbk_pack_weights / mbk_alloc_kv /
+ * mbk_describe); a launch on a device with fewer compute units fails with
+ * MBK_ERR_UNSUPPORTED.  With n > 0 the handle plans without touching a device. */
+int mbk_set_workgroups(mbk_model *m, int32_t n);
+
+/* Plans the schedule if needed and writes a NUL-terminated JSON summary of it
+ * (workgroups, threads, waves per role, intervals, packed/workspace/LDS/ring
+ * bytes, task counts and sizes, attention splits and piece size) into buf.
+ * MBK_ERR_SIZE if len is too small. */
+int mbk_describe(mbk_model *m, char *buf, size_t len);
+
 /* Message for the last non-zero status returned on this thread. */
 const char *mbk_last_error(void);
 

@@ -62,11 +62,13 @@ def lib():
         L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
         L.mbk_set_attention_split.argtypes = [vp, i32]
         L.mbk_set_sync_mode.argtypes = [vp, i32]
+        L.mbk_set_workgroups.argtypes = [vp, i32]
+        L.mbk_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
                   "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
-                  "mbk_set_attention_split", "mbk_set_sync_mode"):
+                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_workgroups", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +192,15 @@ class Decoder:
 
     def set_debug(self, spin_limit: int = 0, skip_wg: int = -1, skip_interval: int = -1) -> None:
         _chk(lib().mbk_set_debug(self.h, spin_limit, skip_wg, skip_interval))
+
+    def set_workgroups(self, n: int) -> None:
+        _chk(lib().mbk_set_workgroups(self.h, n))
+
+    def describe(self) -> dict:
+        import json
+        buf = ctypes.create_string_buffer(4096)
+        _chk(lib().mbk_describe(self.h, buf, len(buf)))
+        return json.loads(buf.value.decode())
 
     def set_sync_mode(self, mode: int) -> None:
         """MBK_SYNC_DATAFLOW (0, default) or MBK_SYNC_BARRIER (1)."""

@@ -68,7 +68,7 @@ struct Params {
     int32_t H, nq, nkv, hd, I, V, S, NL;
     int32_t max_splits, gqa, attn_min_chunk, piece_pos, hd_shift;
     // LDS offsets in bytes of the dynamic area
-    int32_t lds_ivtab, lds_tasks, lds_trace, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_ring;
+    int32_t lds_ivtab, lds_tasks, lds_trace, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
     int32_t ring_bytes, max_tasks;
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
     int32_t token, pos;       // token < 0: previous device argmax
@@ -131,6 +131,9 @@ MBK_DEV uint32_t ord_key(float f) {
 
 // LDS byte address of a pointer into LDS.
 MBK_DEV uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(const lds_void_t *)p; }
+
+// Index of the calling wave in its workgroup, known to the compiler as wave-uniform.
+MBK_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // LDS accesses the compiler cannot see: used by loader waves, whose
 // outstanding direct-to-LDS loads would otherwise be drained before each one.
@@ -263,14 +266,34 @@ MBK_DEV bool grid_barrier(const Params &p, uint32_t epoch) {
 }
 
 // ---- reductions ----------------------------------------------------------------------------------
-// Butterfly sums over groups of N consecutive lanes.  Steps inside 16 lanes
-// use DPP moves: after the xor-1 and xor-2 steps every quad is uniform, so a
-// half-row mirror (lane i <-> 7-i) pairs quad 0 with quad 1, and after that a
-// row mirror (i <-> 15-i) pairs the two halves of a 16-lane row.  The 16- and
-// 32-lane steps go through the LDS crossbar.
+// Butterfly sums over groups of N consecutive lanes, all on the VALU.  Steps
+// inside 16 lanes use DPP moves: after the xor-1 and xor-2 steps every quad is
+// uniform, so a half-row mirror (lane i <-> 7-i) pairs quad 0 with quad 1,
+// and after that a row mirror (i <-> 15-i) pairs the two halves of a 16-lane
+// row.  The 16- and 32-lane steps use the gfx950 lane swaps: permlane16_swap
+// returns, in every lane, its own value and the value 16 lanes away (rows
+// 2k, 2k+1 exchanged), permlane32_swap likewise for the two wave halves.
 
 template <int CTRL> MBK_DEV float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// v + (the value 16 lanes away), v + (the value 32 lanes away); max forms.
+MBK_DEV float xsum16(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+MBK_DEV float xsum32(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+MBK_DEV float xmax16(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+MBK_DEV float xmax32(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
 template <int N> MBK_DEV float group_sum(float v) {
@@ -278,8 +301,8 @@ template <int N> MBK_DEV float group_sum(float v) {
     if constexpr (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
     if constexpr (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
     if constexpr (N >= 16) v += dpp<0x140>(v);  // row_mirror
-    if constexpr (N >= 32) v += __shfl_xor(v, 16);
-    if constexpr (N >= 64) v += __shfl_xor(v, 32);
+    if constexpr (N >= 32) v = xsum16(v);
+    if constexpr (N >= 64) v = xsum32(v);
     return v;
 }
 
@@ -313,7 +336,7 @@ MBK_DEV int step_pos(const Params &p) {
 // compute waves derive the same sequence of allocations from the task list
 // and the step's position.  An allocation is placed at the current virtual
 // ring offset, or at the next multiple of the ring size if it would straddle
-// the ring's end; allocations are at most a quarter of the ring (a loader
+// the ring's end; allocations are at most a third of the ring (a loader
 // waiting for space then always waits for data the compute waves will
 // release, and several allocations stream at once).
 
@@ -375,10 +398,12 @@ MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, int
     return A;
 }
 
-MBK_DEV int n_chunks(const Alloc &A) { return (int)((A.b0 + kChunk - 1) / kChunk + (A.b1 + kChunk - 1) / kChunk); }
-
-// Chunks of an allocation handled by loader wave w (chunk c goes to wave c % kLW).
-MBK_DEV uint32_t wave_chunks(int nch, int w) { return nch > w ? (uint32_t)((nch - w + kLW - 1) / kLW) : 0u; }
+// Chunks of a segment of `bytes` handled by loader wave w: chunk c of every
+// segment goes to wave c % kLW.
+MBK_DEV uint32_t wave_chunks(uint32_t bytes, int w) {
+    const int nch = (int)((bytes + kChunk - 1) / kChunk);
+    return nch > w ? (uint32_t)((nch - w + kLW - 1) / kLW) : 0u;
+}
 
 // Virtual start of an allocation of `size` bytes after offset v.
 MBK_DEV uint32_t ring_place(uint32_t v, uint32_t size, uint32_t R) {
@@ -417,28 +442,54 @@ MBK_DEV Task task_opaque(const uint8_t *lds, const Params &p, int k) {
     return t;
 }
 
-// One wave copies `bytes` (multiple of 16, > 0) from global src to LDS dst,
-// one 16-byte element per lane per instruction; the chunk is counted by the caller.
-MBK_DEV void dma_chunk(const uint8_t *src, uint8_t *dst, uint32_t bytes, uint32_t aux_sc1) {
+// Loader wave lw's share of one segment: chunks lw, lw + kLW, ... of `bytes`
+// (a multiple of 16) from global src to LDS dst, 16 bytes per lane per
+// chunk; the last chunk may be partial.  Every kBatch chunks the wave waits
+// until at most kInflight of its chunks are in flight and publishes the
+// count of its completed chunks.
+template <int SC1>
+MBK_DEV void dma_segment(const uint8_t *src, uint8_t *dst, uint32_t bytes, int lw, Ctl &ctl, uint32_t &issued,
+                         uint32_t &published, int &inbatch) {
     const int lane = threadIdx.x & 63;
-    if ((uint32_t)lane * 16u < bytes) {
-        if (aux_sc1)
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)dst, 16, 0, (int)kCacheSc1);
-        else
-            __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)dst, 16, 0, 0);
+    const int full = (int)(bytes / kChunk);
+    const uint8_t *g = src + lane * 16;
+    for (int c = lw; c < full; c += kLW) {
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)c * kChunk), (lds_void_t *)(dst + c * kChunk), 16, 0,
+                                         SC1 ? (int)kCacheSc1 : 0);
+        ++issued;
+        if (++inbatch == kBatch) {
+            inbatch = 0;
+            asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // kInflight
+            if (issued - (uint32_t)kInflight > published && issued > (uint32_t)kInflight) {
+                published = issued - (uint32_t)kInflight;
+                lds_st_opaque(&ctl.prog[lw], published);
+            }
+        }
+    }
+    const uint32_t rest = bytes - (uint32_t)full * kChunk;
+    if (rest && full % kLW == lw) {
+        if ((uint32_t)lane * 16u < rest)
+            __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)full * kChunk), (lds_void_t *)(dst + full * kChunk), 16,
+                                             0, SC1 ? (int)kCacheSc1 : 0);
+        ++issued;
+        ++inbatch;
     }
 }
 
 // Loader wave lw: streams every allocation of tasks [0, nt) into the ring.
 MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
-    const int lw = (int)(threadIdx.x >> 6) - kCW;
+    const int lw = wave_id() - kCW;
     const uint32_t R = (uint32_t)p.ring_bytes;
     uint8_t *ring = lds + p.lds_ring;
     uint32_t vpos = 0, issued = 0, published = 0, cons_seen = 0;
-    int inbatch = 0;
+    int inbatch = 0, cur = -1;
+    Interval iv;
     for (int k = 0; k < nt; ++k) {
         const Task T = task_opaque(lds, p, k);
-        const Interval iv = interval_opaque(p, lds, T.iv);
+        if (T.iv != cur) {
+            iv = interval_opaque(p, lds, T.iv);
+            cur = T.iv;
+        }
         const int na = n_allocs(p, iv, T, pos);
         const uint32_t sc1 = iv.op == OP_ATTN ? 1u : 0u;
         for (int ai = 0; ai < na; ++ai) {
@@ -482,20 +533,11 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
                 inbatch = 0;
             }
             uint8_t *base = ring + (start % R);
-            const int n0 = (int)((A.b0 + kChunk - 1) / kChunk), nch = n0 + (int)((A.b1 + kChunk - 1) / kChunk);
-            for (int c = lw; c < nch; c += kLW) {
-                if (c < n0) dma_chunk(A.g0 + (size_t)c * kChunk, base + (size_t)c * kChunk, min((uint32_t)kChunk, A.b0 - (uint32_t)c * kChunk), sc1);
-                else dma_chunk(A.g1 + (size_t)(c - n0) * kChunk, base + A.r1 + (size_t)(c - n0) * kChunk,
-                               min((uint32_t)kChunk, A.b1 - (uint32_t)(c - n0) * kChunk), sc1);
-                ++issued;
-                if (++inbatch == kBatch) {
-                    inbatch = 0;
-                    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // kInflight
-                    if (issued > (uint32_t)kInflight && issued - (uint32_t)kInflight > published) {
-                        published = issued - (uint32_t)kInflight;
-                        lds_st_opaque(&ctl.prog[lw], published);
-                    }
-                }
+            if (sc1) {
+                dma_segment<1>(A.g0, base, A.b0, lw, ctl, issued, published, inbatch);
+                if (A.b1) dma_segment<1>(A.g1, base + A.r1, A.b1, lw, ctl, issued, published, inbatch);
+            } else {
+                dma_segment<0>(A.g0, base, A.b0, lw, ctl, issued, published, inbatch);
             }
             vpos = end;
         }
@@ -529,9 +571,8 @@ struct RingPos {
 MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Alloc &A) {
     const uint32_t start = ring_place(rp.vpos, A.size, (uint32_t)p.ring_bytes);
     rp.vpos = start + A.size;
-    const int nch = n_chunks(A);
 #pragma unroll
-    for (int w = 0; w < kLW; ++w) rp.cum[w] += wave_chunks(nch, w);
+    for (int w = 0; w < kLW; ++w) rp.cum[w] += wave_chunks(A.b0, w) + wave_chunks(A.b1, w);
 #pragma unroll
     for (int w = 0; w < kLW; ++w) {
         for (int it = 0; (int32_t)(lds_ld(&ctl.prog[w]) - rp.cum[w]) < 0; ++it) {
@@ -543,7 +584,7 @@ MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Allo
     return start;
 }
 
-MBK_DEV void ring_release(Ctl &ctl, const RingPos &rp) { lds_st(&ctl.cons[threadIdx.x >> 6], rp.vpos); }
+MBK_DEV void ring_release(Ctl &ctl, const RingPos &rp) { lds_st(&ctl.cons[wave_id()], rp.vpos); }
 
 // ---- GEMV input vectors ------------------------------------------------------------------------------
 // GEMV input vectors live in LDS as bf16 pairs: each 8-element group g is 32
@@ -758,7 +799,7 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
         const uint64_t o = ((uint64_t)__shfl_xor((uint32_t)(best >> 32), m) << 32) | __shfl_xor((uint32_t)best, m);
         best = o > best ? o : best;
     }
-    const int cw = threadIdx.x >> 6;
+    const int cw = wave_id();
     if ((threadIdx.x & 63) == 0) ctl.best[cw] = best;
     if (!cw_barrier(p, ctl, sc.gen)) return false;
     if (threadIdx.x == 0) {
@@ -852,42 +893,52 @@ MBK_DEV void attn_inputs(const Params &p, int item, int ivi, uint8_t *lds, const
 // G query heads of the group packed together so each key and value is read
 // once (README mirror, "Current status": flash decoding, query heads sharing
 // a KV head packed at long context).  Lane (slot, dl) of a compute wave
-// takes one position per block and head dims dl*8 .. dl*8+7; the compute
-// waves take alternate blocks.  Each lane keeps a running (max, sum, acc)
-// per head; lanes, then waves, are combined by the log-sum-exp merge.
+// takes one position per block and head dims dl*8 .. dl*8+7 (LP = hd/8
+// lanes per position); the compute waves take alternate blocks.  Positions
+// arrive in segments (the ring pieces, the last one extended by the position
+// appended this step).  Per segment: the scores go to LDS; one maximum per
+// head is formed over the whole workgroup; then exp(score - max) weights the
+// values.  With one shared maximum the lanes' and waves' sums combine by
+// plain addition; a new segment rescales the running sums once when the
+// maximum grows.
 
-struct AttnState {
-    float m, l, acc[8];
-};
-
-MBK_DEV void lse_merge(AttnState &a, float m2, float l2, const float *acc2) {
-    const float mn = fmaxf(a.m, m2);
-    if (mn == -INFINITY) return;
-    const float c1 = __expf(a.m - mn), c2 = __expf(m2 - mn);
-    a.l = a.l * c1 + l2 * c2;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a.acc[e] = a.acc[e] * c1 + acc2[e] * c2;
-    a.m = mn;
+// K and V of position t of a segment: ring positions t < nring (bf16), then
+// the appended position (fp32 in LDS).
+MBK_DEV void seg_kv(int t, int nring, const uint8_t *kb, const uint8_t *vb, const float *cur, int hd, int dl,
+                    float *kf, float *vf) {
+    if (t < nring) {
+        unpack8(*(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16), kf);
+        unpack8(*(const u32x4 *)(vb + (size_t)t * hd * 2 + dl * 16), vf);
+    } else {
+        const float4 a = *(const float4 *)(cur + dl * 8), b = *(const float4 *)(cur + dl * 8 + 4);
+        const float4 c = *(const float4 *)(cur + hd + dl * 8), d = *(const float4 *)(cur + hd + dl * 8 + 4);
+        kf[0] = a.x; kf[1] = a.y; kf[2] = a.z; kf[3] = a.w; kf[4] = b.x; kf[5] = b.y; kf[6] = b.z; kf[7] = b.w;
+        vf[0] = c.x; vf[1] = c.y; vf[2] = c.z; vf[3] = c.w; vf[4] = d.x; vf[5] = d.y; vf[6] = d.z; vf[7] = d.w;
+    }
 }
 
-// One position for every head: kf/vf are this lane's 8 dims of the key and value.
-template <int G>
-MBK_DEV void attend_one(AttnState (&st)[G], const float (&qf)[G][8], const float *kf, const float *vf, bool valid, int LP) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
-        d = group_sum_n(d, LP);
-        if (valid) {
-            const float mn = fmaxf(st[h].m, d);
-            const float c = __expf(st[h].m - mn), w = __expf(d - mn);
-            st[h].l = st[h].l * c + w;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st[h].acc[e] = fmaf(w, vf[e], st[h].acc[e] * c);
-            st[h].m = mn;
-        }
-    }
+// Sum (max) over the slots of a wave: the lanes with the same lane % LP.
+// Inside a 16-lane row the slots are combined by rotating the row by 2, 4
+// and 8 lanes (each step doubles the slots covered), then rows by the lane
+// swaps.
+MBK_DEV float slot_sum(float v, int LP) {
+    if (LP <= 1) v += dpp<0x121>(v);   // row_ror:1
+    if (LP <= 2) v += dpp<0x122>(v);   // row_ror:2
+    if (LP <= 4) v += dpp<0x124>(v);   // row_ror:4
+    if (LP <= 8) v += dpp<0x128>(v);   // row_ror:8
+    return xsum32(xsum16(v));
+}
+MBK_DEV float slot_max(float v, int LP) {
+    if (LP <= 1) v = fmaxf(v, dpp<0x121>(v));
+    if (LP <= 2) v = fmaxf(v, dpp<0x122>(v));
+    if (LP <= 4) v = fmaxf(v, dpp<0x124>(v));
+    if (LP <= 8) v = fmaxf(v, dpp<0x128>(v));
+    return xmax32(xmax16(v));
+}
+
+// Tagged 16-byte store of entries i, i+1 (i even).
+MBK_DEV void put2(const Params &p, uint64_t base, int i, float a, float b, uint32_t tag) {
+    stc16(p.ws, (uint32_t)(base + 8u * (uint32_t)i), (u32x4){__float_as_uint(a), tag, __float_as_uint(b), tag});
 }
 
 // One attention item.  False when a wait failed.
@@ -895,11 +946,15 @@ template <int G>
 MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const Task &T, uint8_t *lds, Ctl &ctl,
                             RingPos &rp, StepCtx &sc) {
     const int pos = sc.pos, hd = p.hd, LP = hd / 8, PPW = 64 / LP;
-    const int lane = threadIdx.x & 63, cw = threadIdx.x >> 6, dl = lane % LP, slot = lane / LP;
+    const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane % LP, slot = lane / LP;
     const int j = T.a / p.max_splits, s = T.a % p.max_splits;
     const Split sp = split_range(p, s, pos);
     if (s >= sp.nsplit) return true;  // no allocations either
     const float *qkv = (const float *)(lds + p.lds_qkv);
+    const float *cur = qkv + G * hd;        // this step's key, then value
+    float *scores = (float *)(lds + p.lds_score);   // [G][piece_pos + 1]
+    float *wmax = scores + G * (p.piece_pos + 1);   // [2][kCW][G]
+    const int sstride = p.piece_pos + 1;
     float qf[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -907,66 +962,105 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
         qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
     }
-    AttnState st[G];
+    float M[G], l[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        st[h].m = -INFINITY;
-        st[h].l = 0.f;
+        M[h] = -INFINITY;
+        l[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st[h].acc[e] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
     const uint8_t *ring = lds + p.lds_ring;
     const int na = n_allocs(p, iv, T, pos);
-    for (int k = 0; k < na; ++k) {
-        const Alloc A = task_alloc(p, iv, T, pos, k);
-        const uint32_t start = ring_acquire(p, ctl, rp, A);
-        if (start == ~0u) return false;
-        const uint8_t *kb = ring + start % (uint32_t)p.ring_bytes, *vb = kb + A.r1;
-        const int np = (int)(A.b0 / (uint32_t)(hd * 2));
-        for (int b = cw; b * PPW < np; b += kCW) {
+    const bool has_cur = pos >= sp.t0 && pos < sp.t1;
+    const int nseg = na > 0 ? na : (has_cur ? 1 : 0);
+    for (int k = 0; k < nseg; ++k) {
+        const uint8_t *kb = nullptr, *vb = nullptr;
+        int nring = 0;
+        if (k < na) {
+            const Alloc A = task_alloc(p, iv, T, pos, k);
+            const uint32_t start = ring_acquire(p, ctl, rp, A);
+            if (start == ~0u) return false;
+            kb = ring + start % (uint32_t)p.ring_bytes;
+            vb = kb + A.r1;
+            nring = (int)(A.b0 / (uint32_t)(hd * 2));
+        }
+        const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
+        // scores of this segment
+        float lmax[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
+        for (int b = cw; b * PPW < npos; b += kCW) {
             const int t = b * PPW + slot;
-            const bool valid = t < np;
             float kf[8], vf[8];
-            if (valid) {
-                unpack8(*(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16), kf);
-                unpack8(*(const u32x4 *)(vb + (size_t)t * hd * 2 + dl * 16), vf);
-            } else {
+            if (t < npos) seg_kv(t, nring, kb, vb, cur, hd, dl, kf, vf);
+            else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kf[e] = vf[e] = 0.f;
+                for (int e = 0; e < 8; ++e) kf[e] = 0.f;
             }
-            attend_one<G>(st, qf, kf, vf, valid, LP);
-        }
-        ring_release(ctl, rp);
-    }
-    // the position appended this step (its key and value came with the inputs)
-    if (pos >= sp.t0 && pos < sp.t1 && cw == 0) {
-        float kf[8], vf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kf[e] = qkv[G * hd + dl * 8 + e];
-            vf[e] = qkv[(G + 1) * hd + dl * 8 + e];
-        }
-        attend_one<G>(st, qf, kf, vf, slot == 0, LP);
-    }
-    // merge the slots of the wave (lanes LP apart), then the compute waves in LDS
+            for (int h = 0; h < G; ++h) {
+                float d = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        for (int msk = LP; msk < 64; msk <<= 1) {
-            float acc2[8];
-            const float m2 = __shfl_xor(st[h].m, msk), l2 = __shfl_xor(st[h].l, msk);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc2[e] = __shfl_xor(st[h].acc[e], msk);
-            lse_merge(st[h], m2, l2, acc2);
+                for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
+                d = group_sum_n(d, LP);
+                if (t < npos) {
+                    lmax[h] = fmaxf(lmax[h], d);
+                    if (dl == 0) scores[h * sstride + t] = d;
+                }
+            }
         }
-    }
-    const int stride = hd + 4;
-    float *scr = (float *)(lds + p.lds_attn);  // [kCW][G][stride]
-    if (slot == 0) {
+        // one maximum per head over the workgroup
+        float *wm = wmax + (k & 1) * kCW * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            const float m = slot_max(lmax[h], LP);
+            if (lane == 0) wm[cw * G + h] = m;
+        }
+        if (!cw_barrier(p, ctl, sc.gen)) return false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float m = wm[h];
+            for (int w = 1; w < kCW; ++w) m = fmaxf(m, wm[w * G + h]);
+            const float mn = fmaxf(M[h], m);
+            if (mn != M[h]) {
+                const float c = __expf(M[h] - mn);  // 0 while M is -inf
+                l[h] *= c;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= c;
+                M[h] = mn;
+            }
+        }
+        // weights and values
+        for (int b = cw; b * PPW < npos; b += kCW) {
+            const int t = b * PPW + slot;
+            if (t >= npos) continue;
+            float kf[8], vf[8];
+            seg_kv(t, nring, kb, vb, cur, hd, dl, kf, vf);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float w = __expf(scores[h * sstride + t] - M[h]);
+                l[h] += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+            }
+        }
+        if (k < na) ring_release(ctl, rp);
+        // the scores are rewritten by the next segment
+        if (k + 1 < nseg && !cw_barrier(p, ctl, sc.gen)) return false;
+    }
+    // sums over the slots, then over the compute waves in LDS
+    const int stride = hd + 4;
+    float *scr = (float *)(lds + p.lds_attn);  // [kCW][G][stride]
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] = slot_sum(l[h], LP);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum(acc[h][e], LP);
+        if (slot == 0) {
             float *r = scr + ((size_t)cw * G + h) * stride;
-            if (dl == 0) { r[0] = st[h].m; r[1] = st[h].l; }
-            store8(r + 4 + dl * 8, st[h].acc);
+            if (dl == 0) r[1] = l[h];
+            store8(r + 4 + dl * 8, acc[h]);
         }
     }
     if (!cw_barrier(p, ctl, sc.gen)) return false;
@@ -974,26 +1068,28 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     if (cw == 0 && slot == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            AttnState a;
-            a.m = scr[h * stride];
-            a.l = scr[h * stride + 1];
+            float ll = 0.f, a[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a.acc[e] = scr[h * stride + 4 + dl * 8 + e];
-            for (int w = 1; w < kCW; ++w) {
+            for (int e = 0; e < 8; ++e) a[e] = 0.f;
+            for (int w = 0; w < kCW; ++w) {
                 const float *r = scr + ((size_t)w * G + h) * stride;
-                lse_merge(a, r[0], r[1], r + 4 + dl * 8);
-            }
-            if (sp.nsplit == 1) {
+                ll += r[1];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) put(p, p.wl.o, (j * G + h) * hd + dl * 8 + e, a.acc[e] / a.l, tag);
+                for (int e = 0; e < 8; ++e) a[e] += r[4 + dl * 8 + e];
+            }
+            const int o0 = (j * G + h) * hd + dl * 8;
+            if (sp.nsplit == 1) {
+                const float inv = 1.f / ll;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) put2(p, p.wl.o, o0 + e, a[e] * inv, a[e + 1] * inv, tag);
             } else {
-                // this split's partial: part[j][s][h][stride] = {m, l, -, -, acc[hd]}
+                // this split's partial: part[j][s][h][stride] = {max, sum, -, -, acc[hd]}
                 const uint64_t pb = p.wl.part + ((uint64_t)(j * p.max_splits + s) * G + h) * stride * 4u;
-                if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(a.m), __float_as_uint(a.l), 0u, 0u});
-                stc16(p.ws, (uint32_t)(pb + 16u + 32u * dl), (u32x4){__float_as_uint(a.acc[0]), __float_as_uint(a.acc[1]),
-                                                                     __float_as_uint(a.acc[2]), __float_as_uint(a.acc[3])});
-                stc16(p.ws, (uint32_t)(pb + 32u + 32u * dl), (u32x4){__float_as_uint(a.acc[4]), __float_as_uint(a.acc[5]),
-                                                                     __float_as_uint(a.acc[6]), __float_as_uint(a.acc[7])});
+                if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(M[h]), __float_as_uint(ll), 0u, 0u});
+                stc16(p.ws, (uint32_t)(pb + 16u + 32u * dl), (u32x4){__float_as_uint(a[0]), __float_as_uint(a[1]),
+                                                                     __float_as_uint(a[2]), __float_as_uint(a[3])});
+                stc16(p.ws, (uint32_t)(pb + 32u + 32u * dl), (u32x4){__float_as_uint(a[4]), __float_as_uint(a[5]),
+                                                                     __float_as_uint(a[6]), __float_as_uint(a[7])});
             }
         }
     }
@@ -1018,19 +1114,20 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             for (int idx = threadIdx.x; idx < n16; idx += kCW * 64)
                 *(u32x4 *)(scr + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
             if (!cw_barrier(p, ctl, sc.gen)) return false;
-            for (int idx = threadIdx.x; idx < G * hd; idx += kCW * 64) {
+            for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
                 const int h = idx / hd, e = idx % hd;
-                float mm = -INFINITY, ll = 0.f, aa = 0.f;
+                float mm = -INFINITY, ll = 0.f, a0 = 0.f, a1 = 0.f;
                 for (int q = 0; q < sp.nsplit; ++q) {
                     const float *r = scr + ((size_t)q * G + h) * stride;
                     const float m2 = r[0], mn = fmaxf(mm, m2);
                     if (mn == -INFINITY) continue;
                     const float c1 = __expf(mm - mn), c2 = __expf(m2 - mn);
                     ll = ll * c1 + r[1] * c2;
-                    aa = aa * c1 + r[4 + e] * c2;
+                    a0 = a0 * c1 + r[4 + e] * c2;
+                    a1 = a1 * c1 + r[5 + e] * c2;
                     mm = mn;
                 }
-                put(p, p.wl.o, (j * G + h) * hd + e, aa / ll, tag);
+                put2(p, p.wl.o, (j * G + h) * hd + e, a0 / ll, a1 / ll, tag);
             }
         }
     }
@@ -1069,7 +1166,7 @@ MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &s
     rp.vpos = 0;
 #pragma unroll
     for (int w = 0; w < kLW; ++w) rp.cum[w] = 0;
-    const int cw = threadIdx.x >> 6;
+    const int cw = wave_id();
     int k = 0;
     for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
         if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return false;
@@ -1189,7 +1286,7 @@ MBK_DEV void run_step(const Params &p) {
     __shared__ Ctl ctl;
     const int pos = step_pos(p);
     const int nt = prologue(p, lds, ctl, pos);
-    if ((int)(threadIdx.x >> 6) >= kCW) {
+    if (wave_id() >= kCW) {
         loader(p, lds, ctl, nt, pos);
     } else {
         StepCtx sc;

@@ -11,7 +11,7 @@
 
 namespace mbk {
 
-constexpr int kThreads = 384;          // threads per workgroup (6 wave64)
+constexpr int kThreads = 512;          // threads per workgroup (8 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kCW = 4;                 // compute waves (0 .. kCW-1): poll inputs, compute, publish
 constexpr int kLW = kWaves - kCW;      // loader waves: stream this workgroup's future weights into LDS

@@ -115,7 +115,7 @@ struct Plan {
     int max_splits = 1, piece_pos = 1, max_tasks = 0;
     // LDS layout (bytes of the dynamic area)
     int lds_ivtab = 0, lds_tasks = 0, lds_trace = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
-        lds_xres = 0, lds_attn = 0, lds_ring = 0, ring_bytes = 0;
+        lds_xres = 0, lds_attn = 0, lds_score = 0, lds_ring = 0, ring_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
 };
@@ -137,6 +137,8 @@ struct mbk_model {
     int32_t sync_mode = MBK_SYNC_DATAFLOW;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
     int32_t attn_min_chunk = 128;
+    int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
+    bool kernels_ready = false;
     uint64_t *trace = nullptr;
     // graph replay of the ablation
     hipGraph_t graph = nullptr;
@@ -175,8 +177,14 @@ Interval gemv_interval(int op, int layer, const MatGeom &g, uint64_t norm, uint6
     return v;
 }
 
+// Workgroup count: the value set with mbk_set_workgroups, else the current
+// device's compute units.
 int ensure_device(mbk_model *m) {
     if (m->n_wg > 0) return MBK_OK;
+    if (m->n_wg_set > 0) {
+        m->n_wg = m->n_wg_set;
+        return MBK_OK;
+    }
     HIPCHK(hipGetDevice(&m->device));
     int cus = 0;
     HIPCHK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m->device));
@@ -185,9 +193,26 @@ int ensure_device(mbk_model *m) {
     return MBK_OK;
 }
 
+// Launch attributes of the kernels for this plan (once per handle, on the current device).
+int ensure_kernels(mbk_model *m) {
+    if (m->kernels_ready) return MBK_OK;
+    int cus = 0, dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    HIPCHK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if (m->n_wg > cus)
+        return fail(MBK_ERR_UNSUPPORTED, "%d workgroups requested but the device has %d compute units", m->n_wg, cus);
+    const int G = m->c.n_heads / m->c.n_kv_heads;
+    const int lds = (int)m->plan.lds_bytes;
+    HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    m->kernels_ready = true;
+    return MBK_OK;
+}
+
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr size_t kLdsStatic = 512;      // Ctl and the other static LDS words of the kernels
 constexpr int kMinRing = 16 * 1024;
+constexpr int kPiecePos = 128;          // most cached positions per attention piece
 
 size_t a16(size_t v) { return (v + 15) / 16 * 16; }
 
@@ -279,15 +304,16 @@ std::string build_plan(mbk_model *m) {
     fixed += a16((size_t)kmax * 4);                                // GEMV input (hi/lo pairs)
     fixed += a16((size_t)max_rows * 4);                            // residual rows
     fixed += a16((size_t)std::max(kCW, ms) * G * stride * 4);      // attention merge scratch
+    fixed += a16(((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);  // attention scores and maxima
 
-    // tile runs of at most a quarter of the ring: first size the ring assuming a task
+    // tile runs of at most a third of the ring: first size the ring assuming a task
     // list of 64 entries per workgroup, then build the lists and shrink the ring
     // to what the lists leave.
     size_t max_tile = 0;
     for (const Interval &v : P.iv)
         if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.IT * kChunk);
     auto build_tasks = [&](size_t ring) {
-        const size_t max_alloc = ring / 4;
+        const size_t max_alloc = ring / 3;
         P.task_list.clear();
         P.task_index.assign((size_t)n_wg * (n_iv + 1), 0);
         int max_tasks = 0;
@@ -319,13 +345,13 @@ std::string build_plan(mbk_model *m) {
     const size_t avail0 = kLdsMax - kLdsStatic - task_slot - fixed;
     size_t ring = avail0 > (size_t)64 * 16 ? (avail0 - 64 * 16) / kChunk * kChunk : 0;
     for (int iter = 0; iter < 4; ++iter) {
-        if (ring < (size_t)kMinRing || ring < 4 * max_tile) break;
+        if (ring < (size_t)kMinRing || ring < 3 * max_tile) break;
         build_tasks(ring);
         const size_t need = task_slot + a16((size_t)P.max_tasks * 16) + fixed;
         if (need + kLdsStatic + ring <= kLdsMax) break;
         ring = need + kLdsStatic < kLdsMax ? (kLdsMax - kLdsStatic - need) / kChunk * kChunk : 0;
     }
-    if (ring < (size_t)kMinRing || ring < 4 * max_tile)
+    if (ring < (size_t)kMinRing || ring < 3 * max_tile)
         return "not enough LDS for the weight ring (" + std::to_string(ring) + " bytes)";
     build_tasks(ring);
     off = task_slot;
@@ -337,17 +363,18 @@ std::string build_plan(mbk_model *m) {
     P.lds_xs = (int)off; off = a16(off + (size_t)kmax * 4);
     P.lds_xres = (int)off; off = a16(off + (size_t)max_rows * 4);
     P.lds_attn = (int)off; off = a16(off + (size_t)std::max(kCW, ms) * G * stride * 4);
+    P.lds_score = (int)off; off = a16(off + ((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);
     off = (off + kChunk - 1) / kChunk * kChunk;
     P.lds_ring = (int)off;
     if (off + ring + kLdsStatic > kLdsMax) ring = (kLdsMax - kLdsStatic - off) / kChunk * kChunk;
-    if (ring < (size_t)kMinRing || ring < 4 * max_tile) return "not enough LDS for the weight ring";
+    if (ring < (size_t)kMinRing || ring < 3 * max_tile) return "not enough LDS for the weight ring";
     // task runs were cut for the ring size used by build_tasks; re-cut if the ring shrank
     build_tasks(ring);
     if (P.lds_tasks + (size_t)P.max_tasks * 16 > (size_t)P.lds_trace) return "task list does not fit its LDS slot";
     P.ring_bytes = (int)ring;
     P.lds_bytes = off + ring;
-    // attention pieces: at most a quarter of the ring, keys and values each rounded up to whole chunks
-    P.piece_pos = (int)((ring / 4 / 2) / kChunk * kChunk / ((size_t)hd * 2));
+    // attention pieces: at most a third of the ring, keys and values each rounded up to whole chunks
+    P.piece_pos = std::min(kPiecePos, (int)((ring / 3 / 2) / kChunk * kChunk / ((size_t)hd * 2)));
     if (P.piece_pos < 1) return "attention piece too small";
 
     P.table = cur;
@@ -397,9 +424,6 @@ int ensure_plan(mbk_model *m) {
     if (!why.empty()) return fail(MBK_ERR_UNSUPPORTED, "%s", why.c_str());
     const size_t lds = m->plan.lds_bytes;
     if (lds + kLdsStatic > kLdsMax) return fail(MBK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", lds);
-    const int G = m->c.n_heads / m->c.n_kv_heads;
-    HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     return MBK_OK;
 }
 
@@ -451,6 +475,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.lds_xs = P.lds_xs;
     p.lds_xres = P.lds_xres;
     p.lds_attn = P.lds_attn;
+    p.lds_score = P.lds_score;
     p.lds_ring = P.lds_ring;
     p.ring_bytes = P.ring_bytes;
     p.max_tasks = P.max_tasks;
@@ -633,7 +658,7 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
 
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream) {
     int rc = check_step_args(m, token, pos, argmax);
-    if (rc) return rc;
+    if (rc || (rc = ensure_kernels(m))) return rc;
     next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
     void *args[] = {&p};
@@ -646,7 +671,7 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
 int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax,
                              int32_t use_graph, void *stream) {
     int rc = check_step_args(m, token, pos, argmax);
-    if (rc) return rc;
+    if (rc || (rc = ensure_kernels(m))) return rc;
     hipStream_t st = (hipStream_t)stream;
     next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
@@ -739,6 +764,8 @@ int mbk_set_attention_split(mbk_model *m, int32_t min_positions) {
 int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier) {
     if (!m || !us_per_barrier || n <= 0) return fail(MBK_ERR_ARG, "bad arguments");
     if (!m->ws || !m->blob) return fail(MBK_ERR_STATE, "workspace not bound");
+    int rc = ensure_kernels(m);
+    if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t e0, e1;
     HIPCHK(hipEventCreate(&e0));
@@ -759,6 +786,36 @@ int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barri
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     *us_per_barrier = (t[1] - t[0]) * 1000.f / (float)n;
+    return MBK_OK;
+}
+
+int mbk_set_workgroups(mbk_model *m, int32_t n) {
+    if (!m || n < 0) return fail(MBK_ERR_ARG, "bad arguments");
+    if (m->planned && n != (m->n_wg_set ? m->n_wg_set : m->n_wg) && !(n == 0 && m->n_wg_set == 0))
+        return fail(MBK_ERR_STATE, "the schedule is already planned for %d workgroups", m->n_wg);
+    if (n > 0 && n < 1) return fail(MBK_ERR_ARG, "need at least one workgroup");
+    m->n_wg_set = n;
+    return MBK_OK;
+}
+
+int mbk_describe(mbk_model *m, char *buf, size_t len) {
+    if (!m || !buf || len == 0) return fail(MBK_ERR_ARG, "bad arguments");
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    const Plan &P = m->plan;
+    size_t tile_max = 0, task_max = 0;
+    for (const Interval &v : P.iv)
+        if (v.op != OP_ATTN) tile_max = std::max(tile_max, (size_t)v.mat.IT * kChunk);
+    for (const Task &t : P.task_list)
+        if (P.iv[t.iv].op != OP_ATTN) task_max = std::max(task_max, (size_t)t.n * P.iv[t.iv].mat.IT * kChunk);
+    const int n = snprintf(buf, len,
+        "{\"workgroups\": %d, \"threads\": %d, \"compute_waves\": %d, \"loader_waves\": %d, \"intervals\": %zu, "
+        "\"packed_bytes\": %llu, \"workspace_bytes\": %llu, \"lds_bytes\": %zu, \"ring_bytes\": %d, "
+        "\"max_tasks\": %d, \"tasks\": %zu, \"max_task_bytes\": %zu, \"max_tile_bytes\": %zu, "
+        "\"max_splits\": %d, \"piece_positions\": %d}",
+        m->n_wg, kThreads, kCW, kLW, P.iv.size(), (unsigned long long)P.total, (unsigned long long)P.ws.total,
+        P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos);
+    if (n < 0 || (size_t)n >= len) return fail(MBK_ERR_SIZE, "description needs %d bytes", n + 1);
     return MBK_OK;
 }
 
