@@ -53,7 +53,7 @@ def phase_breakdown(dec, wl, positions, logits, am, steps=8, dump=""):
         t = tr.cpu().numpy().astype(np.int64)          # [iv][wg][4]
         raw.append(t.copy())
         n_iv = t.shape[0]
-        prev_done = t[0, :, 0].min()
+        prev_done = t[0, t[0, :, 0] > 0, 0].min()
         for iv in range(n_iv):
             op = "lmhead" if iv == n_iv - 1 else OPS[iv % 5]
             work = t[iv, :, 1] > 0
@@ -93,6 +93,10 @@ def main():
                     help="interval ordering of the persistent kernel (the other mode is timed as an extra)")
     ap.add_argument("--phase", action="store_true", help="print a per-operator phase-timer breakdown to stderr")
     ap.add_argument("--phase-dump", default="", help="also save the raw phase-timer arrays (.npy) to this path")
+    ap.add_argument("--attn-split", type=int, default=0, help="attention split size in positions (0: library default)")
+    ap.add_argument("--no-other-mode", action="store_true", help="skip timing the other sync mode")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -116,6 +120,8 @@ def main():
     dec = Decoder(wl)
     dec.pack_weights(Wt)
     dec.alloc_kv()
+    if args.attn_split:
+        dec.set_attention_split(args.attn_split)
     sync_modes = {"dataflow": MBK_SYNC_DATAFLOW, "barrier": MBK_SYNC_BARRIER}
     dec.set_sync_mode(sync_modes[args.sync])
     stream = torch.cuda.current_stream()
@@ -152,6 +158,13 @@ def main():
     elapsed = time.perf_counter() - t0
     dec.check()
     kern_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     mean_kern_us = sum(kern_us) / K
     bytes_mean = sum(algorithmic_bytes(wl, positions(i)) for i in range(K)) / K
     achieved = bytes_mean / (mean_kern_us * 1e-6) / 1e9
@@ -171,20 +184,21 @@ def main():
         "bytes_per_token": int(bytes_mean), "intervals_per_step": dec.num_intervals(),
     }
     # the other interval ordering of the same persistent kernel
-    other = "barrier" if args.sync == "dataflow" else "dataflow"
-    dec.set_sync_mode(sync_modes[other])
-    for i in range(8):
-        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
-    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(128)]
-    for i in range(128):
-        ev2[i][0].record(stream)
-        dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
-        ev2[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec.check()
     extra["sync_mode"] = args.sync
-    extra[other + "_mode_us_per_token"] = round(sum(a.elapsed_time(b) for a, b in ev2) / 128 * 1e3, 2)
-    dec.set_sync_mode(sync_modes[args.sync])
+    if not args.no_other_mode:
+        other = "barrier" if args.sync == "dataflow" else "dataflow"
+        dec.set_sync_mode(sync_modes[other])
+        for i in range(8):
+            dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+        ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(128)]
+        for i in range(128):
+            ev2[i][0].record(stream)
+            dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+            ev2[i][1].record(stream)
+        torch.cuda.synchronize()
+        dec.check()
+        extra[other + "_mode_us_per_token"] = round(sum(a.elapsed_time(b) for a, b in ev2) / 128 * 1e3, 2)
+        dec.set_sync_mode(sync_modes[args.sync])
 
     if not args.no_ablation:
         for mode, use_graph in (("ablation_plain", False), ("ablation_graph", True)):
@@ -225,6 +239,13 @@ def main():
                "sample": "%d greedy steps at positions %d..%d after the %s setup, fp64-accumulating C oracle" % (
                    n, g0, g0 + n - 1, "prefill" if wl.kv_prefill else "64-token prompt")}
 
+    # HBM bytes per launch from the committed counter summary, while it matches these kernel sources
+    from persistent_megakernel_decode_wg_amd import profile_traffic
+    rec = profile_traffic.read(os.path.join(ROOT, "profiles", "traffic_k_persistent_%s.md" % wl.name))
+    traffic = round(rec["traffic_bytes"]) if rec else None
+    if rec:
+        extra["traffic_fetch_bytes"] = round(rec["fetch_bytes"])
+        extra["traffic_write_bytes"] = round(rec["write_bytes"])
     out = {
         "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",
         "value": round(K / elapsed, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -235,7 +256,7 @@ def main():
                    "vocab": wl.vocab, "kv_capacity": wl.kv_capacity, "batch": 1,
                    "positions": "%d-%d" % (g0, g1 - 1), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "us_per_token": round(mean_kern_us, 2),
         "extra": extra,

@@ -67,6 +67,7 @@ struct Params {
     int32_t n_wg, n_intervals;
     int32_t H, nq, nkv, hd, I, V, S, NL;
     int32_t max_splits, gqa, attn_min_chunk, piece_pos, hd_shift;
+    int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
     // LDS offsets in bytes of the dynamic area
     int32_t lds_ivtab, lds_tasks, lds_trace, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
     int32_t ring_bytes, max_tasks;
@@ -341,6 +342,13 @@ MBK_DEV int step_pos(const Params &p) {
 // release, and several allocations stream at once).
 
 struct Split { int nsplit, t0, t1; };
+
+MBK_DEV int n_splits(const Params &p, int pos) {
+    const int Lc = pos + 1;
+    int chunk = (Lc + p.max_splits - 1) / p.max_splits;
+    if (chunk < p.attn_min_chunk) chunk = p.attn_min_chunk;
+    return (Lc + chunk - 1) / chunk;
+}
 
 MBK_DEV Split split_range(const Params &p, int s, int pos) {
     const int Lc = pos + 1;
@@ -648,6 +656,55 @@ MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag
     }
 }
 
+// Entries i, i+1 (i even) of a tagged vector.
+MBK_DEV bool poll2(const Params &p, uint64_t base, int i, uint32_t tag, float &a, float &b) {
+    const uint32_t off = (uint32_t)(base + 8u * (uint32_t)i);
+    for (int it = 0;; ++it) {
+        const u32x4 v = ldc16(p.ws, off);
+        if (v.y == tag && v.w == tag) {
+            a = __uint_as_float(v.x);
+            b = __uint_as_float(v.z);
+            return true;
+        }
+        if (it >= p.spin_limit) { set_error(p); return false; }
+        if (aborted(p, it)) return false;
+    }
+}
+
+MBK_DEV int n_splits(const Params &p, int pos);
+
+// xs <- hi/lo pairs of the attention output, merged from the split partials
+// (log-sum-exp merge in split order): thread u takes query head u / (hd/8),
+// dims 8 * (u % (hd/8)) .. + 8.  Threads [tid, nt).
+MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int pos, int tid, int nt, bool &ok) {
+    const int hd = p.hd, gpr = hd / 8, G = p.gqa;
+    const int nsplit = n_splits(p, pos);
+    for (int u = tid; u < p.nq * gpr; u += nt) {
+        const int h = u / gpr, g = u % gpr, j = h / G, hh = h % G;
+        float M = -INFINITY, L = 0.f, a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const int e0 = ((j * p.max_splits + s) * G + hh) * (hd + 2);
+            float m2, l2, v[8];
+            if (!poll2(p, p.wl.part, e0 + hd, tag, m2, l2) || !poll8(p, p.wl.part + 8u * (uint32_t)(e0 + 8 * g), 0, tag, v)) {
+                ok = false;
+                return;
+            }
+            const float mn = fmaxf(M, m2);
+            const float c1 = __expf(M - mn), c2 = __expf(m2 - mn);
+            L = L * c1 + l2 * c2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = a[e] * c1 + v[e] * c2;
+            M = mn;
+        }
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] *= inv;
+        split8_store(xs + 8 * u, a);
+    }
+}
+
 // ---- GEMV tile ---------------------------------------------------------------------------------------
 // A tile is RT packed rows; lane l covers row l / L and input groups
 // (l % L) + it * L, it < IT, reading the 16-byte chunk at it * 1 KiB + l * 16
@@ -847,7 +904,8 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
                     return 0.f;
                 }
             }
-            if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt, ok);
+            if (iv.op == OP_O && p.merge_in_o) merge_input(p, xs, tag_of(p, sc.seq, ivi - 1), sc.pos, tid, nt, ok);
+            else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt, ok);
             else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt, ok);
             return 0.f;
         }
@@ -1078,7 +1136,13 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                 for (int e = 0; e < 8; ++e) a[e] += r[4 + dl * 8 + e];
             }
             const int o0 = (j * G + h) * hd + dl * 8;
-            if (sp.nsplit == 1) {
+            if (p.merge_in_o) {
+                // tagged partial: entries [acc[hd] | max, sum] of (j, s, h)
+                const int e0 = ((j * p.max_splits + s) * G + h) * (hd + 2);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) put2(p, p.wl.part, e0 + dl * 8 + e, a[e], a[e + 1], tag);
+                if (dl == 0) put2(p, p.wl.part, e0 + hd, M[h], ll, tag);
+            } else if (sp.nsplit == 1) {
                 const float inv = 1.f / ll;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.o, o0 + e, a[e] * inv, a[e + 1] * inv, tag);
@@ -1093,7 +1157,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
         }
     }
-    if (sp.nsplit > 1) {
+    if (sp.nsplit > 1 && !p.merge_in_o) {
         // the last split to arrive (one atomic per split) merges all partials in
         // split order, so the result does not depend on arrival order
         if (threadIdx.x == 0) {

@@ -136,7 +136,7 @@ struct mbk_model {
     uint32_t seq = 0;     // decode steps run on the bound workspace (activation tags)
     int32_t sync_mode = MBK_SYNC_DATAFLOW;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
-    int32_t attn_min_chunk = 128;
+    int32_t attn_min_chunk = 32;
     int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
     bool kernels_ready = false;
     uint64_t *trace = nullptr;
@@ -401,7 +401,11 @@ std::string build_plan(mbk_model *m) {
     W.v = w; w = align256(w + 8u * KV);
     W.o = w; w = align256(w + 8u * Q);
     W.a = w; w = align256(w + 8u * c.intermediate);
-    W.part = w; w = align256(w + 4u * (uint64_t)c.n_kv_heads * ms * G * stride);
+    // attention partials: fp32 [nkv][ms][G][hd + 4] for the last-arriver merge, or tagged
+    // 8-byte entries [nkv][ms][G][hd + 2] for the merge in the output projection
+    W.part = w;
+    w = align256(w + std::max<uint64_t>(4u * (uint64_t)c.n_kv_heads * ms * G * stride,
+                                        8u * (uint64_t)c.n_kv_heads * ms * G * (hd + 2)));
     W.total = w;
 
     // RoPE table: angle pos * theta^(-2i/hd), evaluated in double, stored fp32
@@ -463,6 +467,12 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.max_splits = P.max_splits;
     p.gqa = c.n_heads / c.n_kv_heads;
     p.attn_min_chunk = m->attn_min_chunk;
+    {
+        // the output projection merges the split partials itself when they are few: every one of
+        // its workgroups polls nq * splits * (hd + 2) tagged entries
+        const int splits = std::min(P.max_splits, (c.kv_capacity + m->attn_min_chunk - 1) / m->attn_min_chunk);
+        p.merge_in_o = (size_t)c.n_heads * splits * (c.head_dim + 2) * 8u <= 48u * 1024u ? 1 : 0;
+    }
     p.piece_pos = P.piece_pos;
     p.hd_shift = 0;
     while ((1 << p.hd_shift) < c.head_dim) ++p.hd_shift;

@@ -85,3 +85,36 @@ def test_no_device_is_reported_as_hip_error(L):
     n = ctypes.c_size_t()
     assert L.mbk_pack_weights(h, None, None, ctypes.byref(n), None) == 5          # MBK_ERR_HIP
     L.mbk_destroy(h)
+
+
+@pytest.mark.parametrize("name", ["tiny-2L-h64-kv32", "smollm135m-kv128", "smollm135m-kv4096", "qwen2-0.5b-kv128",
+                                  "smollm1.7b-kv4096"])
+def test_plan_fits_lds_and_ring_rules(name):
+    """The host planner (no device: workgroups fixed) keeps every workgroup inside the 160 KiB of LDS, every
+    allocation within a third of the ring, and the packed payload at 2 bytes per parameter."""
+    from persistent_megakernel_decode_wg_amd import Decoder
+    wl = synth.get(name)
+    d = Decoder(wl)
+    d.set_workgroups(256)
+    info = d.describe()
+    assert info["workgroups"] == 256 and info["intervals"] == 5 * wl.n_layers + 1
+    assert info["lds_bytes"] + 512 <= 160 * 1024
+    assert info["max_task_bytes"] * 3 <= info["ring_bytes"]
+    assert info["max_tile_bytes"] * 3 <= info["ring_bytes"]
+    assert info["piece_positions"] >= 1
+    seg = (info["piece_positions"] * wl.head_dim * 2 + 1023) // 1024 * 1024   # keys (or values) of one piece
+    assert 2 * seg * 3 <= info["ring_bytes"]
+    # packed matrices are exactly 2 bytes per parameter (plus norms, RoPE table and schedule tables)
+    assert info["packed_bytes"] >= 2 * wl.param_count()
+    d.close()
+
+
+def test_set_workgroups_after_planning_is_a_state_error():
+    from persistent_megakernel_decode_wg_amd import Decoder, MbkError, MBK_ERR_STATE
+    d = Decoder(synth.get("tiny-2L-h64-kv32"))
+    d.set_workgroups(128)
+    d.describe()
+    with pytest.raises(MbkError) as e:
+        d.set_workgroups(64)
+    assert e.value.code == MBK_ERR_STATE
+    d.close()
