@@ -150,7 +150,8 @@ int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
 
 /* Attention split policy: each split of the cached context covers at least
  * min_positions positions (default 128); contexts up to that length run
- * unsplit, one workgroup per KV head. */
+ * unsplit.  Short caches whose keys and values of one head fit in 64 KiB get one
+ * work item per query head, longer ones one per KV head (all its query heads). */
 int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
 
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */

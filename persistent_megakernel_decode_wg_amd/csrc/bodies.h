@@ -68,9 +68,11 @@ struct Params {
     int32_t H, nq, nkv, hd, I, V, S, NL;
     int32_t max_splits, gqa, attn_min_chunk, piece_pos, hd_shift;
     int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
+    int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
     // LDS offsets in bytes of the dynamic area
     int32_t lds_ivtab, lds_tasks, lds_trace, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
     int32_t ring_bytes, max_tasks;
+    int32_t in_bytes, in_double;  // LDS input block [qkv | bias | xs | xres] size; 1: two copies used in turn
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
     int32_t token, pos;       // token < 0: previous device argmax
     uint32_t seq;             // step number: tags of this step's activations
@@ -83,11 +85,11 @@ struct Params {
 
 // LDS control words shared by the waves of a workgroup.
 struct Ctl {
-    uint32_t prog[kLW];   // loader wave w: number of its chunks known complete
+    alignas(16) uint32_t prog[kLW];   // loader wave w: number of its chunks known complete
+    alignas(16) float ss[2][kCW];     // RMSNorm partial sums, by input-block parity
     uint32_t cons[kCW];   // compute wave c: ring consumed up to this virtual offset
     uint32_t bar;         // compute-wave barrier arrivals
     uint32_t abort;       // nonzero: leave (a bounded wait expired or the debug switch fired)
-    float ss[kCW];        // RMSNorm partial sums
     uint64_t best[kCW];   // argmax keys
     int32_t last_s;       // attention split merge: this workgroup arrived last
 };
@@ -218,6 +220,32 @@ MBK_DEV bool poll1(const Params &p, uint64_t base, int i, uint32_t tag, float &v
             v = __uint_as_float((uint32_t)w);
             return true;
         }
+        if (it >= p.spin_limit) { set_error(p); return false; }
+        if (aborted(p, it)) return false;
+    }
+}
+
+// Polls up to kPollMax 16-byte chunks of the workspace (byte offsets off[i],
+// each holding two tagged entries; need[i] bit 0 / bit 1: entry 0 / 1 must
+// carry the tag, bit 2: the tag is tag_b instead of tag_a) until all of them
+// are ready.  Every round has all its loads in flight at once, so ready
+// inputs cost one memory round trip.
+constexpr int kPollMax = 12;
+MBK_DEV bool poll_round(const Params &p, const uint32_t *off, const uint32_t *need, int n, uint32_t tag_a,
+                        uint32_t tag_b, u32x4 *v) {
+    uint32_t pending = n >= 32 ? ~0u : ((1u << n) - 1u);
+    for (int it = 0;; ++it) {
+#pragma unroll
+        for (int i = 0; i < kPollMax; ++i)
+            if ((pending >> i) & 1u) v[i] = ldc16(p.ws, off[i]);
+#pragma unroll
+        for (int i = 0; i < kPollMax; ++i) {
+            if (!((pending >> i) & 1u)) continue;
+            const uint32_t tag = (need[i] & 4u) ? tag_b : tag_a;
+            const bool a = !(need[i] & 1u) || v[i].y == tag, c = !(need[i] & 2u) || v[i].w == tag;
+            if (a && c) pending &= ~(1u << i);
+        }
+        if (!pending) return true;
         if (it >= p.spin_limit) { set_error(p); return false; }
         if (aborted(p, it)) return false;
     }
@@ -372,6 +400,14 @@ MBK_DEV const uint16_t *kv_block(const Params &p, int layer, int which, int j) {
     return p.kv + (((size_t)layer * 2 + which) * p.nkv + j) * p.S * p.hd;
 }
 
+// An attention item: KV head j, split s, query heads h0 .. h0 + nh - 1 of the group.
+struct AttnItem { int j, s, h0, nh; };
+MBK_DEV AttnItem attn_item(const Params &p, int item) {
+    const int jh = item / p.max_splits, s = item % p.max_splits;
+    if (p.attn_hpi == 1) return AttnItem{jh / p.gqa, s, jh % p.gqa, 1};
+    return AttnItem{jh, s, 0, p.gqa};
+}
+
 MBK_DEV int n_allocs(const Params &p, const Interval &iv, const Task &T, int pos) {
     if (iv.op != OP_ATTN) return 1;
     const int s = T.a % p.max_splits;
@@ -393,8 +429,9 @@ MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, int
         A.size = A.b0;
         return A;
     }
-    const int j = T.a / p.max_splits, s = T.a % p.max_splits;
-    const Split sp = split_range(p, s, pos);
+    const AttnItem it = attn_item(p, T.a);
+    const int j = it.j;
+    const Split sp = split_range(p, it.s, pos);
     const int te = min(sp.t1, pos);
     const int pa = sp.t0 + k * p.piece_pos, pb = min(te, pa + p.piece_pos);
     const uint32_t row = (uint32_t)p.hd * 2u;
@@ -571,8 +608,17 @@ MBK_DEV bool cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
 // Position of the compute waves in the allocation sequence.
 struct RingPos {
     uint32_t vpos;
-    uint32_t cum[kLW];
+    uint32_t cum[kLW];    // chunks of each loader wave up to the current allocation
+    uint32_t seen[kLW];   // loader progress last read from LDS
 };
+
+// All loader waves' progress with one LDS read.
+MBK_DEV void read_prog(Ctl &ctl, uint32_t *out) {
+    static_assert(kLW == 4, "one 16-byte read of the loader progress");
+    const u32x4 v = *(volatile u32x4 *)ctl.prog;
+    asm volatile("" ::: "memory");
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
 
 // Places the next allocation; waits until the loader waves have completed it.
 // Returns its virtual start, or ~0 when the wait failed.
@@ -581,15 +627,19 @@ MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Allo
     rp.vpos = start + A.size;
 #pragma unroll
     for (int w = 0; w < kLW; ++w) rp.cum[w] += wave_chunks(A.b0, w) + wave_chunks(A.b1, w);
+    // the loader is usually far ahead: the progress read last time often covers this allocation
+    for (int it = 0;; ++it) {
+        bool ready = true;
 #pragma unroll
-    for (int w = 0; w < kLW; ++w) {
-        for (int it = 0; (int32_t)(lds_ld(&ctl.prog[w]) - rp.cum[w]) < 0; ++it) {
+        for (int w = 0; w < kLW; ++w) ready = ready && (int32_t)(rp.seen[w] - rp.cum[w]) >= 0;
+        if (ready) return start;
+        if (it > 0) {
             if (lds_ld(&ctl.abort)) return ~0u;
             if (it >= p.spin_limit) { set_error(p); lds_st(&ctl.abort, 1u); return ~0u; }
             __builtin_amdgcn_s_sleep(1);
         }
+        read_prog(ctl, rp.seen);
     }
-    return start;
 }
 
 MBK_DEV void ring_release(Ctl &ctl, const RingPos &rp) { lds_st(&ctl.cons[wave_id()], rp.vpos); }
@@ -634,9 +684,11 @@ MBK_DEV float norm_input(const Params &p, float *xs, bool from_embed, int token,
     float ss = 0.f;
     for (int g = tid; g < K / 8; g += nt) {
         float v[8], w[8];
+        // the norm weights (and the embedding row) are requested before the poll, so they arrive with it
+        const u32x4 wn = *(const u32x4 *)(p.blob + norm_off + 16u * g);
         if (from_embed) unpack8(*(const u32x4 *)(p.blob + row_group_offset(p.embed, token, g)), v);
         else if (!poll8(p, p.wl.x, g, tag, v)) { ok = false; return 0.f; }
-        unpack8(*(const u32x4 *)(p.blob + norm_off + 16u * g), w);
+        unpack8(wn, w);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             ss += v[e] * v[e];
@@ -679,24 +731,42 @@ MBK_DEV int n_splits(const Params &p, int pos);
 MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int pos, int tid, int nt, bool &ok) {
     const int hd = p.hd, gpr = hd / 8, G = p.gqa;
     const int nsplit = n_splits(p, pos);
+    constexpr int kPer = kPollMax / 5;  // splits per polling round: {max, sum} chunk + 4 chunks of acc
     for (int u = tid; u < p.nq * gpr; u += nt) {
         const int h = u / gpr, g = u % gpr, j = h / G, hh = h % G;
         float M = -INFINITY, L = 0.f, a[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const int e0 = ((j * p.max_splits + s) * G + hh) * (hd + 2);
-            float m2, l2, v[8];
-            if (!poll2(p, p.wl.part, e0 + hd, tag, m2, l2) || !poll8(p, p.wl.part + 8u * (uint32_t)(e0 + 8 * g), 0, tag, v)) {
-                ok = false;
-                return;
-            }
-            const float mn = fmaxf(M, m2);
-            const float c1 = __expf(M - mn), c2 = __expf(m2 - mn);
-            L = L * c1 + l2 * c2;
+        for (int s0 = 0; s0 < nsplit; s0 += kPer) {
+            const int ns = min(kPer, nsplit - s0);
+            uint32_t off[kPollMax], need[kPollMax];
+            u32x4 v[kPollMax];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = a[e] * c1 + v[e] * c2;
-            M = mn;
+            for (int i = 0; i < kPollMax; ++i) { off[i] = 0; need[i] = 0; }
+            for (int q = 0; q < ns; ++q) {
+                const uint32_t e0 = (uint32_t)(((j * p.max_splits + s0 + q) * G + hh) * (hd + 2));
+                off[5 * q] = (uint32_t)p.wl.part + 8u * (e0 + (uint32_t)hd);
+                need[5 * q] = 3u;
+                for (int c = 0; c < 4; ++c) {
+                    off[5 * q + 1 + c] = (uint32_t)p.wl.part + 8u * (e0 + 8u * (uint32_t)g) + 16u * c;
+                    need[5 * q + 1 + c] = 3u;
+                }
+            }
+            if (!poll_round(p, off, need, 5 * ns, tag, tag, v)) { ok = false; return; }
+            for (int q = 0; q < ns; ++q) {
+                const float m2 = __uint_as_float(v[5 * q].x), l2 = __uint_as_float(v[5 * q].z);
+                float w[8];
+                for (int c = 0; c < 4; ++c) {
+                    w[2 * c] = __uint_as_float(v[5 * q + 1 + c].x);
+                    w[2 * c + 1] = __uint_as_float(v[5 * q + 1 + c].z);
+                }
+                const float mn = fmaxf(M, m2);
+                const float c1 = __expf(M - mn), c2 = __expf(m2 - mn);
+                L = L * c1 + l2 * c2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = a[e] * c1 + w[e] * c2;
+                M = mn;
+            }
         }
         const float inv = 1.f / L;
 #pragma unroll
@@ -762,6 +832,8 @@ struct StepCtx {
     uint32_t gen;    // compute-wave barrier generation
     uint64_t best;   // this lane's argmax key (LM head)
     int blk0;        // first tile of this workgroup's block in the current interval
+    int in;          // byte offset of the input block in use
+    uint32_t nin;    // input blocks loaded so far
 };
 
 // Q/K/V: bias, RoPE on query/key pairs (packed rows 2m, 2m+1 are head dims
@@ -784,7 +856,7 @@ MBK_DEV void epi_qkv(const Params &p, const Interval &iv, const uint8_t *lds, in
         s.row = s.which == 2 ? base : (base & ~(hd - 1)) + ((i & 1) ? (i >> 1) + half : (i >> 1));
     }
     if (iv.bias_off != ~(uint64_t)0 && valid) {
-        const float *bias = (const float *)(lds + p.lds_bias);
+        const float *bias = (const float *)(lds + p.lds_bias + sc.in);
         y += bias[(s.which == 0 ? 0 : (s.which == 1 ? Q : Q + KVr)) + s.row];
     }
     const float partner = __shfl_xor(y, g.L);  // row ^ 1
@@ -818,7 +890,7 @@ MBK_DEV void epi_qkv(const Params &p, const Interval &iv, const uint8_t *lds, in
 MBK_DEV void gemv_tile_op(const Params &p, const Interval &iv, const uint8_t *lds, const uint8_t *wt, int t,
                           StepCtx &sc, uint32_t tag) {
     const MatGeom &g = iv.mat;
-    const float *xs = (const float *)(lds + p.lds_xs);
+    const float *xs = (const float *)(lds + p.lds_xs + sc.in);
     float y = gemv_tile(g, wt, xs) * sc.rnorm;
     const int lane = threadIdx.x & 63;
     const int row = t * g.RT + (lane >> (6 - g.lrt));
@@ -827,7 +899,7 @@ MBK_DEV void gemv_tile_op(const Params &p, const Interval &iv, const uint8_t *ld
         case OP_QKV: epi_qkv(p, iv, lds, t, y, sc, tag); break;
         case OP_O:
         case OP_DOWN: {
-            const float *xres = (const float *)(lds + p.lds_xres);
+            const float *xres = (const float *)(lds + p.lds_xres + sc.in);
             if (lead) put(p, p.wl.x, row, xres[row - sc.blk0 * g.RT] + y, tag);
             break;
         }
@@ -883,7 +955,7 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
 // Returns this thread's part of the RMSNorm sum of squares (0 if none).
 MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t *lds, StepCtx &sc, bool &ok) {
     const int tid = threadIdx.x, nt = kCW * 64;
-    float *xs = (float *)(lds + p.lds_xs);
+    float *xs = (float *)(lds + p.lds_xs + sc.in);
     const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(p, sc.seq, iv.x_src);
     switch (iv.op) {
         case OP_O:
@@ -893,7 +965,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
             const int k = participant(iv, blockIdx.x, p.n_wg);
             const int b0 = block_begin(iv.n_items, k, iv.nwg), b1 = block_begin(iv.n_items, k + 1, iv.nwg);
             sc.blk0 = b0;
-            float *xres = (float *)(lds + p.lds_xres);
+            float *xres = (float *)(lds + p.lds_xres + sc.in);
             const int r0 = b0 * g.RT, r1 = min(b1 * g.RT, g.rows);
             for (int r = r0 + tid; r < r1; r += nt) {
                 if (iv.x_src < 0) {
@@ -909,13 +981,23 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
             else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt, ok);
             return 0.f;
         }
-        case OP_QKV:
-            if (iv.bias_off != ~(uint64_t)0) {
-                const uint16_t *b = (const uint16_t *)(p.blob + iv.bias_off);
-                float *bias = (float *)(lds + p.lds_bias);
-                for (int i = tid; i < (p.nq + 2 * p.nkv) * p.hd; i += nt) bias[i] = bf16f(b[i]);
+        case OP_QKV: {
+            if (iv.bias_off == ~(uint64_t)0) return norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt, ok);
+            // Q/K/V bias to LDS (fp32), 8 values per 16-byte load; the first load of each thread is
+            // in flight while the residual stream is polled
+            const int nb8 = (p.nq + 2 * p.nkv) * p.hd / 8;
+            const u32x4 *bsrc = (const u32x4 *)(p.blob + iv.bias_off);
+            float *bias = (float *)(lds + p.lds_bias + sc.in);
+            u32x4 first = {0u, 0u, 0u, 0u};
+            if (tid < nb8) first = bsrc[tid];
+            const float ss = norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt, ok);
+            for (int i = tid; i < nb8; i += nt) {
+                float v[8];
+                unpack8(i == tid ? first : bsrc[i], v);
+                store8(bias + 8 * i, v);
             }
-            return norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt, ok);
+            return ss;
+        }
         default:  // gate/up and LM head: RMS-normalised residual stream
             return norm_input(p, xs, false, 0, xtag, iv.norm_off, p.H, tid, nt, ok);
     }
@@ -926,23 +1008,26 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
 // holds them.  LDS at lds_qkv: [G][hd] queries, [hd] key, [hd] value.
 MBK_DEV void attn_inputs(const Params &p, int item, int ivi, uint8_t *lds, const StepCtx &sc, bool &ok) {
     const int tid = threadIdx.x, nt = kCW * 64;
-    const int j = item / p.max_splits;
-    const int G = p.gqa, hd = p.hd, qg = G * hd / 8, kg = hd / 8;
+    const AttnItem it = attn_item(p, item);
+    const int G = p.gqa, hd = p.hd, kg = hd / 8, qg = it.nh * kg;
     const uint32_t tag = tag_of(p, sc.seq, ivi - 1);
-    float *dst = (float *)(lds + p.lds_qkv);
+    float *dst = (float *)(lds + p.lds_qkv + sc.in);
     for (int g = tid; g < qg + 2 * kg; g += nt) {
         float v[8];
         if (g < qg) {
-            if (!poll8(p, p.wl.q, j * qg + g, tag, v)) { ok = false; return; }
+            // queries of heads h0 .. h0 + nh - 1 of group j, at [0, nh)
+            if (!poll8(p, p.wl.q, (it.j * G + it.h0) * kg + g, tag, v)) { ok = false; return; }
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] *= p.scale;
+            store8(dst + 8 * g, v);
         } else {
             const bool key = g < qg + kg;
-            if (!poll8(p, key ? p.wl.k : p.wl.v, j * kg + g - qg - (key ? 0 : kg), tag, v)) { ok = false; return; }
+            const int gg = g - qg - (key ? 0 : kg);
+            if (!poll8(p, key ? p.wl.k : p.wl.v, it.j * kg + gg, tag, v)) { ok = false; return; }
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = bf16f(to_bf16(v[e]));
+            store8(dst + G * hd + (key ? 0 : hd) + 8 * gg, v);
         }
-        store8(dst + 8 * g, v);
     }
 }
 
@@ -1005,10 +1090,11 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                             RingPos &rp, StepCtx &sc) {
     const int pos = sc.pos, hd = p.hd, LP = hd / 8, PPW = 64 / LP;
     const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane % LP, slot = lane / LP;
-    const int j = T.a / p.max_splits, s = T.a % p.max_splits;
+    const AttnItem item = attn_item(p, T.a);
+    const int j = item.j, s = item.s, h0 = item.h0, nh = item.nh;
     const Split sp = split_range(p, s, pos);
     if (s >= sp.nsplit) return true;  // no allocations either
-    const float *qkv = (const float *)(lds + p.lds_qkv);
+    const float *qkv = (const float *)(lds + p.lds_qkv + sc.in);
     const float *cur = qkv + G * hd;        // this step's key, then value
     float *scores = (float *)(lds + p.lds_score);   // [G][piece_pos + 1]
     float *wmax = scores + G * (p.piece_pos + 1);   // [2][kCW][G]
@@ -1016,6 +1102,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     float qf[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+        if (h >= nh) break;
         const float4 a = *(const float4 *)(qkv + h * hd + dl * 8), b = *(const float4 *)(qkv + h * hd + dl * 8 + 4);
         qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
         qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
@@ -1058,6 +1145,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
+                if (h >= nh) break;
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
@@ -1072,12 +1160,14 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         float *wm = wmax + (k & 1) * kCW * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            if (h >= nh) break;
             const float m = slot_max(lmax[h], LP);
             if (lane == 0) wm[cw * G + h] = m;
         }
         if (!cw_barrier(p, ctl, sc.gen)) return false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            if (h >= nh) break;
             float m = wm[h];
             for (int w = 1; w < kCW; ++w) m = fmaxf(m, wm[w * G + h]);
             const float mn = fmaxf(M[h], m);
@@ -1097,6 +1187,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             seg_kv(t, nring, kb, vb, cur, hd, dl, kf, vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
+                if (h >= nh) break;
                 const float w = __expf(scores[h * sstride + t] - M[h]);
                 l[h] += w;
 #pragma unroll
@@ -1112,6 +1203,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     float *scr = (float *)(lds + p.lds_attn);  // [kCW][G][stride]
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+        if (h >= nh) break;
         l[h] = slot_sum(l[h], LP);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum(acc[h][e], LP);
@@ -1126,6 +1218,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     if (cw == 0 && slot == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            if (h >= nh) break;
             float ll = 0.f, a[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = 0.f;
@@ -1135,10 +1228,10 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) a[e] += r[4 + dl * 8 + e];
             }
-            const int o0 = (j * G + h) * hd + dl * 8;
+            const int o0 = (j * G + h0 + h) * hd + dl * 8;
             if (p.merge_in_o) {
                 // tagged partial: entries [acc[hd] | max, sum] of (j, s, h)
-                const int e0 = ((j * p.max_splits + s) * G + h) * (hd + 2);
+                const int e0 = ((j * p.max_splits + s) * G + h0 + h) * (hd + 2);
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.part, e0 + dl * 8 + e, a[e], a[e + 1], tag);
                 if (dl == 0) put2(p, p.wl.part, e0 + hd, M[h], ll, tag);
@@ -1148,7 +1241,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.o, o0 + e, a[e] * inv, a[e + 1] * inv, tag);
             } else {
                 // this split's partial: part[j][s][h][stride] = {max, sum, -, -, acc[hd]}
-                const uint64_t pb = p.wl.part + ((uint64_t)(j * p.max_splits + s) * G + h) * stride * 4u;
+                const uint64_t pb = p.wl.part + ((uint64_t)(j * p.max_splits + s) * G + h0 + h) * stride * 4u;
                 if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(M[h]), __float_as_uint(ll), 0u, 0u});
                 stc16(p.ws, (uint32_t)(pb + 16u + 32u * dl), (u32x4){__float_as_uint(a[0]), __float_as_uint(a[1]),
                                                                      __float_as_uint(a[2]), __float_as_uint(a[3])});
@@ -1163,7 +1256,8 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         if (threadIdx.x == 0) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
             uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.merge_cnt + 256u * j);
-            const bool last = atom_add(cnt, 1u) == (uint32_t)sp.nsplit - 1u;
+            // every item of the group arrives: splits x (query heads / heads per item)
+            const bool last = atom_add(cnt, 1u) == (uint32_t)(sp.nsplit * (G / nh)) - 1u;
             if (last) {
                 stc_u(cnt, 0u);
                 __builtin_amdgcn_s_waitcnt(0);  // the reset lands before this group's output does
@@ -1229,7 +1323,7 @@ MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &s
     RingPos rp;
     rp.vpos = 0;
 #pragma unroll
-    for (int w = 0; w < kLW; ++w) rp.cum[w] = 0;
+    for (int w = 0; w < kLW; ++w) rp.cum[w] = rp.seen[w] = 0;
     const int cw = wave_id();
     int k = 0;
     for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
@@ -1240,21 +1334,27 @@ MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &s
         if (T.iv == ivi) {
             const Interval iv = interval_at(p, lds, ivi);
             stamp(p, lds, ivi, 0);
-            // inputs: the other compute wave is done with the previous interval's LDS inputs
-            if (!cw_barrier(p, ctl, sc.gen)) return false;
+            // inputs go to the input block not read by the previous interval; with a single block the
+            // other compute waves must first be done with it
+            const int par = (int)(sc.nin & 1u);
+            ++sc.nin;
+            if (p.in_double) sc.in = par * p.in_bytes;
+            else if (!cw_barrier(p, ctl, sc.gen)) return false;
             bool ok = true;
             float ss = 0.f;
             if (iv.op == OP_ATTN) attn_inputs(p, T.a, ivi, lds, sc, ok);
             else ss = gemv_inputs(p, iv, ivi, lds, sc, ok);
             ss = group_sum<64>(ss);
-            if ((threadIdx.x & 63) == 0) ctl.ss[cw] = ss;
+            if ((threadIdx.x & 63) == 0) ctl.ss[par][cw] = ss;
             if (!ok) { lds_st(&ctl.abort, 1u); return false; }
             if (!cw_barrier(p, ctl, sc.gen)) return false;
             stamp(p, lds, ivi, 1);
             sc.rnorm = 1.f;
             if (iv.op == OP_QKV || iv.op == OP_GATEUP || iv.op == OP_LMHEAD) {
-                float tot = 0.f;
-                for (int w = 0; w < kCW; ++w) tot += ctl.ss[w];
+                static_assert(kCW == 4, "one 16-byte read of the partial sums");
+                const u32x4 s4 = *(volatile u32x4 *)ctl.ss[par];
+                const float tot = (__uint_as_float(s4.x) + __uint_as_float(s4.y)) +
+                                  (__uint_as_float(s4.z) + __uint_as_float(s4.w));
                 sc.rnorm = rsqrtf(tot / (float)p.H + p.eps);
             }
             const uint32_t tag = tag_of(p, sc.seq, ivi);
@@ -1361,6 +1461,8 @@ MBK_DEV void run_step(const Params &p) {
         sc.gen = 0;
         sc.best = 0;
         sc.blk0 = 0;
+        sc.in = 0;
+        sc.nin = 0;
         if (p.first_iv == 0 && blockIdx.x == 0 && threadIdx.x == 0 && !p.step_from_ws) {
             // this step's inputs, for launches that read them from the workspace
             uint32_t *ctrl = ws_ptr<uint32_t>(p, p.wl.ctrl);

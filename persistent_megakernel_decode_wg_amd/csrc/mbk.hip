@@ -112,7 +112,7 @@ struct Plan {
     std::vector<Interval> iv;
     std::vector<Task> task_list;       // all workgroups' tasks, workgroup-major
     std::vector<int32_t> task_index;   // [n_wg][n_iv + 1]
-    int max_splits = 1, piece_pos = 1, max_tasks = 0;
+    int max_splits = 1, piece_pos = 1, max_tasks = 0, in_bytes = 0, in_double = 0, attn_hpi = 1;
     // LDS layout (bytes of the dynamic area)
     int lds_ivtab = 0, lds_tasks = 0, lds_trace = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
         lds_xres = 0, lds_attn = 0, lds_score = 0, lds_ring = 0, ring_bytes = 0;
@@ -136,7 +136,7 @@ struct mbk_model {
     uint32_t seq = 0;     // decode steps run on the bound workspace (activation tags)
     int32_t sync_mode = MBK_SYNC_DATAFLOW;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
-    int32_t attn_min_chunk = 32;
+    int32_t attn_min_chunk = 128;
     int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
     bool kernels_ready = false;
     uint64_t *trace = nullptr;
@@ -252,7 +252,11 @@ std::string build_plan(mbk_model *m) {
     // one KV head fits the LDS merge scratch
     const int stride = hd + 4;
     const size_t merge_budget = 16 * 1024;
-    int ms = std::max(1, n_wg / c.n_kv_heads);
+    // attention items: one per query head when a head's cached keys and values are small (every item
+    // then reads its group's keys and values, from the caches), else the query heads of a KV head packed
+    P.attn_hpi = (size_t)c.kv_capacity * hd * 4 <= 64 * 1024 ? 1 : G;
+    const int item_heads = P.attn_hpi == 1 ? c.n_heads : c.n_kv_heads;
+    int ms = std::max(1, n_wg / item_heads);
     ms = std::min<int>(ms, (int)(merge_budget / ((size_t)G * stride * 4)));
     ms = std::max(1, std::min(ms, 64));
     P.max_splits = ms;
@@ -267,7 +271,7 @@ std::string build_plan(mbk_model *m) {
         Interval a{};
         a.op = OP_ATTN;
         a.layer = l;
-        a.n_items = c.n_kv_heads * ms;
+        a.n_items = item_heads * ms;
         a.x_src = -1;
         a.norm_off = a.bias_off = none;
         P.iv.push_back(a);
@@ -305,6 +309,15 @@ std::string build_plan(mbk_model *m) {
     fixed += a16((size_t)max_rows * 4);                            // residual rows
     fixed += a16((size_t)std::max(kCW, ms) * G * stride * 4);      // attention merge scratch
     fixed += a16(((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);  // attention scores and maxima
+    // input block [attention inputs | bias | GEMV input | residual rows]; a second copy lets an
+    // interval's inputs load while other compute waves still read the previous interval's
+    const size_t in_block = a16((size_t)(G + 2) * hd * 4) + (c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0) +
+                            a16((size_t)kmax * 4) + a16((size_t)max_rows * 4);
+    {
+        const size_t left = kLdsMax - kLdsStatic - task_slot - fixed - in_block;
+        P.in_double = left > (size_t)64 * 16 + 64 * 1024 ? 1 : 0;
+        if (P.in_double) fixed += in_block;
+    }
 
     // tile runs of at most a third of the ring: first size the ring assuming a task
     // list of 64 entries per workgroup, then build the lists and shrink the ring
@@ -362,6 +375,8 @@ std::string build_plan(mbk_model *m) {
     P.lds_bias = (int)off; off = c.qkv_bias ? a16(off + (size_t)(Q + 2 * KV) * 4) : off;
     P.lds_xs = (int)off; off = a16(off + (size_t)kmax * 4);
     P.lds_xres = (int)off; off = a16(off + (size_t)max_rows * 4);
+    P.in_bytes = (int)(off - (size_t)P.lds_qkv);
+    if (P.in_double) off += P.in_bytes;
     P.lds_attn = (int)off; off = a16(off + (size_t)std::max(kCW, ms) * G * stride * 4);
     P.lds_score = (int)off; off = a16(off + ((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);
     off = (off + kChunk - 1) / kChunk * kChunk;
@@ -471,7 +486,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
         // the output projection merges the split partials itself when they are few: every one of
         // its workgroups polls nq * splits * (hd + 2) tagged entries
         const int splits = std::min(P.max_splits, (c.kv_capacity + m->attn_min_chunk - 1) / m->attn_min_chunk);
-        p.merge_in_o = (size_t)c.n_heads * splits * (c.head_dim + 2) * 8u <= 48u * 1024u ? 1 : 0;
+        p.merge_in_o = splits > 1 && (size_t)c.n_heads * splits * (c.head_dim + 2) * 8u <= 48u * 1024u ? 1 : 0;
     }
     p.piece_pos = P.piece_pos;
     p.hd_shift = 0;
@@ -488,6 +503,9 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.lds_score = P.lds_score;
     p.lds_ring = P.lds_ring;
     p.ring_bytes = P.ring_bytes;
+    p.in_bytes = P.in_bytes;
+    p.in_double = P.in_double;
+    p.attn_hpi = P.attn_hpi;
     p.max_tasks = P.max_tasks;
     p.eps = c.rms_eps;
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
@@ -822,9 +840,9 @@ int mbk_describe(mbk_model *m, char *buf, size_t len) {
         "{\"workgroups\": %d, \"threads\": %d, \"compute_waves\": %d, \"loader_waves\": %d, \"intervals\": %zu, "
         "\"packed_bytes\": %llu, \"workspace_bytes\": %llu, \"lds_bytes\": %zu, \"ring_bytes\": %d, "
         "\"max_tasks\": %d, \"tasks\": %zu, \"max_task_bytes\": %zu, \"max_tile_bytes\": %zu, "
-        "\"max_splits\": %d, \"piece_positions\": %d}",
+        "\"max_splits\": %d, \"piece_positions\": %d, \"double_inputs\": %d}",
         m->n_wg, kThreads, kCW, kLW, P.iv.size(), (unsigned long long)P.total, (unsigned long long)P.ws.total,
-        P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos);
+        P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos, P.in_double);
     if (n < 0 || (size_t)n >= len) return fail(MBK_ERR_SIZE, "description needs %d bytes", n + 1);
     return MBK_OK;
 }
