@@ -45,6 +45,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
+// LDS views: accesses through them compile to LDS instructions even where
+// they are volatile or atomic (through a generic pointer they would become
+// flat accesses, which wait for every outstanding global access too).
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kBatch = 8;                          // loader: chunks per wave between progress updates
 constexpr int kInflight = 24;                      // loader: chunks per wave left in flight (3 batches)
@@ -74,6 +79,7 @@ struct Params {
     int32_t ring_bytes, max_tasks;
     int32_t in_bytes, in_double;  // LDS input block [qkv | bias | xs | xres] size; 1: two copies used in turn
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
+    float inv_h;              // 1 / hidden
     int32_t token, pos;       // token < 0: previous device argmax
     uint32_t seq;             // step number: tags of this step's activations
     int32_t step_from_ws;     // 1: read token/pos/seq from the workspace (graph replay)
@@ -143,7 +149,7 @@ MBK_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x 
 MBK_DEV uint32_t lds_ld_opaque(const void *p) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-    return v;
+    return __builtin_amdgcn_readfirstlane(v);
 }
 MBK_DEV u32x4 lds_ld16_opaque(const void *p) {
     u32x4 v;
@@ -154,8 +160,16 @@ MBK_DEV void lds_st_opaque(void *p, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
 
-MBK_DEV uint32_t lds_ld(const uint32_t *p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-MBK_DEV void lds_st(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+// Control words read by every lane of a wave: the value goes to a scalar
+// register, so the branches and loops that test it stay wave-uniform.
+// True when c holds in any lane of the wave (a wave-uniform condition).
+MBK_DEV bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
+MBK_DEV uint32_t lds_ld(const uint32_t *p) { return __builtin_amdgcn_readfirstlane(*(volatile lds_u32 *)(lds_u32 *)p); }
+MBK_DEV u32x4 lds_ld16(const void *p) { return *(volatile lds_u32x4 *)(lds_u32x4 *)p; }
+// LDS accesses of one wave complete in order, so a control word stored after
+// the data it announces is seen after that data.
+MBK_DEV void lds_st(uint32_t *p, uint32_t v) { *(volatile lds_u32 *)(lds_u32 *)p = v; }
 
 // ---- error handling ------------------------------------------------------------------------------
 
@@ -369,24 +383,23 @@ MBK_DEV int step_pos(const Params &p) {
 // waiting for space then always waits for data the compute waves will
 // release, and several allocations stream at once).
 
-struct Split { int nsplit, t0, t1; };
+// Attention split of this step: positions [0, pos] in nsplit splits of at
+// most chunk positions (computed once per step: the divisions stay out of
+// the per-item paths).
+struct StepSplit { int Lc, chunk, nsplit; };
 
-MBK_DEV int n_splits(const Params &p, int pos) {
-    const int Lc = pos + 1;
-    int chunk = (Lc + p.max_splits - 1) / p.max_splits;
-    if (chunk < p.attn_min_chunk) chunk = p.attn_min_chunk;
-    return (Lc + chunk - 1) / chunk;
+MBK_DEV StepSplit step_split(const Params &p, int pos) {
+    StepSplit r;
+    r.Lc = pos + 1;
+    r.chunk = max((r.Lc + p.max_splits - 1) / p.max_splits, p.attn_min_chunk);
+    r.nsplit = (r.Lc + r.chunk - 1) / r.chunk;
+    return r;
 }
 
-MBK_DEV Split split_range(const Params &p, int s, int pos) {
-    const int Lc = pos + 1;
-    int chunk = (Lc + p.max_splits - 1) / p.max_splits;
-    if (chunk < p.attn_min_chunk) chunk = p.attn_min_chunk;
-    Split r;
-    r.nsplit = (Lc + chunk - 1) / chunk;
-    r.t0 = s * chunk;
-    r.t1 = min(Lc, r.t0 + chunk);
-    return r;
+struct Range { int t0, t1; };
+MBK_DEV Range split_range(const StepSplit &ss, int s) {
+    const int t0 = s * ss.chunk;
+    return Range{t0, min(ss.Lc, t0 + ss.chunk)};
 }
 
 struct Alloc {
@@ -400,24 +413,25 @@ MBK_DEV const uint16_t *kv_block(const Params &p, int layer, int which, int j) {
     return p.kv + (((size_t)layer * 2 + which) * p.nkv + j) * p.S * p.hd;
 }
 
-// An attention item: KV head j, split s, query heads h0 .. h0 + nh - 1 of the group.
+// An attention item (packed by the planner into the task's n): KV head j,
+// split s, query heads h0 .. h0 + nh - 1 of the group.
 struct AttnItem { int j, s, h0, nh; };
-MBK_DEV AttnItem attn_item(const Params &p, int item) {
-    const int jh = item / p.max_splits, s = item % p.max_splits;
-    if (p.attn_hpi == 1) return AttnItem{jh / p.gqa, s, jh % p.gqa, 1};
-    return AttnItem{jh, s, 0, p.gqa};
+MBK_DEV AttnItem attn_item(const Task &T) {
+    return AttnItem{T.n & 0xff, (T.n >> 8) & 0xff, (T.n >> 16) & 0xff, (int)((uint32_t)T.n >> 24)};
 }
 
-MBK_DEV int n_allocs(const Params &p, const Interval &iv, const Task &T, int pos) {
+// Cached positions [t0, min(t1, pos)) of an attention item, in pieces of
+// piece_pos (a power of two) positions.
+MBK_DEV int n_allocs(const Params &p, const Interval &iv, const Task &T, const StepSplit &ss) {
     if (iv.op != OP_ATTN) return 1;
-    const int s = T.a % p.max_splits;
-    const Split sp = split_range(p, s, pos);
-    if (s >= sp.nsplit) return 0;
-    const int te = min(sp.t1, pos);
-    return te > sp.t0 ? (te - sp.t0 + p.piece_pos - 1) / p.piece_pos : 0;
+    const int s = (T.n >> 8) & 0xff;
+    if (s >= ss.nsplit) return 0;
+    const Range r = split_range(ss, s);
+    const int te = min(r.t1, ss.Lc - 1);
+    return te > r.t0 ? (te - r.t0 + p.piece_pos - 1) >> __builtin_ctz((unsigned)p.piece_pos) : 0;
 }
 
-MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, int pos, int k) {
+MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, const StepSplit &ss, int k) {
     Alloc A;
     if (iv.op != OP_ATTN) {
         const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
@@ -429,31 +443,43 @@ MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, int
         A.size = A.b0;
         return A;
     }
-    const AttnItem it = attn_item(p, T.a);
-    const int j = it.j;
-    const Split sp = split_range(p, it.s, pos);
-    const int te = min(sp.t1, pos);
-    const int pa = sp.t0 + k * p.piece_pos, pb = min(te, pa + p.piece_pos);
+    const AttnItem it = attn_item(T);
+    const Range r = split_range(ss, it.s);
+    const int te = min(r.t1, ss.Lc - 1);
+    const int pa = r.t0 + k * p.piece_pos, pb = min(te, pa + p.piece_pos);
     const uint32_t row = (uint32_t)p.hd * 2u;
-    A.g0 = (const uint8_t *)kv_block(p, iv.layer, 0, j) + (size_t)pa * row;
-    A.g1 = (const uint8_t *)kv_block(p, iv.layer, 1, j) + (size_t)pa * row;
+    A.g0 = (const uint8_t *)kv_block(p, iv.layer, 0, it.j) + (size_t)pa * row;
+    A.g1 = (const uint8_t *)kv_block(p, iv.layer, 1, it.j) + (size_t)pa * row;
     A.b0 = A.b1 = (uint32_t)(pb - pa) * row;
-    A.r1 = (A.b0 + kChunk - 1) / kChunk * kChunk;
+    A.r1 = (A.b0 + (kChunk - 1u)) & ~(kChunk - 1u);
     A.size = 2u * A.r1;
     return A;
 }
 
 // Chunks of a segment of `bytes` handled by loader wave w: chunk c of every
 // segment goes to wave c % kLW.
-MBK_DEV uint32_t wave_chunks(uint32_t bytes, int w) {
-    const int nch = (int)((bytes + kChunk - 1) / kChunk);
-    return nch > w ? (uint32_t)((nch - w + kLW - 1) / kLW) : 0u;
+MBK_DEV uint32_t wave_chunks(uint32_t bytes, uint32_t w) {
+    static_assert((kChunk & (kChunk - 1)) == 0 && (kLW & (kLW - 1)) == 0, "shifts");
+    const uint32_t nch = (bytes + (kChunk - 1u)) / (uint32_t)kChunk;
+    return nch > w ? (nch - w + (uint32_t)kLW - 1u) / (uint32_t)kLW : 0u;
 }
 
-// Virtual start of an allocation of `size` bytes after offset v.
-MBK_DEV uint32_t ring_place(uint32_t v, uint32_t size, uint32_t R) {
-    const uint32_t r = v % R;
-    return r + size > R ? v + (R - r) : v;
+// Position in the allocation sequence: virtual offset v and its ring offset
+// r = v mod R, kept together so that placing needs no division.
+struct RingCursor { uint32_t v, r; };
+
+// Places an allocation of `size` bytes: at the cursor, or at the start of the
+// next turn of the ring if it would straddle the end.  Returns the ring
+// offset of its start; the cursor moves to its end.
+MBK_DEV uint32_t ring_place(RingCursor &c, uint32_t size, uint32_t R) {
+    if (c.r + size > R) {
+        c.v += R - c.r;
+        c.r = 0;
+    }
+    const uint32_t at = c.r;
+    c.v += size;
+    c.r += size;
+    return at;
 }
 
 // ---- loader waves ------------------------------------------------------------------------------------
@@ -526,8 +552,10 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
     const int lw = wave_id() - kCW;
     const uint32_t R = (uint32_t)p.ring_bytes;
     uint8_t *ring = lds + p.lds_ring;
-    uint32_t vpos = 0, issued = 0, published = 0, cons_seen = 0;
+    RingCursor rc{0u, 0u};
+    uint32_t issued = 0, published = 0, cons_seen = 0;
     int inbatch = 0, cur = -1;
+    const StepSplit ss = step_split(p, pos);
     Interval iv;
     for (int k = 0; k < nt; ++k) {
         const Task T = task_opaque(lds, p, k);
@@ -535,11 +563,11 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
             iv = interval_opaque(p, lds, T.iv);
             cur = T.iv;
         }
-        const int na = n_allocs(p, iv, T, pos);
+        const int na = n_allocs(p, iv, T, ss);
         const uint32_t sc1 = iv.op == OP_ATTN ? 1u : 0u;
         for (int ai = 0; ai < na; ++ai) {
-            const Alloc A = task_alloc(p, iv, T, pos, ai);
-            const uint32_t start = ring_place(vpos, A.size, R), end = start + A.size;
+            const Alloc A = task_alloc(p, iv, T, ss, ai);
+            const uint32_t at = ring_place(rc, A.size, R), end = rc.v;
             if ((int32_t)(end - R - cons_seen) > 0) {
                 // ring full: publish completed chunks oldest first until the
                 // compute waves have released enough space
@@ -577,14 +605,13 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
                 }
                 inbatch = 0;
             }
-            uint8_t *base = ring + (start % R);
+            uint8_t *base = ring + at;
             if (sc1) {
                 dma_segment<1>(A.g0, base, A.b0, lw, ctl, issued, published, inbatch);
                 if (A.b1) dma_segment<1>(A.g1, base + A.r1, A.b1, lw, ctl, issued, published, inbatch);
             } else {
                 dma_segment<0>(A.g0, base, A.b0, lw, ctl, issued, published, inbatch);
             }
-            vpos = end;
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -596,7 +623,7 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
 // Barrier among the compute waves (LDS counter).  gen counts this wave's barriers.
 MBK_DEV bool cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
     gen += kCW;
-    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(&ctl.bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((threadIdx.x & 63) == 0) __atomic_fetch_add((lds_u32 *)&ctl.bar, 1u, __ATOMIC_RELAXED);
     for (int it = 0; (int32_t)(lds_ld(&ctl.bar) - gen) < 0; ++it) {
         if (lds_ld(&ctl.abort)) return false;
         if (it >= p.spin_limit) { set_error(p); lds_st(&ctl.abort, 1u); return false; }
@@ -607,7 +634,7 @@ MBK_DEV bool cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
 
 // Position of the compute waves in the allocation sequence.
 struct RingPos {
-    uint32_t vpos;
+    RingCursor cur;
     uint32_t cum[kLW];    // chunks of each loader wave up to the current allocation
     uint32_t seen[kLW];   // loader progress last read from LDS
 };
@@ -615,18 +642,19 @@ struct RingPos {
 // All loader waves' progress with one LDS read.
 MBK_DEV void read_prog(Ctl &ctl, uint32_t *out) {
     static_assert(kLW == 4, "one 16-byte read of the loader progress");
-    const u32x4 v = *(volatile u32x4 *)ctl.prog;
-    asm volatile("" ::: "memory");
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    const u32x4 v = lds_ld16(ctl.prog);
+    out[0] = __builtin_amdgcn_readfirstlane(v.x);
+    out[1] = __builtin_amdgcn_readfirstlane(v.y);
+    out[2] = __builtin_amdgcn_readfirstlane(v.z);
+    out[3] = __builtin_amdgcn_readfirstlane(v.w);
 }
 
 // Places the next allocation; waits until the loader waves have completed it.
-// Returns its virtual start, or ~0 when the wait failed.
+// Returns its ring offset, or ~0 when the wait failed.
 MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Alloc &A) {
-    const uint32_t start = ring_place(rp.vpos, A.size, (uint32_t)p.ring_bytes);
-    rp.vpos = start + A.size;
+    const uint32_t start = ring_place(rp.cur, A.size, (uint32_t)p.ring_bytes);
 #pragma unroll
-    for (int w = 0; w < kLW; ++w) rp.cum[w] += wave_chunks(A.b0, w) + wave_chunks(A.b1, w);
+    for (int w = 0; w < kLW; ++w) rp.cum[w] += wave_chunks(A.b0, (uint32_t)w) + wave_chunks(A.b1, (uint32_t)w);
     // the loader is usually far ahead: the progress read last time often covers this allocation
     for (int it = 0;; ++it) {
         bool ready = true;
@@ -642,7 +670,7 @@ MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Allo
     }
 }
 
-MBK_DEV void ring_release(Ctl &ctl, const RingPos &rp) { lds_st(&ctl.cons[wave_id()], rp.vpos); }
+MBK_DEV void ring_release(Ctl &ctl, const RingPos &rp) { lds_st(&ctl.cons[wave_id()], rp.cur.v); }
 
 // ---- GEMV input vectors ------------------------------------------------------------------------------
 // GEMV input vectors live in LDS as bf16 pairs: each 8-element group g is 32
@@ -723,17 +751,15 @@ MBK_DEV bool poll2(const Params &p, uint64_t base, int i, uint32_t tag, float &a
     }
 }
 
-MBK_DEV int n_splits(const Params &p, int pos);
-
 // xs <- hi/lo pairs of the attention output, merged from the split partials
 // (log-sum-exp merge in split order): thread u takes query head u / (hd/8),
 // dims 8 * (u % (hd/8)) .. + 8.  Threads [tid, nt).
-MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int pos, int tid, int nt, bool &ok) {
-    const int hd = p.hd, gpr = hd / 8, G = p.gqa;
-    const int nsplit = n_splits(p, pos);
+template <int G>
+MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, int tid, int nt, bool &ok) {
+    const int hd = p.hd, gsh = p.hd_shift - 3, gpr = 1 << gsh;
     constexpr int kPer = kPollMax / 5;  // splits per polling round: {max, sum} chunk + 4 chunks of acc
     for (int u = tid; u < p.nq * gpr; u += nt) {
-        const int h = u / gpr, g = u % gpr, j = h / G, hh = h % G;
+        const int h = u >> gsh, g = u & (gpr - 1), j = h / G, hh = h - j * G;
         float M = -INFINITY, L = 0.f, a[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = 0.f;
@@ -827,6 +853,7 @@ MBK_DEV float gemv_tile(const MatGeom &g, const uint8_t *wt, const float *xs) {
 
 struct StepCtx {
     int pos, token;
+    StepSplit ss;    // this step's attention split
     uint32_t seq;
     float rnorm;     // 1/rms of the interval's normalised input (1 when not normalised)
     uint32_t gen;    // compute-wave barrier generation
@@ -952,8 +979,11 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
 
 // ---- interval inputs (compute waves, threads [0, kCW * 64)) ------------------------------------------
 
-// Returns this thread's part of the RMSNorm sum of squares (0 if none).
-MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t *lds, StepCtx &sc, bool &ok) {
+// Returns this thread's part of the RMSNorm sum of squares (0 if none).  T is
+// the workgroup's first task of the interval.
+template <int G>
+MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, int ivi, uint8_t *lds, StepCtx &sc,
+                          bool &ok) {
     const int tid = threadIdx.x, nt = kCW * 64;
     float *xs = (float *)(lds + p.lds_xs + sc.in);
     const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(p, sc.seq, iv.x_src);
@@ -962,8 +992,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
         case OP_DOWN: {
             // residual rows of this workgroup's tile block
             const MatGeom &g = iv.mat;
-            const int k = participant(iv, blockIdx.x, p.n_wg);
-            const int b0 = block_begin(iv.n_items, k, iv.nwg), b1 = block_begin(iv.n_items, k + 1, iv.nwg);
+            const int b0 = T.a, b1 = T.flags >> 8;  // this workgroup's tile block
             sc.blk0 = b0;
             float *xres = (float *)(lds + p.lds_xres + sc.in);
             const int r0 = b0 * g.RT, r1 = min(b1 * g.RT, g.rows);
@@ -976,7 +1005,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
                     return 0.f;
                 }
             }
-            if (iv.op == OP_O && p.merge_in_o) merge_input(p, xs, tag_of(p, sc.seq, ivi - 1), sc.pos, tid, nt, ok);
+            if (iv.op == OP_O && p.merge_in_o) merge_input<G>(p, xs, tag_of(p, sc.seq, ivi - 1), sc.ss.nsplit, tid, nt, ok);
             else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt, ok);
             else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt, ok);
             return 0.f;
@@ -1006,10 +1035,11 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, int ivi, uint8_t 
 // Attention item inputs: the G queries of its KV head, pre-scaled, and the
 // key and value appended this step, rounded to bf16 exactly as the cache
 // holds them.  LDS at lds_qkv: [G][hd] queries, [hd] key, [hd] value.
-MBK_DEV void attn_inputs(const Params &p, int item, int ivi, uint8_t *lds, const StepCtx &sc, bool &ok) {
+template <int G>
+MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, const StepCtx &sc, bool &ok) {
     const int tid = threadIdx.x, nt = kCW * 64;
-    const AttnItem it = attn_item(p, item);
-    const int G = p.gqa, hd = p.hd, kg = hd / 8, qg = it.nh * kg;
+    const AttnItem it = attn_item(T);
+    const int hd = p.hd, kg = hd >> 3, qg = it.nh * kg;
     const uint32_t tag = tag_of(p, sc.seq, ivi - 1);
     float *dst = (float *)(lds + p.lds_qkv + sc.in);
     for (int g = tid; g < qg + 2 * kg; g += nt) {
@@ -1088,12 +1118,13 @@ MBK_DEV void put2(const Params &p, uint64_t base, int i, float a, float b, uint3
 template <int G>
 MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const Task &T, uint8_t *lds, Ctl &ctl,
                             RingPos &rp, StepCtx &sc) {
-    const int pos = sc.pos, hd = p.hd, LP = hd / 8, PPW = 64 / LP;
-    const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane % LP, slot = lane / LP;
-    const AttnItem item = attn_item(p, T.a);
+    const int pos = sc.pos, hd = p.hd, lsh = p.hd_shift - 3, LP = 1 << lsh, PPW = 64 >> lsh;
+    const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane & (LP - 1), slot = lane >> lsh;
+    const AttnItem item = attn_item(T);
     const int j = item.j, s = item.s, h0 = item.h0, nh = item.nh;
-    const Split sp = split_range(p, s, pos);
-    if (s >= sp.nsplit) return true;  // no allocations either
+    if (s >= sc.ss.nsplit) return true;  // no allocations either
+    const Range sp = split_range(sc.ss, s);
+    const int nsplit = sc.ss.nsplit;
     const float *qkv = (const float *)(lds + p.lds_qkv + sc.in);
     const float *cur = qkv + G * hd;        // this step's key, then value
     float *scores = (float *)(lds + p.lds_score);   // [G][piece_pos + 1]
@@ -1116,19 +1147,19 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
     const uint8_t *ring = lds + p.lds_ring;
-    const int na = n_allocs(p, iv, T, pos);
+    const int na = n_allocs(p, iv, T, sc.ss);
     const bool has_cur = pos >= sp.t0 && pos < sp.t1;
     const int nseg = na > 0 ? na : (has_cur ? 1 : 0);
     for (int k = 0; k < nseg; ++k) {
         const uint8_t *kb = nullptr, *vb = nullptr;
         int nring = 0;
         if (k < na) {
-            const Alloc A = task_alloc(p, iv, T, pos, k);
+            const Alloc A = task_alloc(p, iv, T, sc.ss, k);
             const uint32_t start = ring_acquire(p, ctl, rp, A);
             if (start == ~0u) return false;
-            kb = ring + start % (uint32_t)p.ring_bytes;
+            kb = ring + start;
             vb = kb + A.r1;
-            nring = (int)(A.b0 / (uint32_t)(hd * 2));
+            nring = (int)(A.b0 >> (p.hd_shift + 1));
         }
         const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
         // scores of this segment
@@ -1235,7 +1266,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.part, e0 + dl * 8 + e, a[e], a[e + 1], tag);
                 if (dl == 0) put2(p, p.wl.part, e0 + hd, M[h], ll, tag);
-            } else if (sp.nsplit == 1) {
+            } else if (nsplit == 1) {
                 const float inv = 1.f / ll;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.o, o0 + e, a[e] * inv, a[e + 1] * inv, tag);
@@ -1250,14 +1281,14 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
         }
     }
-    if (sp.nsplit > 1 && !p.merge_in_o) {
+    if (nsplit > 1 && !p.merge_in_o) {
         // the last split to arrive (one atomic per split) merges all partials in
         // split order, so the result does not depend on arrival order
         if (threadIdx.x == 0) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
             uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.merge_cnt + 256u * j);
             // every item of the group arrives: splits x (query heads / heads per item)
-            const bool last = atom_add(cnt, 1u) == (uint32_t)(sp.nsplit * (G / nh)) - 1u;
+            const bool last = atom_add(cnt, 1u) == (uint32_t)(nsplit * (nh == 1 ? G : 1)) - 1u;
             if (last) {
                 stc_u(cnt, 0u);
                 __builtin_amdgcn_s_waitcnt(0);  // the reset lands before this group's output does
@@ -1265,17 +1296,17 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             ctl.last_s = last;
         }
         if (!cw_barrier(p, ctl, sc.gen)) return false;
-        if (ctl.last_s) {
+        if (lds_ld((const uint32_t *)&ctl.last_s)) {
             // every partial of head group j into LDS (scratch holds max_splits * G * stride floats)
             const uint64_t gbase = p.wl.part + ((uint64_t)(j * p.max_splits) * G) * stride * 4u;
-            const int n16 = sp.nsplit * G * stride / 4;
+            const int n16 = nsplit * G * stride / 4;
             for (int idx = threadIdx.x; idx < n16; idx += kCW * 64)
                 *(u32x4 *)(scr + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
             if (!cw_barrier(p, ctl, sc.gen)) return false;
             for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
-                const int h = idx / hd, e = idx % hd;
+                const int h = idx >> p.hd_shift, e = idx & (hd - 1);
                 float mm = -INFINITY, ll = 0.f, a0 = 0.f, a1 = 0.f;
-                for (int q = 0; q < sp.nsplit; ++q) {
+                for (int q = 0; q < nsplit; ++q) {
                     const float *r = scr + ((size_t)q * G + h) * stride;
                     const float m2 = r[0], mn = fmaxf(mm, m2);
                     if (mn == -INFINITY) continue;
@@ -1321,7 +1352,7 @@ MBK_DEV Task task_at(const Params &p, const uint8_t *lds, int k) {
 template <int G>
 MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &sc) {
     RingPos rp;
-    rp.vpos = 0;
+    rp.cur = RingCursor{0u, 0u};
 #pragma unroll
     for (int w = 0; w < kLW; ++w) rp.cum[w] = rp.seen[w] = 0;
     const int cw = wave_id();
@@ -1342,30 +1373,30 @@ MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &s
             else if (!cw_barrier(p, ctl, sc.gen)) return false;
             bool ok = true;
             float ss = 0.f;
-            if (iv.op == OP_ATTN) attn_inputs(p, T.a, ivi, lds, sc, ok);
-            else ss = gemv_inputs(p, iv, ivi, lds, sc, ok);
+            if (iv.op == OP_ATTN) attn_inputs<G>(p, T, ivi, lds, sc, ok);
+            else ss = gemv_inputs<G>(p, iv, T, ivi, lds, sc, ok);
             ss = group_sum<64>(ss);
             if ((threadIdx.x & 63) == 0) ctl.ss[par][cw] = ss;
-            if (!ok) { lds_st(&ctl.abort, 1u); return false; }
+            if (any_lane(!ok)) { lds_st(&ctl.abort, 1u); return false; }
             if (!cw_barrier(p, ctl, sc.gen)) return false;
             stamp(p, lds, ivi, 1);
             sc.rnorm = 1.f;
             if (iv.op == OP_QKV || iv.op == OP_GATEUP || iv.op == OP_LMHEAD) {
                 static_assert(kCW == 4, "one 16-byte read of the partial sums");
-                const u32x4 s4 = *(volatile u32x4 *)ctl.ss[par];
+                const u32x4 s4 = lds_ld16(ctl.ss[par]);
                 const float tot = (__uint_as_float(s4.x) + __uint_as_float(s4.y)) +
                                   (__uint_as_float(s4.z) + __uint_as_float(s4.w));
-                sc.rnorm = rsqrtf(tot / (float)p.H + p.eps);
+                sc.rnorm = rsqrtf(tot * p.inv_h + p.eps);
             }
             const uint32_t tag = tag_of(p, sc.seq, ivi);
             for (;;) {
                 if (iv.op == OP_ATTN) {
                     if (!attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc)) return false;
                 } else {
-                    const Alloc A = task_alloc(p, iv, T, sc.pos, 0);
+                    const Alloc A = task_alloc(p, iv, T, sc.ss, 0);
                     const uint32_t start = ring_acquire(p, ctl, rp, A);
                     if (start == ~0u) return false;
-                    const uint8_t *wt = lds + p.lds_ring + start % (uint32_t)p.ring_bytes;
+                    const uint8_t *wt = lds + p.lds_ring + start;
                     const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
                     for (int t = cw; t < T.n; t += kCW) gemv_tile_op(p, iv, lds, wt + (size_t)t * tile_bytes, T.a + t, sc, tag);
                     ring_release(ctl, rp);
@@ -1379,8 +1410,8 @@ MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &s
                 if (iv.op == OP_ATTN) {
                     // a further item of the same interval: its own inputs
                     if (!cw_barrier(p, ctl, sc.gen)) return false;
-                    attn_inputs(p, T.a, ivi, lds, sc, ok);
-                    if (!ok) { lds_st(&ctl.abort, 1u); return false; }
+                    attn_inputs<G>(p, T, ivi, lds, sc, ok);
+                    if (any_lane(!ok)) { lds_st(&ctl.abort, 1u); return false; }
                     if (!cw_barrier(p, ctl, sc.gen)) return false;
                 }
             }
@@ -1455,6 +1486,7 @@ MBK_DEV void run_step(const Params &p) {
     } else {
         StepCtx sc;
         sc.pos = pos;
+        sc.ss = step_split(p, pos);
         sc.token = step_token(p);
         sc.seq = step_seq(p);
         sc.rnorm = 1.f;

@@ -116,9 +116,20 @@ enum TaskFlag : int32_t { TASK_FIRST = 1, TASK_LAST = 2 };
 struct Task {
     int32_t iv;     // interval
     int32_t a;      // GEMV: first tile; attention: item
-    int32_t n;      // GEMV: tiles; attention: 1
-    int32_t flags;  // TASK_FIRST: first task of this workgroup in iv; TASK_LAST: last one
+    int32_t n;      // GEMV: tiles; attention: the item packed by attn_task_item
+    int32_t flags;  // bit 0 TASK_FIRST: first task of this workgroup in iv; bit 1 TASK_LAST: last one;
+                    // GEMV: bits 8.. hold the end of the workgroup's tile block
 };
+
+// Attention item `item` of an interval with ms splits per item group: KV
+// head j, split s, query heads h0 .. h0 + nh - 1 of the group (one query head
+// per item when hpi is 1, else all G of the KV head), packed as
+// j | s << 8 | h0 << 16 | nh << 24.
+MBK_HD int32_t attn_task_item(int item, int ms, int G, int hpi) {
+    const int jh = item / ms, s = item % ms;
+    const int j = hpi == 1 ? jh / G : jh, h0 = hpi == 1 ? jh % G : 0, nh = hpi == 1 ? 1 : G;
+    return (int32_t)((uint32_t)j | ((uint32_t)s << 8) | ((uint32_t)h0 << 16) | ((uint32_t)nh << 24));
+}
 
 // Block of tiles of participant k out of nwg over ntiles tiles.
 MBK_HD int block_begin(int64_t ntiles, int k, int nwg) { return (int)(ntiles * k / nwg); }

@@ -281,6 +281,8 @@ std::string build_plan(mbk_model *m) {
     }
     P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, none, 5 * c.n_layers - 1));
     const int n_iv = (int)P.iv.size();
+    for (const Interval &v : P.iv)
+        if (v.n_items >= (1 << 23)) return "too many tiles in one operator";
     int rot = 0;
     for (Interval &v : P.iv) {
         v.nwg = std::min(n_wg, v.n_items);
@@ -339,11 +341,13 @@ std::string build_plan(mbk_model *m) {
                 if (k < 0) continue;
                 const size_t first = P.task_list.size();
                 if (v.op == OP_ATTN) {
-                    for (int it = k; it < v.n_items; it += v.nwg) P.task_list.push_back(Task{i, it, 1, 0});
+                    for (int it = k; it < v.n_items; it += v.nwg)
+                        P.task_list.push_back(Task{i, it, attn_task_item(it, P.max_splits, G, P.attn_hpi), 0});
                 } else {
                     const int b0 = block_begin(v.n_items, k, v.nwg), b1 = block_begin(v.n_items, k + 1, v.nwg);
                     const int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
-                    for (int t = b0; t < b1; t += per) P.task_list.push_back(Task{i, t, std::min(per, b1 - t), 0});
+                    for (int t = b0; t < b1; t += per)
+                        P.task_list.push_back(Task{i, t, std::min(per, b1 - t), b1 << 8});
                 }
                 if (P.task_list.size() > first) {
                     P.task_list[first].flags |= TASK_FIRST;
@@ -391,6 +395,7 @@ std::string build_plan(mbk_model *m) {
     // attention pieces: at most a third of the ring, keys and values each rounded up to whole chunks
     P.piece_pos = std::min(kPiecePos, (int)((ring / 3 / 2) / kChunk * kChunk / ((size_t)hd * 2)));
     if (P.piece_pos < 1) return "attention piece too small";
+    while (P.piece_pos & (P.piece_pos - 1)) P.piece_pos &= P.piece_pos - 1;  // a power of two
 
     P.table = cur;
     cur = align256(cur + P.iv.size() * sizeof(Interval));
@@ -509,6 +514,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.max_tasks = P.max_tasks;
     p.eps = c.rms_eps;
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
+    p.inv_h = 1.0f / (float)c.hidden;
     p.token = token;
     p.pos = pos;
     p.seq = m->seq;
@@ -572,6 +578,7 @@ int mbk_create(const mbk_config *cfg, mbk_model **out) {
         return fail(MBK_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", c.head_dim);
     if (c.n_heads % c.n_kv_heads != 0) return fail(MBK_ERR_UNSUPPORTED, "n_heads %% n_kv_heads != 0");
     if (c.n_heads / c.n_kv_heads > kMaxGqa) return fail(MBK_ERR_UNSUPPORTED, "more than %d query heads per KV head", kMaxGqa);
+    if (c.n_kv_heads > 255) return fail(MBK_ERR_UNSUPPORTED, "more than 255 KV heads");
     const int Q = c.n_heads * c.head_dim;
     if (c.hidden % 8 || Q % 8 || c.intermediate % 8) return fail(MBK_ERR_UNSUPPORTED, "hidden, heads*head_dim and intermediate must be multiples of 8");
     if (c.hidden > kMaxVec || Q > kMaxVec || c.intermediate > kMaxVec)
