@@ -102,6 +102,18 @@ struct Ctl {
 
 #define MBK_DEV __device__ __forceinline__
 
+// The launch parameters as the kernel-argument segment holds them (the
+// kernels take Params as their first and only argument), through a pointer
+// the compiler cannot follow from one call to the next: a loop that calls
+// this once per iteration loads each field from the constant cache where it
+// is used, instead of holding every field in scalar registers for the whole
+// loop (which would spill them).
+MBK_DEV const Params &params_opaque() {
+    auto pp = (__attribute__((address_space(4))) const Params *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pp));
+    return *(const Params *)pp;
+}
+
 // ---- access helpers ------------------------------------------------------------------------------
 
 MBK_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -1350,14 +1362,15 @@ MBK_DEV Task task_at(const Params &p, const uint8_t *lds, int k) {
 // Compute waves: every interval of [first_iv, last_iv) in order; tasks [0, nt)
 // of this workgroup in LDS.  False when a wait failed (the workgroup leaves).
 template <int G>
-MBK_DEV bool compute(const Params &p, uint8_t *lds, Ctl &ctl, int nt, StepCtx &sc) {
+MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &sc) {
     RingPos rp;
     rp.cur = RingCursor{0u, 0u};
 #pragma unroll
     for (int w = 0; w < kLW; ++w) rp.cum[w] = rp.seen[w] = 0;
     const int cw = wave_id();
     int k = 0;
-    for (int ivi = p.first_iv; ivi < p.last_iv; ++ivi) {
+    for (int ivi = p0.first_iv; ivi < p0.last_iv; ++ivi) {
+        const Params &p = params_opaque();
         if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return false;
         Task T;
         T.iv = -1;

@@ -36,16 +36,17 @@ __global__ __launch_bounds__(kThreads) void k_persistent(Params p) {
     run_step<G>(p);
 }
 
+// Params must stay the first kernel argument and reach the body unmodified:
+// the compute waves read it from the kernel-argument segment (params_opaque).
+// The ablation's host sets first_iv / last_iv to the launch's interval.
 template <int G>
-__global__ __launch_bounds__(kThreads) void k_interval(Params p, int ivi) {
-    p.first_iv = ivi;
-    p.last_iv = ivi + 1;
+__global__ __launch_bounds__(kThreads) void k_interval(Params p) {
     run_step<G>(p);
 }
 
 // One instance per query-group size G (query heads per KV head).
 typedef void (*persistent_fn)(Params);
-typedef void (*interval_fn)(Params, int);
+typedef void (*interval_fn)(Params);
 static const persistent_fn kPersistent[kMaxGqa] = {k_persistent<1>, k_persistent<2>, k_persistent<3>, k_persistent<4>,
                                                    k_persistent<5>, k_persistent<6>, k_persistent<7>, k_persistent<8>};
 static const interval_fn kInterval[kMaxGqa] = {k_interval<1>, k_interval<2>, k_interval<3>, k_interval<4>,
@@ -713,8 +714,12 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
     p.barrier = 0;
     const unsigned lds = (unsigned)m->plan.lds_bytes;
     if (!use_graph) {
-        for (int i = 0; i < p.n_intervals; ++i)
-            hipLaunchKernelGGL(kInterval[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), lds, st, p, i);
+        for (int i = 0; i < p.n_intervals; ++i) {
+            Params pi = p;
+            pi.first_iv = i;
+            pi.last_iv = i + 1;
+            hipLaunchKernelGGL(kInterval[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), lds, st, pi);
+        }
         HIPCHK(hipGetLastError());
         return MBK_OK;
     }
@@ -723,11 +728,11 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
         HIPCHK(hipGraphCreate(&m->graph, 0));
         hipGraphNode_t prev = nullptr;
         std::vector<Params> ps(p.n_intervals, p);
-        std::vector<int> idx(p.n_intervals);
         for (int i = 0; i < p.n_intervals; ++i) {
             ps[i].step_from_ws = i == 0 ? 0 : 1;
-            idx[i] = i;
-            void *kargs[] = {&ps[i], &idx[i]};
+            ps[i].first_iv = i;
+            ps[i].last_iv = i + 1;
+            void *kargs[] = {&ps[i]};
             hipKernelNodeParams kp{};
             kp.func = (void *)kInterval[p.gqa - 1];
             kp.gridDim = dim3(m->n_wg);
@@ -743,8 +748,9 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
         m->g_logits = logits;
         m->g_argmax = argmax;
     }
-    int zero = 0;
-    void *kargs[] = {&p, &zero};
+    p.first_iv = 0;
+    p.last_iv = 1;
+    void *kargs[] = {&p};
     hipKernelNodeParams kp{};
     kp.func = (void *)kInterval[p.gqa - 1];
     kp.gridDim = dim3(m->n_wg);
