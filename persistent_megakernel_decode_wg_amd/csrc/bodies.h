@@ -212,9 +212,37 @@ MBK_DEV uint32_t tag_of(const Params &p, uint32_t seq, int ivi) {
     return seq * (uint32_t)p.n_intervals + (uint32_t)ivi + 1u;
 }
 
+// Polling loops read memory that other workgroups write: the buffer loads
+// they use are not atomic, so without this compiler barrier between two
+// rounds the compiler may assume a repeated read returns the same value and
+// fold the loop away.  Emits no instruction.
+MBK_DEV void reread() { asm volatile("" ::: "memory"); }
+
 MBK_DEV void put(const Params &p, uint64_t base, int i, float v, uint32_t tag) {
     __hip_atomic_store(ws_ptr<uint64_t>(p, base) + i, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 64 bytes of a tagged vector: 8 entries, tags in the odd words.
+struct Group8 { u32x4 c[4]; };
+MBK_DEV Group8 load8(const Params &p, uint32_t off) {
+    Group8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.c[i] = ldc16(p.ws, off + 16u * i);
+    return r;
+}
+MBK_DEV bool tagged8(const Group8 &r, uint32_t tag) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok = ok && r.c[i].y == tag && r.c[i].w == tag;
+    return ok;
+}
+MBK_DEV void values8(const Group8 &r, float *v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(r.c[i].x);
+        v[2 * i + 1] = __uint_as_float(r.c[i].z);
+    }
 }
 
 // v[0..8) <- entries 8g..8g+7 of the tagged vector at base, once all of them
@@ -222,18 +250,14 @@ MBK_DEV void put(const Params &p, uint64_t base, int i, float v, uint32_t tag) {
 MBK_DEV bool poll8(const Params &p, uint64_t base, int g, uint32_t tag, float *v) {
     const uint32_t off = (uint32_t)(base + 64u * (uint32_t)g);
     for (int it = 0;; ++it) {
-        const u32x4 a = ldc16(p.ws, off), b = ldc16(p.ws, off + 16u), c = ldc16(p.ws, off + 32u),
-                    d = ldc16(p.ws, off + 48u);
-        if (a.y == tag && a.w == tag && b.y == tag && b.w == tag && c.y == tag && c.w == tag && d.y == tag &&
-            d.w == tag) {
-            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.z);
-            v[2] = __uint_as_float(b.x); v[3] = __uint_as_float(b.z);
-            v[4] = __uint_as_float(c.x); v[5] = __uint_as_float(c.z);
-            v[6] = __uint_as_float(d.x); v[7] = __uint_as_float(d.z);
+        const Group8 a = load8(p, off);
+        if (tagged8(a, tag)) {
+            values8(a, v);
             return true;
         }
         if (it >= p.spin_limit) { set_error(p); return false; }
         if (aborted(p, it)) return false;
+        reread();
     }
 }
 
@@ -248,6 +272,7 @@ MBK_DEV bool poll1(const Params &p, uint64_t base, int i, uint32_t tag, float &v
         }
         if (it >= p.spin_limit) { set_error(p); return false; }
         if (aborted(p, it)) return false;
+        reread();
     }
 }
 
@@ -274,6 +299,7 @@ MBK_DEV bool poll_round(const Params &p, const uint32_t *off, const uint32_t *ne
         if (!pending) return true;
         if (it >= p.spin_limit) { set_error(p); return false; }
         if (aborted(p, it)) return false;
+        reread();
     }
 }
 
@@ -745,21 +771,6 @@ MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag
         float v[8];
         if (!poll8(p, base, g, tag, v)) { ok = false; return; }
         split8_store(xs + 8 * g, v);
-    }
-}
-
-// Entries i, i+1 (i even) of a tagged vector.
-MBK_DEV bool poll2(const Params &p, uint64_t base, int i, uint32_t tag, float &a, float &b) {
-    const uint32_t off = (uint32_t)(base + 8u * (uint32_t)i);
-    for (int it = 0;; ++it) {
-        const u32x4 v = ldc16(p.ws, off);
-        if (v.y == tag && v.w == tag) {
-            a = __uint_as_float(v.x);
-            b = __uint_as_float(v.z);
-            return true;
-        }
-        if (it >= p.spin_limit) { set_error(p); return false; }
-        if (aborted(p, it)) return false;
     }
 }
 
