@@ -185,6 +185,7 @@ def main():
     }
     # the other interval ordering of the same persistent kernel
     extra["sync_mode"] = args.sync
+    extra["launch"] = "plain launch, one workgroup per compute unit"
     if not args.no_other_mode:
         other = "barrier" if args.sync == "dataflow" else "dataflow"
         dec.set_sync_mode(sync_modes[other])

@@ -157,6 +157,19 @@ int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */
 int mbk_set_sync_mode(mbk_model *m, int32_t mode);
 
+/* How mbk_decode_step launches the persistent kernel.  Every workgroup of it
+ * must be resident at once (they wait for one another).
+ * PLAIN (default): an ordinary launch of one workgroup per compute unit,
+ *   each workgroup taking most of its unit's LDS, so that an otherwise idle
+ *   device holds all of them; the caller keeps other kernels off the device
+ *   while a step runs (a workgroup kept out by another kernel only starts
+ * *   when that kernel ends; the bounded waits report MBK_ERR_TIMEOUT if that
+ *   takes too long).
+ * COOPERATIVE: a cooperative launch, which the runtime admits only when all
+ *   workgroups can be resident; about 15 us more per step on MI355X. */
+enum { MBK_LAUNCH_PLAIN = 0, MBK_LAUNCH_COOPERATIVE = 1 };
+int mbk_set_launch_mode(mbk_model *m, int32_t mode);
+
 /* Number of workgroups of the persistent kernel (one per compute unit); n = 0
  * (default) uses every compute unit of the current device.  Only before the
  * schedule is planned (the first mbk_pack_weights / mbk_alloc_kv /

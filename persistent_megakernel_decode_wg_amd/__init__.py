@@ -7,4 +7,5 @@ the import of ``Decoder`` fails loudly; there is no fallback path.
 """
 from .binding import (  # noqa: F401
     MBK_ERR_ARG, MBK_ERR_HIP, MBK_ERR_RANGE, MBK_ERR_SIZE, MBK_ERR_STATE, MBK_ERR_TIMEOUT, MBK_ERR_UNSUPPORTED,
-    MBK_OK, MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV, Decoder, MbkError, lib, lib_path)
+    MBK_LAUNCH_COOPERATIVE, MBK_LAUNCH_PLAIN, MBK_OK, MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV, Decoder,
+    MbkError, lib, lib_path)

@@ -13,6 +13,8 @@ MBK_ERR_HIP, MBK_ERR_TIMEOUT, MBK_ERR_STATE = 5, 6, 7
 MBK_TOKEN_PREV = -1
 MBK_SYNC_DATAFLOW = 0
 MBK_SYNC_BARRIER = 1
+MBK_LAUNCH_PLAIN = 0
+MBK_LAUNCH_COOPERATIVE = 1
 
 
 class MbkError(RuntimeError):
@@ -62,13 +64,14 @@ def lib():
         L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
         L.mbk_set_attention_split.argtypes = [vp, i32]
         L.mbk_set_sync_mode.argtypes = [vp, i32]
+        L.mbk_set_launch_mode.argtypes = [vp, i32]
         L.mbk_set_workgroups.argtypes = [vp, i32]
         L.mbk_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
                   "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
-                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_workgroups", "mbk_describe"):
+                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +208,10 @@ class Decoder:
     def set_sync_mode(self, mode: int) -> None:
         """MBK_SYNC_DATAFLOW (0, default) or MBK_SYNC_BARRIER (1)."""
         _chk(lib().mbk_set_sync_mode(self.h, int(mode)))
+
+    def set_launch_mode(self, mode: int) -> None:
+        """MBK_LAUNCH_PLAIN (0, default) or MBK_LAUNCH_COOPERATIVE (1)."""
+        _chk(lib().mbk_set_launch_mode(self.h, int(mode)))
 
     def set_attention_split(self, min_positions: int) -> None:
         _chk(lib().mbk_set_attention_split(self.h, int(min_positions)))

@@ -136,6 +136,7 @@ struct mbk_model {
     uint32_t epoch = 0;   // grid barriers completed on the bound workspace
     uint32_t seq = 0;     // decode steps run on the bound workspace (activation tags)
     int32_t sync_mode = MBK_SYNC_DATAFLOW;
+    int32_t launch_mode = MBK_LAUNCH_PLAIN;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
     int32_t attn_min_chunk = 128;
     int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
@@ -206,6 +207,10 @@ int ensure_kernels(mbk_model *m) {
     const int lds = (int)m->plan.lds_bytes;
     HIPCHK(hipFuncSetAttribute((const void *)kPersistent[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, lds));
     HIPCHK(hipFuncSetAttribute((const void *)kInterval[G - 1], hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    // a plain launch relies on one resident workgroup per compute unit
+    int per_cu = 0;
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kPersistent[G - 1], kThreads, (size_t)lds));
+    if (per_cu < 1) return fail(MBK_ERR_UNSUPPORTED, "the persistent kernel does not fit on a compute unit");
     m->kernels_ready = true;
     return MBK_OK;
 }
@@ -697,9 +702,15 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
     if (rc || (rc = ensure_kernels(m))) return rc;
     next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
-    void *args[] = {&p};
-    HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
-                                      (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
+    if (m->launch_mode == MBK_LAUNCH_COOPERATIVE) {
+        void *args[] = {&p};
+        HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
+                                          (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
+    } else {
+        hipLaunchKernelGGL(kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), (unsigned)m->plan.lds_bytes,
+                           (hipStream_t)stream, p);
+        HIPCHK(hipGetLastError());
+    }
     if (p.barrier) m->epoch += (uint32_t)(p.n_intervals - 1);
     return MBK_OK;
 }
@@ -792,6 +803,13 @@ int mbk_set_sync_mode(mbk_model *m, int32_t mode) {
     if (!m) return fail(MBK_ERR_ARG, "null model");
     if (mode != MBK_SYNC_DATAFLOW && mode != MBK_SYNC_BARRIER) return fail(MBK_ERR_ARG, "unknown sync mode %d", mode);
     m->sync_mode = mode;
+    return MBK_OK;
+}
+
+int mbk_set_launch_mode(mbk_model *m, int32_t mode) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    if (mode != MBK_LAUNCH_PLAIN && mode != MBK_LAUNCH_COOPERATIVE) return fail(MBK_ERR_ARG, "unknown launch mode %d", mode);
+    m->launch_mode = mode;
     return MBK_OK;
 }
 

@@ -52,10 +52,17 @@ class Pair:
         torch.cuda.synchronize()
 
     def gpu_step(self, token, pos, mode="mega"):
-        """mode: mega (persistent kernel, dataflow), barrier (persistent kernel, grid barriers),
-        ablation (one launch per interval) or graph (the ablation replayed as a hipGraph)."""
+        """mode: mega (persistent kernel, dataflow), cooperative (the same, cooperative launch),
+        barrier (persistent kernel, grid barriers), ablation (one launch per interval) or graph
+        (the ablation replayed as a hipGraph)."""
         if mode == "mega":
             self.dec.decode_step(token, pos, self.logits, self.am)
+        elif mode == "cooperative":
+            self.dec.set_launch_mode(1)
+            try:
+                self.dec.decode_step(token, pos, self.logits, self.am)
+            finally:
+                self.dec.set_launch_mode(0)
         elif mode == "barrier":
             self.dec.set_sync_mode(1)
             try:

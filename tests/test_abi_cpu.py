@@ -72,6 +72,9 @@ def test_step_before_pack_is_a_state_error_and_args_are_checked(L):
     assert L.mbk_decode_step(None, 1, 0, None, ctypes.byref(am), None) == 1        # MBK_ERR_ARG
     assert L.mbk_decode_step_ablation(h, 1, 0, None, ctypes.byref(am), 0, None) == 7
     assert L.mbk_set_debug(h, -1, 0, 0) == 1
+    assert L.mbk_set_launch_mode(h, 2) == 1                                       # unknown mode
+    assert L.mbk_set_launch_mode(h, 1) == 0 and L.mbk_set_launch_mode(h, 0) == 0
+    assert L.mbk_set_launch_mode(None, 0) == 1
     assert L.mbk_pack_weights(h, None, None, None, None) == 1
     L.mbk_destroy(h)
     L.mbk_destroy(None)

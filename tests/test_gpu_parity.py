@@ -21,7 +21,7 @@ def test_tiny_full_schedule_teacher_forced(tiny):
     log("tiny worst max|dlogit|/std = %.3g" % worst)
 
 
-@pytest.mark.parametrize("mode", ["barrier", "ablation", "graph"])
+@pytest.mark.parametrize("mode", ["cooperative", "barrier", "ablation", "graph"])
 def test_tiny_executors_are_bitwise_equal(tiny, mode):
     wl = tiny.wl
     prompt = list(synth.prompt_tokens(wl))
