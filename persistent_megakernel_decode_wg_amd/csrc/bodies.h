@@ -1092,24 +1092,20 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
 // takes one position per block and head dims dl*8 .. dl*8+7 (LP = hd/8
 // lanes per position); the compute waves take alternate blocks.  Positions
 // arrive in segments (the ring pieces, the last one extended by the position
-// appended this step).  Per segment: the scores go to LDS; one maximum per
-// head is formed over the whole workgroup; then exp(score - max) weights the
-// values.  With one shared maximum the lanes' and waves' sums combine by
-// plain addition; a new segment rescales the running sums once when the
-// maximum grows.
+// appended this step).  Each compute wave keeps its own running maximum, sum
+// and weighted values over its positions (online softmax: a segment that
+// raises the maximum rescales them once), so the waves never wait for one
+// another inside an item; at its end the wave partials meet in LDS and are
+// combined with the log-sum-exp rule, like the partials of different splits.
 
-// K and V of position t of a segment: ring positions t < nring (bf16), then
-// the appended position (fp32 in LDS).
-MBK_DEV void seg_kv(int t, int nring, const uint8_t *kb, const uint8_t *vb, const float *cur, int hd, int dl,
-                    float *kf, float *vf) {
+// Key (or value) of position t of a segment: ring positions t < nring
+// (bf16), then the appended position (fp32 in LDS at cur).
+MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int hd, int dl, float *f) {
     if (t < nring) {
-        unpack8(*(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16), kf);
-        unpack8(*(const u32x4 *)(vb + (size_t)t * hd * 2 + dl * 16), vf);
+        unpack8(*(const u32x4 *)(rb + (size_t)t * hd * 2 + dl * 16), f);
     } else {
         const float4 a = *(const float4 *)(cur + dl * 8), b = *(const float4 *)(cur + dl * 8 + 4);
-        const float4 c = *(const float4 *)(cur + hd + dl * 8), d = *(const float4 *)(cur + hd + dl * 8 + 4);
-        kf[0] = a.x; kf[1] = a.y; kf[2] = a.z; kf[3] = a.w; kf[4] = b.x; kf[5] = b.y; kf[6] = b.z; kf[7] = b.w;
-        vf[0] = c.x; vf[1] = c.y; vf[2] = c.z; vf[3] = c.w; vf[4] = d.x; vf[5] = d.y; vf[6] = d.z; vf[7] = d.w;
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     }
 }
 
@@ -1151,7 +1147,6 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     const float *qkv = (const float *)(lds + p.lds_qkv + sc.in);
     const float *cur = qkv + G * hd;        // this step's key, then value
     float *scores = (float *)(lds + p.lds_score);   // [G][piece_pos + 1]
-    float *wmax = scores + G * (p.piece_pos + 1);   // [2][kCW][G]
     const int sstride = p.piece_pos + 1;
     float qf[G][8];
 #pragma unroll
@@ -1185,14 +1180,14 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             nring = (int)(A.b0 >> (p.hd_shift + 1));
         }
         const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
-        // scores of this segment
+        // this wave's scores of the segment (to LDS, read back by the same lanes) and their maximum
         float lmax[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
         for (int b = cw; b * PPW < npos; b += kCW) {
             const int t = b * PPW + slot;
-            float kf[8], vf[8];
-            if (t < npos) seg_kv(t, nring, kb, vb, cur, hd, dl, kf, vf);
+            float kf[8];
+            if (t < npos) seg_row(t, nring, kb, cur, hd, dl, kf);
             else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kf[e] = 0.f;
@@ -1210,21 +1205,10 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                 }
             }
         }
-        // one maximum per head over the workgroup
-        float *wm = wmax + (k & 1) * kCW * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (h >= nh) break;
-            const float m = slot_max(lmax[h], LP);
-            if (lane == 0) wm[cw * G + h] = m;
-        }
-        if (!cw_barrier(p, ctl, sc.gen)) return false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (h >= nh) break;
-            float m = wm[h];
-            for (int w = 1; w < kCW; ++w) m = fmaxf(m, wm[w * G + h]);
-            const float mn = fmaxf(M[h], m);
+            const float mn = fmaxf(M[h], slot_max(lmax[h], LP));
             if (mn != M[h]) {
                 const float c = __expf(M[h] - mn);  // 0 while M is -inf
                 l[h] *= c;
@@ -1237,8 +1221,8 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         for (int b = cw; b * PPW < npos; b += kCW) {
             const int t = b * PPW + slot;
             if (t >= npos) continue;
-            float kf[8], vf[8];
-            seg_kv(t, nring, kb, vb, cur, hd, dl, kf, vf);
+            float vf[8];
+            seg_row(t, nring, vb, cur + hd, hd, dl, vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 if (h >= nh) break;
@@ -1249,10 +1233,8 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
         }
         if (k < na) ring_release(ctl, rp);
-        // the scores are rewritten by the next segment
-        if (k + 1 < nseg && !cw_barrier(p, ctl, sc.gen)) return false;
     }
-    // sums over the slots, then over the compute waves in LDS
+    // wave partials {max, sum, -, -, acc[hd]} to LDS; compute wave 0 combines them
     const int stride = hd + 4;
     float *scr = (float *)(lds + p.lds_attn);  // [kCW][G][stride]
 #pragma unroll
@@ -1263,7 +1245,10 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum(acc[h][e], LP);
         if (slot == 0) {
             float *r = scr + ((size_t)cw * G + h) * stride;
-            if (dl == 0) r[1] = l[h];
+            if (dl == 0) {
+                r[0] = M[h];
+                r[1] = l[h];
+            }
             store8(r + 4 + dl * 8, acc[h]);
         }
     }
@@ -1273,14 +1258,18 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (h >= nh) break;
+            // log-sum-exp combination of the wave partials (a wave without positions has max -inf)
+            float mw = -INFINITY;
+            for (int w = 0; w < kCW; ++w) mw = fmaxf(mw, scr[((size_t)w * G + h) * stride]);
             float ll = 0.f, a[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = 0.f;
             for (int w = 0; w < kCW; ++w) {
                 const float *r = scr + ((size_t)w * G + h) * stride;
-                ll += r[1];
+                const float c = r[0] == -INFINITY ? 0.f : __expf(r[0] - mw);
+                ll += r[1] * c;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] += r[4 + dl * 8 + e];
+                for (int e = 0; e < 8; ++e) a[e] = fmaf(r[4 + dl * 8 + e], c, a[e]);
             }
             const int o0 = (j * G + h0 + h) * hd + dl * 8;
             if (p.merge_in_o) {
@@ -1288,7 +1277,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                 const int e0 = ((j * p.max_splits + s) * G + h0 + h) * (hd + 2);
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) put2(p, p.wl.part, e0 + dl * 8 + e, a[e], a[e + 1], tag);
-                if (dl == 0) put2(p, p.wl.part, e0 + hd, M[h], ll, tag);
+                if (dl == 0) put2(p, p.wl.part, e0 + hd, mw, ll, tag);
             } else if (nsplit == 1) {
                 const float inv = 1.f / ll;
 #pragma unroll
@@ -1296,7 +1285,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             } else {
                 // this split's partial: part[j][s][h][stride] = {max, sum, -, -, acc[hd]}
                 const uint64_t pb = p.wl.part + ((uint64_t)(j * p.max_splits + s) * G + h0 + h) * stride * 4u;
-                if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(M[h]), __float_as_uint(ll), 0u, 0u});
+                if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(mw), __float_as_uint(ll), 0u, 0u});
                 stc16(p.ws, (uint32_t)(pb + 16u + 32u * dl), (u32x4){__float_as_uint(a[0]), __float_as_uint(a[1]),
                                                                      __float_as_uint(a[2]), __float_as_uint(a[3])});
                 stc16(p.ws, (uint32_t)(pb + 32u + 32u * dl), (u32x4){__float_as_uint(a[4]), __float_as_uint(a[5]),
@@ -1343,7 +1332,9 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
         }
     }
-    // the scratch is reused by the next item
+    // the scratch is reused by the next item of the interval (a later interval's item comes after
+    // that interval's input barrier)
+    if (T.flags & TASK_LAST) return true;
     return cw_barrier(p, ctl, sc.gen);
 }
 
