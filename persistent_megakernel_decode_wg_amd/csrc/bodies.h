@@ -387,16 +387,22 @@ template <int N> MBK_DEV float group_sum(float v) {
     return v;
 }
 
+// The same for a group size n (a power of two up to 64) known only at run
+// time: every step is computed and kept or dropped by a wave-uniform select,
+// so the code has no branches.
 MBK_DEV float group_sum_n(float v, int n) {
-    switch (n) {
-        case 1: return v;
-        case 2: return group_sum<2>(v);
-        case 4: return group_sum<4>(v);
-        case 8: return group_sum<8>(v);
-        case 16: return group_sum<16>(v);
-        case 32: return group_sum<32>(v);
-        default: return group_sum<64>(v);
-    }
+    float t = dpp<0xB1>(v);
+    v = n >= 2 ? v + t : v;
+    t = dpp<0x4E>(v);
+    v = n >= 4 ? v + t : v;
+    t = dpp<0x141>(v);
+    v = n >= 8 ? v + t : v;
+    t = dpp<0x140>(v);
+    v = n >= 16 ? v + t : v;
+    t = xsum16(v);
+    v = n >= 32 ? t : v;
+    t = xsum32(v);
+    return n >= 64 ? t : v;
 }
 
 // ---- step inputs -----------------------------------------------------------------------------------
@@ -1113,18 +1119,27 @@ MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int 
 // Inside a 16-lane row the slots are combined by rotating the row by 2, 4
 // and 8 lanes (each step doubles the slots covered), then rows by the lane
 // swaps.
+// LP is wave-uniform: each step is computed and kept by a select (no branches).
 MBK_DEV float slot_sum(float v, int LP) {
-    if (LP <= 1) v += dpp<0x121>(v);   // row_ror:1
-    if (LP <= 2) v += dpp<0x122>(v);   // row_ror:2
-    if (LP <= 4) v += dpp<0x124>(v);   // row_ror:4
-    if (LP <= 8) v += dpp<0x128>(v);   // row_ror:8
+    float t = dpp<0x121>(v);   // row_ror:1
+    v = LP <= 1 ? v + t : v;
+    t = dpp<0x122>(v);         // row_ror:2
+    v = LP <= 2 ? v + t : v;
+    t = dpp<0x124>(v);         // row_ror:4
+    v = LP <= 4 ? v + t : v;
+    t = dpp<0x128>(v);         // row_ror:8
+    v = LP <= 8 ? v + t : v;
     return xsum32(xsum16(v));
 }
 MBK_DEV float slot_max(float v, int LP) {
-    if (LP <= 1) v = fmaxf(v, dpp<0x121>(v));
-    if (LP <= 2) v = fmaxf(v, dpp<0x122>(v));
-    if (LP <= 4) v = fmaxf(v, dpp<0x124>(v));
-    if (LP <= 8) v = fmaxf(v, dpp<0x128>(v));
+    float t = dpp<0x121>(v);
+    v = LP <= 1 ? fmaxf(v, t) : v;
+    t = dpp<0x122>(v);
+    v = LP <= 2 ? fmaxf(v, t) : v;
+    t = dpp<0x124>(v);
+    v = LP <= 4 ? fmaxf(v, t) : v;
+    t = dpp<0x128>(v);
+    v = LP <= 8 ? fmaxf(v, t) : v;
     return xmax32(xmax16(v));
 }
 
