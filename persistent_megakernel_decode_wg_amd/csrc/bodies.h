@@ -251,12 +251,11 @@ MBK_DEV bool poll8(const Params &p, uint64_t base, int g, uint32_t tag, float *v
     const uint32_t off = (uint32_t)(base + 64u * (uint32_t)g);
     for (int it = 0;; ++it) {
         const Group8 a = load8(p, off);
-        if (tagged8(a, tag)) {
+        if (tagged8(a, tag) || it >= p.spin_limit || aborted(p, it)) {
             values8(a, v);
-            return true;
+            if (it >= p.spin_limit) set_error(p);
+            return tagged8(a, tag);
         }
-        if (it >= p.spin_limit) { set_error(p); return false; }
-        if (aborted(p, it)) return false;
         reread();
     }
 }
@@ -266,12 +265,11 @@ MBK_DEV bool poll1(const Params &p, uint64_t base, int i, uint32_t tag, float &v
     const uint64_t *e = ws_ptr<uint64_t>(p, base) + i;
     for (int it = 0;; ++it) {
         const uint64_t w = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(w >> 32) == tag) {
+        if ((uint32_t)(w >> 32) == tag || it >= p.spin_limit || aborted(p, it)) {
             v = __uint_as_float((uint32_t)w);
-            return true;
+            if (it >= p.spin_limit) set_error(p);
+            return (uint32_t)(w >> 32) == tag;
         }
-        if (it >= p.spin_limit) { set_error(p); return false; }
-        if (aborted(p, it)) return false;
         reread();
     }
 }
@@ -664,16 +662,24 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
 
 // ---- compute waves: synchronisation ----------------------------------------------------------------
 
-// Barrier among the compute waves (LDS counter).  gen counts this wave's barriers.
-MBK_DEV bool cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
+// Barrier among the compute waves (LDS counter).  gen counts this wave's
+// barriers.  Like every wait of the compute waves it never leaves the code
+// path early: when the workgroup has aborted (a bounded wait expired) it falls
+// through, the step's results are void (the error word reports it) and every
+// wave runs to the end of the step without waiting, so the kernel's loops keep
+// a single exit.
+MBK_DEV void cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
     gen += kCW;
     if ((threadIdx.x & 63) == 0) __atomic_fetch_add((lds_u32 *)&ctl.bar, 1u, __ATOMIC_RELAXED);
     for (int it = 0; (int32_t)(lds_ld(&ctl.bar) - gen) < 0; ++it) {
-        if (lds_ld(&ctl.abort)) return false;
-        if (it >= p.spin_limit) { set_error(p); lds_st(&ctl.abort, 1u); return false; }
+        if (lds_ld(&ctl.abort)) return;
+        if (it >= p.spin_limit) {
+            set_error(p);
+            lds_st(&ctl.abort, 1u);
+            return;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
-    return true;
 }
 
 // Position of the compute waves in the allocation sequence.
@@ -693,8 +699,8 @@ MBK_DEV void read_prog(Ctl &ctl, uint32_t *out) {
     out[3] = __builtin_amdgcn_readfirstlane(v.w);
 }
 
-// Places the next allocation; waits until the loader waves have completed it.
-// Returns its ring offset, or ~0 when the wait failed.
+// Places the next allocation; waits until the loader waves have completed it
+// (falls through once the workgroup has aborted).  Returns its ring offset.
 MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Alloc &A) {
     const uint32_t start = ring_place(rp.cur, A.size, (uint32_t)p.ring_bytes);
 #pragma unroll
@@ -706,8 +712,12 @@ MBK_DEV uint32_t ring_acquire(const Params &p, Ctl &ctl, RingPos &rp, const Allo
         for (int w = 0; w < kLW; ++w) ready = ready && (int32_t)(rp.seen[w] - rp.cum[w]) >= 0;
         if (ready) return start;
         if (it > 0) {
-            if (lds_ld(&ctl.abort)) return ~0u;
-            if (it >= p.spin_limit) { set_error(p); lds_st(&ctl.abort, 1u); return ~0u; }
+            if (lds_ld(&ctl.abort)) return start;
+            if (it >= p.spin_limit) {
+                set_error(p);
+                lds_st(&ctl.abort, 1u);
+                return start;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
         read_prog(ctl, rp.seen);
@@ -752,14 +762,14 @@ MBK_DEV void store8(float *dst, const float *v) {
 // row of `token`) and the bf16 norm weight w; returns this thread's part of
 // sum(v^2).  Threads [tid, nt).
 MBK_DEV float norm_input(const Params &p, float *xs, bool from_embed, int token, uint32_t tag, uint64_t norm_off,
-                         int K, int tid, int nt, bool &ok) {
+                         int K, int tid, int nt) {
     float ss = 0.f;
     for (int g = tid; g < K / 8; g += nt) {
         float v[8], w[8];
         // the norm weights (and the embedding row) are requested before the poll, so they arrive with it
         const u32x4 wn = *(const u32x4 *)(p.blob + norm_off + 16u * g);
         if (from_embed) unpack8(*(const u32x4 *)(p.blob + row_group_offset(p.embed, token, g)), v);
-        else if (!poll8(p, p.wl.x, g, tag, v)) { ok = false; return 0.f; }
+        else poll8(p, p.wl.x, g, tag, v);
         unpack8(wn, w);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -772,10 +782,10 @@ MBK_DEV float norm_input(const Params &p, float *xs, bool from_embed, int token,
 }
 
 // xs <- hi/lo pairs of the tagged vector at base (threads [tid, nt)).
-MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag, int K, int tid, int nt, bool &ok) {
+MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag, int K, int tid, int nt) {
     for (int g = tid; g < K / 8; g += nt) {
         float v[8];
-        if (!poll8(p, base, g, tag, v)) { ok = false; return; }
+        poll8(p, base, g, tag, v);
         split8_store(xs + 8 * g, v);
     }
 }
@@ -784,7 +794,7 @@ MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag
 // (log-sum-exp merge in split order): thread u takes query head u / (hd/8),
 // dims 8 * (u % (hd/8)) .. + 8.  Threads [tid, nt).
 template <int G>
-MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, int tid, int nt, bool &ok) {
+MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, int tid, int nt) {
     const int hd = p.hd, gsh = p.hd_shift - 3, gpr = 1 << gsh;
     constexpr int kPer = kPollMax / 5;  // splits per polling round: {max, sum} chunk + 4 chunks of acc
     for (int u = tid; u < p.nq * gpr; u += nt) {
@@ -807,7 +817,7 @@ MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, i
                     need[5 * q + 1 + c] = 3u;
                 }
             }
-            if (!poll_round(p, off, need, 5 * ns, tag, tag, v)) { ok = false; return; }
+            poll_round(p, off, need, 5 * ns, tag, tag, v);
             for (int q = 0; q < ns; ++q) {
                 const float m2 = __uint_as_float(v[5 * q].x), l2 = __uint_as_float(v[5 * q].z);
                 float w[8];
@@ -978,7 +988,7 @@ MBK_DEV void gemv_tile_op(const Params &p, const Interval &iv, const uint8_t *ld
 // Greedy argmax: the compute waves' keys meet in LDS, one 64-bit atomic max
 // per workgroup; the last participant to arrive publishes the index and
 // clears the key and the count for the next step.
-MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepCtx &sc) {
+MBK_DEV void argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepCtx &sc) {
     uint64_t best = sc.best;
     for (int m = 1; m < 64; m <<= 1) {
         const uint64_t o = ((uint64_t)__shfl_xor((uint32_t)(best >> 32), m) << 32) | __shfl_xor((uint32_t)best, m);
@@ -986,7 +996,7 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
     }
     const int cw = wave_id();
     if ((threadIdx.x & 63) == 0) ctl.best[cw] = best;
-    if (!cw_barrier(p, ctl, sc.gen)) return false;
+    cw_barrier(p, ctl, sc.gen);
     if (threadIdx.x == 0) {
         for (int i = 0; i < kCW; ++i) best = ctl.best[i] > best ? ctl.best[i] : best;
         uint64_t *key = ws_ptr<uint64_t>(p, p.wl.argkey);
@@ -1003,7 +1013,6 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
         }
     }
     sc.best = 0;
-    return true;
 }
 
 // ---- interval inputs (compute waves, threads [0, kCW * 64)) ------------------------------------------
@@ -1011,8 +1020,7 @@ MBK_DEV bool argmax_publish(const Params &p, const Interval &iv, Ctl &ctl, StepC
 // Returns this thread's part of the RMSNorm sum of squares (0 if none).  T is
 // the workgroup's first task of the interval.
 template <int G>
-MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, int ivi, uint8_t *lds, StepCtx &sc,
-                          bool &ok) {
+MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, int ivi, uint8_t *lds, StepCtx &sc) {
     const int tid = threadIdx.x, nt = kCW * 64;
     float *xs = (float *)(lds + p.lds_xs + sc.in);
     const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(p, sc.seq, iv.x_src);
@@ -1029,18 +1037,17 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
                 if (iv.x_src < 0) {
                     const uint16_t *e = (const uint16_t *)(p.blob + row_group_offset(p.embed, sc.token, r >> 3));
                     xres[r - r0] = bf16f(e[r & 7]);
-                } else if (!poll1(p, p.wl.x, r, xtag, xres[r - r0])) {
-                    ok = false;
-                    return 0.f;
+                } else {
+                    poll1(p, p.wl.x, r, xtag, xres[r - r0]);
                 }
             }
-            if (iv.op == OP_O && p.merge_in_o) merge_input<G>(p, xs, tag_of(p, sc.seq, ivi - 1), sc.ss.nsplit, tid, nt, ok);
-            else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt, ok);
-            else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt, ok);
+            if (iv.op == OP_O && p.merge_in_o) merge_input<G>(p, xs, tag_of(p, sc.seq, ivi - 1), sc.ss.nsplit, tid, nt);
+            else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt);
+            else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt);
             return 0.f;
         }
         case OP_QKV: {
-            if (iv.bias_off == ~(uint64_t)0) return norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt, ok);
+            if (iv.bias_off == ~(uint64_t)0) return norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt);
             // Q/K/V bias to LDS (fp32), 8 values per 16-byte load; the first load of each thread is
             // in flight while the residual stream is polled
             const int nb8 = (p.nq + 2 * p.nkv) * p.hd / 8;
@@ -1048,7 +1055,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
             float *bias = (float *)(lds + p.lds_bias + sc.in);
             u32x4 first = {0u, 0u, 0u, 0u};
             if (tid < nb8) first = bsrc[tid];
-            const float ss = norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt, ok);
+            const float ss = norm_input(p, xs, iv.x_src < 0, sc.token, xtag, iv.norm_off, p.H, tid, nt);
             for (int i = tid; i < nb8; i += nt) {
                 float v[8];
                 unpack8(i == tid ? first : bsrc[i], v);
@@ -1057,7 +1064,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
             return ss;
         }
         default:  // gate/up and LM head: RMS-normalised residual stream
-            return norm_input(p, xs, false, 0, xtag, iv.norm_off, p.H, tid, nt, ok);
+            return norm_input(p, xs, false, 0, xtag, iv.norm_off, p.H, tid, nt);
     }
 }
 
@@ -1065,7 +1072,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
 // key and value appended this step, rounded to bf16 exactly as the cache
 // holds them.  LDS at lds_qkv: [G][hd] queries, [hd] key, [hd] value.
 template <int G>
-MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, const StepCtx &sc, bool &ok) {
+MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, const StepCtx &sc) {
     const int tid = threadIdx.x, nt = kCW * 64;
     const AttnItem it = attn_item(T);
     const int hd = p.hd, kg = hd >> 3, qg = it.nh * kg;
@@ -1075,14 +1082,14 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
         float v[8];
         if (g < qg) {
             // queries of heads h0 .. h0 + nh - 1 of group j, at [0, nh)
-            if (!poll8(p, p.wl.q, (it.j * G + it.h0) * kg + g, tag, v)) { ok = false; return; }
+            poll8(p, p.wl.q, (it.j * G + it.h0) * kg + g, tag, v);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] *= p.scale;
             store8(dst + 8 * g, v);
         } else {
             const bool key = g < qg + kg;
             const int gg = g - qg - (key ? 0 : kg);
-            if (!poll8(p, key ? p.wl.k : p.wl.v, it.j * kg + gg, tag, v)) { ok = false; return; }
+            poll8(p, key ? p.wl.k : p.wl.v, it.j * kg + gg, tag, v);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = bf16f(to_bf16(v[e]));
             store8(dst + G * hd + (key ? 0 : hd) + 8 * gg, v);
@@ -1148,15 +1155,15 @@ MBK_DEV void put2(const Params &p, uint64_t base, int i, float a, float b, uint3
     stc16(p.ws, (uint32_t)(base + 8u * (uint32_t)i), (u32x4){__float_as_uint(a), tag, __float_as_uint(b), tag});
 }
 
-// One attention item.  False when a wait failed.
+// One attention item.
 template <int G>
-MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const Task &T, uint8_t *lds, Ctl &ctl,
+MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const Task &T, uint8_t *lds, Ctl &ctl,
                             RingPos &rp, StepCtx &sc) {
     const int pos = sc.pos, hd = p.hd, lsh = p.hd_shift - 3, LP = 1 << lsh, PPW = 64 >> lsh;
     const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane & (LP - 1), slot = lane >> lsh;
     const AttnItem item = attn_item(T);
     const int j = item.j, s = item.s, h0 = item.h0, nh = item.nh;
-    if (s >= sc.ss.nsplit) return true;  // no allocations either
+    if (s >= sc.ss.nsplit) return;  // no allocations either
     const Range sp = split_range(sc.ss, s);
     const int nsplit = sc.ss.nsplit;
     const float *qkv = (const float *)(lds + p.lds_qkv + sc.in);
@@ -1189,7 +1196,6 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
         if (k < na) {
             const Alloc A = task_alloc(p, iv, T, sc.ss, k);
             const uint32_t start = ring_acquire(p, ctl, rp, A);
-            if (start == ~0u) return false;
             kb = ring + start;
             vb = kb + A.r1;
             nring = (int)(A.b0 >> (p.hd_shift + 1));
@@ -1267,7 +1273,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
             store8(r + 4 + dl * 8, acc[h]);
         }
     }
-    if (!cw_barrier(p, ctl, sc.gen)) return false;
+    cw_barrier(p, ctl, sc.gen);
     const uint32_t tag = tag_of(p, sc.seq, ivi);
     if (cw == 0 && slot == 0) {
 #pragma unroll
@@ -1320,16 +1326,16 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
                 stc_u(cnt, 0u);
                 __builtin_amdgcn_s_waitcnt(0);  // the reset lands before this group's output does
             }
-            ctl.last_s = last;
+            lds_st((uint32_t *)&ctl.last_s, last ? 1u : 0u);
         }
-        if (!cw_barrier(p, ctl, sc.gen)) return false;
+        cw_barrier(p, ctl, sc.gen);
         if (lds_ld((const uint32_t *)&ctl.last_s)) {
             // every partial of head group j into LDS (scratch holds max_splits * G * stride floats)
             const uint64_t gbase = p.wl.part + ((uint64_t)(j * p.max_splits) * G) * stride * 4u;
             const int n16 = nsplit * G * stride / 4;
             for (int idx = threadIdx.x; idx < n16; idx += kCW * 64)
                 *(u32x4 *)(scr + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
-            if (!cw_barrier(p, ctl, sc.gen)) return false;
+            cw_barrier(p, ctl, sc.gen);
             for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
                 const int h = idx >> p.hd_shift, e = idx & (hd - 1);
                 float mm = -INFINITY, ll = 0.f, a0 = 0.f, a1 = 0.f;
@@ -1349,8 +1355,7 @@ MBK_DEV bool attention_task(const Params &p, const Interval &iv, int ivi, const 
     }
     // the scratch is reused by the next item of the interval (a later interval's item comes after
     // that interval's input barrier)
-    if (T.flags & TASK_LAST) return true;
-    return cw_barrier(p, ctl, sc.gen);
+    if (!(T.flags & TASK_LAST)) cw_barrier(p, ctl, sc.gen);
 }
 
 // ---- compute waves: the interval loop -----------------------------------------------------------------
@@ -1376,8 +1381,48 @@ MBK_DEV Task task_at(const Params &p, const uint8_t *lds, int k) {
     return t;
 }
 
+// The inputs of interval ivi (first task T) into the input block not read by
+// the previous interval (with a single block, after the other compute waves
+// are done with it), then the RMSNorm statistic.
+template <int G>
+MBK_DEV void interval_inputs(const Params &p, const Interval &iv, const Task &T, int ivi, uint8_t *lds, Ctl &ctl,
+                             StepCtx &sc) {
+    const int par = (int)(sc.nin & 1u);
+    ++sc.nin;
+    if (p.in_double) sc.in = par * p.in_bytes;
+    else cw_barrier(p, ctl, sc.gen);
+    float ss = 0.f;
+    if (iv.op == OP_ATTN) attn_inputs<G>(p, T, ivi, lds, sc);
+    else ss = gemv_inputs<G>(p, iv, T, ivi, lds, sc);
+    ss = group_sum<64>(ss);
+    if ((threadIdx.x & 63) == 0) ctl.ss[par][wave_id()] = ss;
+    cw_barrier(p, ctl, sc.gen);
+    stamp(p, lds, ivi, 1);
+    sc.rnorm = 1.f;
+    if (iv.op == OP_QKV || iv.op == OP_GATEUP || iv.op == OP_LMHEAD) {
+        static_assert(kCW == 4, "one 16-byte read of the partial sums");
+        const u32x4 s4 = lds_ld16(ctl.ss[par]);
+        const float tot = (__uint_as_float(s4.x) + __uint_as_float(s4.y)) +
+                          (__uint_as_float(s4.z) + __uint_as_float(s4.w));
+        sc.rnorm = rsqrtf(tot * p.inv_h + p.eps);
+    }
+}
+
+// Barrier mode: the workgroup's compute waves meet, then one thread takes
+// part in the grid barrier that closes interval ivi.
+MBK_DEV void interval_barrier(const Params &p, uint8_t *lds, Ctl &ctl, StepCtx &sc, int ivi) {
+    // every compute store of this interval is complete before arrival
+    __builtin_amdgcn_s_waitcnt(0);
+    cw_barrier(p, ctl, sc.gen);
+    if (threadIdx.x == 0 && !grid_barrier_thread(p, p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u))
+        lds_st(&ctl.abort, 1u);
+    cw_barrier(p, ctl, sc.gen);
+    stamp(p, lds, ivi, 3);
+}
+
 // Compute waves: every interval of [first_iv, last_iv) in order; tasks [0, nt)
-// of this workgroup in LDS.  False when a wait failed (the workgroup leaves).
+// of this workgroup in LDS.  The loops have no early exit (see cw_barrier);
+// false only when the debug switch made this workgroup leave.
 template <int G>
 MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &sc) {
     RingPos rp;
@@ -1389,75 +1434,38 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
     for (int ivi = p0.first_iv; ivi < p0.last_iv; ++ivi) {
         const Params &p = params_opaque();
         if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return false;
-        Task T;
-        T.iv = -1;
-        if (k < nt) T = task_at(p, lds, k);
-        if (T.iv == ivi) {
+        const int tiv = k < nt ? task_at(p, lds, k).iv : -1;
+        if (tiv == ivi) {
             const Interval iv = interval_at(p, lds, ivi);
             stamp(p, lds, ivi, 0);
-            // inputs go to the input block not read by the previous interval; with a single block the
-            // other compute waves must first be done with it
-            const int par = (int)(sc.nin & 1u);
-            ++sc.nin;
-            if (p.in_double) sc.in = par * p.in_bytes;
-            else if (!cw_barrier(p, ctl, sc.gen)) return false;
-            bool ok = true;
-            float ss = 0.f;
-            if (iv.op == OP_ATTN) attn_inputs<G>(p, T, ivi, lds, sc, ok);
-            else ss = gemv_inputs<G>(p, iv, T, ivi, lds, sc, ok);
-            ss = group_sum<64>(ss);
-            if ((threadIdx.x & 63) == 0) ctl.ss[par][cw] = ss;
-            if (any_lane(!ok)) { lds_st(&ctl.abort, 1u); return false; }
-            if (!cw_barrier(p, ctl, sc.gen)) return false;
-            stamp(p, lds, ivi, 1);
-            sc.rnorm = 1.f;
-            if (iv.op == OP_QKV || iv.op == OP_GATEUP || iv.op == OP_LMHEAD) {
-                static_assert(kCW == 4, "one 16-byte read of the partial sums");
-                const u32x4 s4 = lds_ld16(ctl.ss[par]);
-                const float tot = (__uint_as_float(s4.x) + __uint_as_float(s4.y)) +
-                                  (__uint_as_float(s4.z) + __uint_as_float(s4.w));
-                sc.rnorm = rsqrtf(tot * p.inv_h + p.eps);
-            }
             const uint32_t tag = tag_of(p, sc.seq, ivi);
-            for (;;) {
-                if (iv.op == OP_ATTN) {
-                    if (!attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc)) return false;
-                } else {
+            if (iv.op == OP_ATTN) {
+                // items of the interval, each with its own inputs (an item that is not the interval's
+                // last ends with a compute-wave barrier)
+                for (;;) {
+                    const Task T = task_at(p, lds, k);
+                    interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
+                    attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc);
+                    ++k;
+                    if (T.flags & TASK_LAST) break;
+                }
+            } else {
+                interval_inputs<G>(p, iv, task_at(p, lds, k), ivi, lds, ctl, sc);
+                const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
+                for (;;) {
+                    const Task T = task_at(p, lds, k);
                     const Alloc A = task_alloc(p, iv, T, sc.ss, 0);
-                    const uint32_t start = ring_acquire(p, ctl, rp, A);
-                    if (start == ~0u) return false;
-                    const uint8_t *wt = lds + p.lds_ring + start;
-                    const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
+                    const uint8_t *wt = lds + p.lds_ring + ring_acquire(p, ctl, rp, A);
                     for (int t = cw; t < T.n; t += kCW) gemv_tile_op(p, iv, lds, wt + (size_t)t * tile_bytes, T.a + t, sc, tag);
                     ring_release(ctl, rp);
+                    ++k;
+                    if (T.flags & TASK_LAST) break;
                 }
-                if (T.flags & TASK_LAST) {
-                    if (iv.op == OP_LMHEAD && !argmax_publish(p, iv, ctl, sc)) return false;
-                    break;
-                }
-                if (++k >= nt) break;
-                T = task_at(p, lds, k);
-                if (iv.op == OP_ATTN) {
-                    // a further item of the same interval: its own inputs
-                    if (!cw_barrier(p, ctl, sc.gen)) return false;
-                    attn_inputs<G>(p, T, ivi, lds, sc, ok);
-                    if (any_lane(!ok)) { lds_st(&ctl.abort, 1u); return false; }
-                    if (!cw_barrier(p, ctl, sc.gen)) return false;
-                }
+                if (iv.op == OP_LMHEAD) argmax_publish(p, iv, ctl, sc);
             }
-            ++k;
             stamp(p, lds, ivi, 2);
         }
-        if (p.barrier && ivi + 1 < p.last_iv) {
-            // every compute store of this interval is complete before arrival
-            __builtin_amdgcn_s_waitcnt(0);
-            if (!cw_barrier(p, ctl, sc.gen)) return false;
-            __shared__ int bar_ok;
-            if (threadIdx.x == 0) bar_ok = grid_barrier_thread(p, p.epoch_base + (uint32_t)(ivi - p.first_iv) + 1u);
-            if (!cw_barrier(p, ctl, sc.gen)) return false;
-            if (!bar_ok) return false;
-            stamp(p, lds, ivi, 3);
-        }
+        if (p.barrier && ivi + 1 < p.last_iv) interval_barrier(p, lds, ctl, sc, ivi);
     }
     return true;
 }
