@@ -1033,7 +1033,9 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
             sc.blk0 = b0;
             float *xres = (float *)(lds + p.lds_xres + sc.in);
             const int r0 = b0 * g.RT, r1 = min(b1 * g.RT, g.rows);
-            for (int r = r0 + tid; r < r1; r += nt) {
+            // the last threads take the rows: the input vector's groups go to the first ones, so
+            // both reads are in flight together
+            for (int r = r0 + (nt - 1 - tid); r < r1; r += nt) {
                 if (iv.x_src < 0) {
                     const uint16_t *e = (const uint16_t *)(p.blob + row_group_offset(p.embed, sc.token, r >> 3));
                     xres[r - r0] = bf16f(e[r & 7]);
@@ -1275,42 +1277,36 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
     }
     cw_barrier(p, ctl, sc.gen);
     const uint32_t tag = tag_of(p, sc.seq, ivi);
-    if (cw == 0 && slot == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (h >= nh) break;
-            // log-sum-exp combination of the wave partials (a wave without positions has max -inf)
+    if (cw == 0) {
+        // log-sum-exp combination of the wave partials, one head dimension per lane (a wave without
+        // positions has max -inf)
+        for (int u = lane; u < nh * hd; u += 64) {
+            const int h = u >> p.hd_shift, d = u & (hd - 1);
             float mw = -INFINITY;
             for (int w = 0; w < kCW; ++w) mw = fmaxf(mw, scr[((size_t)w * G + h) * stride]);
-            float ll = 0.f, a[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = 0.f;
+            float ll = 0.f, a = 0.f;
             for (int w = 0; w < kCW; ++w) {
                 const float *r = scr + ((size_t)w * G + h) * stride;
                 const float c = r[0] == -INFINITY ? 0.f : __expf(r[0] - mw);
-                ll += r[1] * c;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = fmaf(r[4 + dl * 8 + e], c, a[e]);
+                ll = fmaf(r[1], c, ll);
+                a = fmaf(r[4 + d], c, a);
             }
-            const int o0 = (j * G + h0 + h) * hd + dl * 8;
             if (p.merge_in_o) {
                 // tagged partial: entries [acc[hd] | max, sum] of (j, s, h)
                 const int e0 = ((j * p.max_splits + s) * G + h0 + h) * (hd + 2);
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) put2(p, p.wl.part, e0 + dl * 8 + e, a[e], a[e + 1], tag);
-                if (dl == 0) put2(p, p.wl.part, e0 + hd, mw, ll, tag);
+                put(p, p.wl.part, e0 + d, a, tag);
+                if (d == 0) put2(p, p.wl.part, e0 + hd, mw, ll, tag);
             } else if (nsplit == 1) {
-                const float inv = 1.f / ll;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) put2(p, p.wl.o, o0 + e, a[e] * inv, a[e + 1] * inv, tag);
+                put(p, p.wl.o, (j * G + h0 + h) * hd + d, a / ll, tag);
             } else {
                 // this split's partial: part[j][s][h][stride] = {max, sum, -, -, acc[hd]}
                 const uint64_t pb = p.wl.part + ((uint64_t)(j * p.max_splits + s) * G + h0 + h) * stride * 4u;
-                if (dl == 0) stc16(p.ws, (uint32_t)pb, (u32x4){__float_as_uint(mw), __float_as_uint(ll), 0u, 0u});
-                stc16(p.ws, (uint32_t)(pb + 16u + 32u * dl), (u32x4){__float_as_uint(a[0]), __float_as_uint(a[1]),
-                                                                     __float_as_uint(a[2]), __float_as_uint(a[3])});
-                stc16(p.ws, (uint32_t)(pb + 32u + 32u * dl), (u32x4){__float_as_uint(a[4]), __float_as_uint(a[5]),
-                                                                     __float_as_uint(a[6]), __float_as_uint(a[7])});
+                uint32_t *pw = ws_ptr<uint32_t>(p, pb);
+                stc_u(pw + 4 + d, __float_as_uint(a));
+                if (d == 0) {
+                    stc_u(pw, __float_as_uint(mw));
+                    stc_u(pw + 1, __float_as_uint(ll));
+                }
             }
         }
     }
