@@ -1440,8 +1440,11 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                 // last ends with a compute-wave barrier)
                 for (;;) {
                     const Task T = task_at(p, lds, k);
-                    interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
-                    attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc);
+                    // splits beyond this step's split count have nothing to do (nor anything to load)
+                    if (attn_item(T).s < sc.ss.nsplit) {
+                        interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
+                        attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc);
+                    }
                     ++k;
                     if (T.flags & TASK_LAST) break;
                 }
