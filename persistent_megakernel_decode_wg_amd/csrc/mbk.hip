@@ -327,14 +327,14 @@ std::string build_plan(mbk_model *m) {
         if (P.in_double) fixed += in_block;
     }
 
-    // tile runs of at most a third of the ring: first size the ring assuming a task
+    // tile runs of at most half the ring: first size the ring assuming a task
     // list of 64 entries per workgroup, then build the lists and shrink the ring
     // to what the lists leave.
     size_t max_tile = 0;
     for (const Interval &v : P.iv)
         if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.IT * kChunk);
     auto build_tasks = [&](size_t ring) {
-        const size_t max_alloc = ring / 3;
+        const size_t max_alloc = ring / 2;
         P.task_list.clear();
         P.task_index.assign((size_t)n_wg * (n_iv + 1), 0);
         int max_tasks = 0;
