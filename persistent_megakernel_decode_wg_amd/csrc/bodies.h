@@ -1443,6 +1443,7 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                     const Task T = task_at(p, lds, k);
                     // splits beyond this step's split count have nothing to do (nor anything to load)
                     if (attn_item(T).s < sc.ss.nsplit) {
+                        read_prog(ctl, rp.seen);
                         interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
                         attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc);
                     }
@@ -1450,16 +1451,21 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                     if (T.flags & TASK_LAST) break;
                 }
             } else {
-                interval_inputs<G>(p, iv, task_at(p, lds, k), ivi, lds, ctl, sc);
+                Task T = task_at(p, lds, k);
+                // the loader's progress is read while the inputs are polled: the weights of the first
+                // task are usually complete by then
+                read_prog(ctl, rp.seen);
+                interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
                 const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
                 for (;;) {
-                    const Task T = task_at(p, lds, k);
+                    if (T.iv != ivi) T = task_at(p, lds, k);  // further runs of the interval
                     const Alloc A = task_alloc(p, iv, T, sc.ss, 0);
                     const uint8_t *wt = lds + p.lds_ring + ring_acquire(p, ctl, rp, A);
                     for (int t = cw; t < T.n; t += kCW) gemv_tile_op(p, iv, lds, wt + (size_t)t * tile_bytes, T.a + t, sc, tag);
                     ring_release(ctl, rp);
                     ++k;
                     if (T.flags & TASK_LAST) break;
+                    T.iv = -1;
                 }
                 if (iv.op == OP_LMHEAD) argmax_publish(p, iv, ctl, sc);
             }
