@@ -809,19 +809,26 @@ MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, i
             u32x4 v[kPollMax];
 #pragma unroll
             for (int i = 0; i < kPollMax; ++i) { off[i] = 0; need[i] = 0; }
-            for (int q = 0; q < ns; ++q) {
+            // fixed trip counts, so the arrays stay in registers
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                if (q >= ns) break;
                 const uint32_t e0 = (uint32_t)(((j * p.max_splits + s0 + q) * G + hh) * (hd + 2));
                 off[5 * q] = (uint32_t)p.wl.part + 8u * (e0 + (uint32_t)hd);
                 need[5 * q] = 3u;
+#pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     off[5 * q + 1 + c] = (uint32_t)p.wl.part + 8u * (e0 + 8u * (uint32_t)g) + 16u * c;
                     need[5 * q + 1 + c] = 3u;
                 }
             }
             poll_round(p, off, need, 5 * ns, tag, tag, v);
-            for (int q = 0; q < ns; ++q) {
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                if (q >= ns) break;
                 const float m2 = __uint_as_float(v[5 * q].x), l2 = __uint_as_float(v[5 * q].z);
                 float w[8];
+#pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     w[2 * c] = __uint_as_float(v[5 * q + 1 + c].x);
                     w[2 * c + 1] = __uint_as_float(v[5 * q + 1 + c].z);
