@@ -322,8 +322,16 @@ std::string build_plan(mbk_model *m) {
     const size_t in_block = a16((size_t)(G + 2) * hd * 4) + (c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0) +
                             a16((size_t)kmax * 4) + a16((size_t)max_rows * 4);
     {
+        // the second copy costs ring space; that matters most where the ring would otherwise hold most
+        // of a layer's weights per workgroup (then the loader runs ahead across whole intervals).
+        // fixed holds one copy already: left is what a second copy leaves.
         const size_t left = kLdsMax - kLdsStatic - task_slot - fixed - in_block;
-        P.in_double = left > (size_t)64 * 16 + 64 * 1024 ? 1 : 0;
+        const LayerPlan &L0 = P.layers[0];
+        const uint64_t layer_bytes = ((uint64_t)L0.qkv.ntiles * L0.qkv.IT + (uint64_t)L0.o.ntiles * L0.o.IT +
+                                      (uint64_t)L0.gu.ntiles * L0.gu.IT + (uint64_t)L0.down.ntiles * L0.down.IT) *
+                                     kChunk / (uint64_t)n_wg;
+        const bool ring_holds_layer = (uint64_t)(left + in_block) * 4 >= layer_bytes * 3;  // with one copy
+        P.in_double = left > (size_t)64 * 16 + 64 * 1024 && (in_block <= 16 * 1024 || !ring_holds_layer) ? 1 : 0;
         if (P.in_double) fixed += in_block;
     }
 
