@@ -151,7 +151,9 @@ int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
 /* Attention split policy: each split of the cached context covers at least
  * min_positions positions (default 128); contexts up to that length run
  * unsplit.  Short caches whose keys and values of one head fit in 64 KiB get one
- * work item per query head, longer ones one per KV head (all its query heads). */
+ * work item per query head, longer ones one per KV head (all its query heads).
+ * The number of splits is bounded by the plan (at most one per 32 cached
+ * positions and per workgroup of a KV head's share of the device). */
 int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
 
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */

@@ -219,6 +219,7 @@ constexpr size_t kLdsMax = 160 * 1024;
 constexpr size_t kLdsStatic = 512;      // Ctl and the other static LDS words of the kernels
 constexpr int kMinRing = 16 * 1024;
 constexpr int kPiecePos = 128;          // most cached positions per attention piece
+constexpr int kMinSplitPos = 32;        // fewest positions per attention split the plan provides for
 
 size_t a16(size_t v) { return (v + 15) / 16 * 16; }
 
@@ -264,6 +265,8 @@ std::string build_plan(mbk_model *m) {
     const int item_heads = P.attn_hpi == 1 ? c.n_heads : c.n_kv_heads;
     int ms = std::max(1, n_wg / item_heads);
     ms = std::min<int>(ms, (int)(merge_budget / ((size_t)G * stride * 4)));
+    // splits shorter than kMinSplitPos positions are never useful: a short cache needs few
+    ms = std::min(ms, (c.kv_capacity + kMinSplitPos - 1) / kMinSplitPos);
     ms = std::max(1, std::min(ms, 64));
     P.max_splits = ms;
 
