@@ -672,14 +672,17 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
 MBK_DEV void cw_barrier(const Params &p, Ctl &ctl, uint32_t &gen) {
     gen += kCW;
     if ((threadIdx.x & 63) == 0) __atomic_fetch_add((lds_u32 *)&ctl.bar, 1u, __ATOMIC_RELAXED);
+    // the first rounds spin without a pause; the abort word is looked at every 32 rounds
     for (int it = 0; (int32_t)(lds_ld(&ctl.bar) - gen) < 0; ++it) {
-        if (lds_ld(&ctl.abort)) return;
-        if (it >= p.spin_limit) {
-            set_error(p);
-            lds_st(&ctl.abort, 1u);
-            return;
+        if ((it & 31) == 31) {
+            if (lds_ld(&ctl.abort)) return;
+            if (it >= p.spin_limit) {
+                set_error(p);
+                lds_st(&ctl.abort, 1u);
+                return;
+            }
         }
-        __builtin_amdgcn_s_sleep(1);
+        if (it >= 64) __builtin_amdgcn_s_sleep(1);
     }
 }
 
