@@ -1035,6 +1035,11 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
     const int tid = threadIdx.x, nt = kCW * 64;
     float *xs = (float *)(lds + p.lds_xs + sc.in);
     const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(p, sc.seq, iv.x_src);
+    // groups past the input (padding of widened tiles) are zero
+    for (int g = iv.mat.K / 8 + tid; g < iv.mat.IT * iv.mat.L; g += nt) {
+        *(u32x4 *)(xs + 8 * g) = (u32x4){0u, 0u, 0u, 0u};
+        *(u32x4 *)(xs + 8 * g + 4) = (u32x4){0u, 0u, 0u, 0u};
+    }
     switch (iv.op) {
         case OP_O:
         case OP_DOWN: {

@@ -28,8 +28,9 @@ enum MatKind : int32_t { MAT_PLAIN = 0, MAT_QKV = 1, MAT_GATEUP = 2 };
 // rows; each row's K inputs are split in 8-element groups (16 bytes) spread
 // over L = 64 / RT lanes.  Chunk (tile t, step it, lane l) holds the 8 values
 //   packed row  t*RT + l / L,   input group  kg = (l % L) + it * L
-// and sits at byte  off + ((t * IT + it) * 64 + l) * 16,  IT = (K / 8) / L.
-// So every wave-wide 16-byte load of one step reads 1 KiB of contiguous memory.
+// and sits at byte  off + ((t * IT + it) * 64 + l) * 16,  IT * L >= K / 8
+// (groups from K / 8 on are zero padding).  So every wave-wide 16-byte load
+// of one step reads 1 KiB of contiguous memory.
 struct MatGeom {
     uint64_t off;    // byte offset in the packed blob
     int32_t rows;    // packed rows = ntiles * RT (rows >= logical rows)
@@ -54,7 +55,8 @@ MBK_HD uint64_t row_group_offset(const MatGeom &g, int64_t r, int kg) {
 
 // Geometry rule: L is the largest power of two <= 64 dividing K/8; operators
 // whose epilogue combines two adjacent packed rows (RoPE pairs, gate/up
-// pairs) need RT >= 2, so their L is capped at 32.
+// pairs) need RT >= 2, so their L is capped at 32.  The planner may widen L
+// for operators with few tiles (see make_geom).
 MBK_HD void choose_lanes(int K, bool pairs, int *L, int *RT) {
     int kg = K / 8, l = 1;
     while (l < 64 && kg % (l * 2) == 0) l *= 2;

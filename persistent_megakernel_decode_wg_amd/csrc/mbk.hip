@@ -68,8 +68,8 @@ __global__ void k_pack(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16
         const int64_t t = (int64_t)(rest / (uint64_t)g.IT);
         const int64_t prow = t * g.RT + lane / g.L;
         const int kg = (lane % g.L) + it * g.L;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (prow < g.rows) {
+        u32x4 v = {0u, 0u, 0u, 0u};  // rows past the matrix and padding groups are zero
+        if (prow < g.rows && kg < g.K / 8) {
             RowSrc s = packed_row_source(g.kind, (int)prow, hd, nq_rows, nkv_rows);
             const uint16_t *src = s.which == 0 ? s0 : (s.which == 1 ? s1 : s2);
             v = *(const u32x4 *)(src + (uint64_t)s.row * g.K + (uint64_t)kg * 8u);
@@ -152,11 +152,27 @@ struct mbk_model {
 
 namespace {
 
-MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind) {
+// An operator with fewer tiles than workgroups leaves workgroups idle while
+// each tile is one wave's chain of IT dependent steps.  Such an operator, if
+// its rows need no pairing, takes one row per tile (L = 64: the fewest steps,
+// up to 4 tiles per workgroup, one per compute wave) over inputs padded with
+// zero groups to a multiple of 64, when the padding stays within 15 % of the
+// bytes.  (Measured on MI355X: one-row tiles help where they turn idle
+// workgroups into busy waves, e.g. the Qwen2-0.5B output projection; tiles of
+// 2-4 rows over more workgroups do not.)
+MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind, int n_wg) {
     MatGeom g{};
     choose_lanes(K, pairs, &g.L, &g.RT);
+    const int kg = K / 8;
+    int kgp = kg;
+    const int kg64 = (kg + 63) / 64 * 64;
+    if (!pairs && g.L < 64 && (rows + g.RT - 1) / g.RT < n_wg && (int64_t)kg64 * 100 <= (int64_t)kg * 115) {
+        g.L = 64;
+        g.RT = 1;
+        kgp = kg64;
+    }
     g.K = K;
-    g.IT = (K / 8) / g.L;
+    g.IT = kgp / g.L;
     g.rows = rows;
     g.ntiles = (rows + g.RT - 1) / g.RT;
     g.kind = kind;
@@ -235,10 +251,10 @@ std::string build_plan(mbk_model *m) {
     P.layers.resize(c.n_layers);
     for (int l = 0; l < c.n_layers; ++l) {
         LayerPlan &L = P.layers[l];
-        L.qkv = make_geom(cur, Q + 2 * KV, c.hidden, true, MAT_QKV);
-        L.o = make_geom(cur, c.hidden, Q, false, MAT_PLAIN);
-        L.gu = make_geom(cur, 2 * c.intermediate, c.hidden, true, MAT_GATEUP);
-        L.down = make_geom(cur, c.hidden, c.intermediate, false, MAT_PLAIN);
+        L.qkv = make_geom(cur, Q + 2 * KV, c.hidden, true, MAT_QKV, n_wg);
+        L.o = make_geom(cur, c.hidden, Q, false, MAT_PLAIN, n_wg);
+        L.gu = make_geom(cur, 2 * c.intermediate, c.hidden, true, MAT_GATEUP, n_wg);
+        L.down = make_geom(cur, c.hidden, c.intermediate, false, MAT_PLAIN, n_wg);
         L.attn_norm = cur;
         cur = align256(cur + 2u * c.hidden);
         L.mlp_norm = cur;
@@ -249,7 +265,7 @@ std::string build_plan(mbk_model *m) {
             cur = align256(cur + 2u * (Q + 2 * KV));
         }
     }
-    P.embed = make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN);
+    P.embed = make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN, n_wg);
     P.final_norm = cur;
     cur = align256(cur + 2u * c.hidden);
     P.rope = cur;
@@ -305,7 +321,9 @@ std::string build_plan(mbk_model *m) {
         if (v.op == OP_O || v.op == OP_DOWN)
             for (int k = 0; k < v.nwg; ++k)
                 max_rows = std::max(max_rows, (block_begin(v.n_items, k + 1, v.nwg) - block_begin(v.n_items, k, v.nwg)) * v.mat.RT);
-    const int kmax = std::max({c.hidden, Q, c.intermediate});
+    int kmax = 8;  // longest (padded) GEMV input
+    for (const Interval &v : P.iv)
+        if (v.op != OP_ATTN) kmax = std::max(kmax, v.mat.IT * v.mat.L * 8);
     size_t off = 0;
     P.lds_ivtab = (int)off; off = a16(off + (size_t)n_iv * sizeof(Interval));
     const size_t task_slot = off;
