@@ -1144,6 +1144,22 @@ MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int 
 // Inside a 16-lane row the slots are combined by rotating the row by 2, 4
 // and 8 lanes (each step doubles the slots covered), then rows by the lane
 // swaps.
+// LP known at compile time: only the steps needed.
+template <int LP> MBK_DEV float slot_sum_c(float v) {
+    if constexpr (LP <= 1) v += dpp<0x121>(v);   // row_ror:1
+    if constexpr (LP <= 2) v += dpp<0x122>(v);   // row_ror:2
+    if constexpr (LP <= 4) v += dpp<0x124>(v);   // row_ror:4
+    if constexpr (LP <= 8) v += dpp<0x128>(v);   // row_ror:8
+    return xsum32(xsum16(v));
+}
+template <int LP> MBK_DEV float slot_max_c(float v) {
+    if constexpr (LP <= 1) v = fmaxf(v, dpp<0x121>(v));
+    if constexpr (LP <= 2) v = fmaxf(v, dpp<0x122>(v));
+    if constexpr (LP <= 4) v = fmaxf(v, dpp<0x124>(v));
+    if constexpr (LP <= 8) v = fmaxf(v, dpp<0x128>(v));
+    return xmax32(xmax16(v));
+}
+
 // LP is wave-uniform: each step is computed and kept by a select (no branches).
 MBK_DEV float slot_sum(float v, int LP) {
     float t = dpp<0x121>(v);   // row_ror:1
@@ -1173,12 +1189,13 @@ MBK_DEV void put2(const Params &p, uint64_t base, int i, float a, float b, uint3
     stc16(p.ws, (uint32_t)(base + 8u * (uint32_t)i), (u32x4){__float_as_uint(a), tag, __float_as_uint(b), tag});
 }
 
-// One attention item.
-template <int G>
+// One attention item, for head size LP * 8 (LP lanes per position).
+template <int G, int LP>
 MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const Task &T, uint8_t *lds, Ctl &ctl,
                             RingPos &rp, StepCtx &sc) {
-    const int pos = sc.pos, hd = p.hd, lsh = p.hd_shift - 3, LP = 1 << lsh, PPW = 64 >> lsh;
-    const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane & (LP - 1), slot = lane >> lsh;
+    constexpr int hd = LP * 8, PPW = 64 / LP;
+    const int pos = sc.pos;
+    const int lane = threadIdx.x & 63, cw = wave_id(), dl = lane & (LP - 1), slot = lane / LP;
     const AttnItem item = attn_item(T);
     const int j = item.j, s = item.s, h0 = item.h0, nh = item.nh;
     if (s >= sc.ss.nsplit) return;  // no allocations either
@@ -1195,6 +1212,21 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         const float4 a = *(const float4 *)(qkv + h * hd + dl * 8), b = *(const float4 *)(qkv + h * hd + dl * 8 + 4);
         qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
         qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
+    }
+    // the queries as hi/lo bf16 pairs for the cached (bf16) keys: dot2 on the packed keys
+    u32x4 qh[G], ql[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        if (h >= nh) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = qf[h][e];
+        qh[h].x = to_bf16x2(v[0], v[1]); qh[h].y = to_bf16x2(v[2], v[3]);
+        qh[h].z = to_bf16x2(v[4], v[5]); qh[h].w = to_bf16x2(v[6], v[7]);
+        ql[h].x = to_bf16x2(v[0] - bf_lo(qh[h].x), v[1] - bf_hi(qh[h].x));
+        ql[h].y = to_bf16x2(v[2] - bf_lo(qh[h].y), v[3] - bf_hi(qh[h].y));
+        ql[h].z = to_bf16x2(v[4] - bf_lo(qh[h].z), v[5] - bf_hi(qh[h].z));
+        ql[h].w = to_bf16x2(v[6] - bf_lo(qh[h].w), v[7] - bf_hi(qh[h].w));
     }
     float M[G], l[G], acc[G][8];
 #pragma unroll
@@ -1216,7 +1248,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
             const uint32_t start = ring_acquire(p, ctl, rp, A);
             kb = ring + start;
             vb = kb + A.r1;
-            nring = (int)(A.b0 >> (p.hd_shift + 1));
+            nring = (int)(A.b0 / (uint32_t)(hd * 2));
         }
         const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
         // this wave's scores of the segment (to LDS, read back by the same lanes) and their maximum
@@ -1225,19 +1257,26 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
         for (int b = cw; b * PPW < npos; b += kCW) {
             const int t = b * PPW + slot;
+            // a cached key (bf16 in the ring), this step's key (fp32 in LDS), or nothing past the segment
+            u32x4 kw = {0u, 0u, 0u, 0u};
             float kf[8];
-            if (t < npos) seg_row(t, nring, kb, cur, hd, dl, kf);
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kf[e] = 0.f;
-            }
+            const bool cached = t < nring;
+            if (cached) kw = *(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16);
+            else if (t < npos) seg_row(t, nring, kb, cur, hd, dl, kf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 if (h >= nh) break;
                 float d = 0.f;
+                if (cached) {
+                    d = dot2(kw.x, qh[h].x, d); d = dot2(kw.y, qh[h].y, d);
+                    d = dot2(kw.z, qh[h].z, d); d = dot2(kw.w, qh[h].w, d);
+                    d = dot2(kw.x, ql[h].x, d); d = dot2(kw.y, ql[h].y, d);
+                    d = dot2(kw.z, ql[h].z, d); d = dot2(kw.w, ql[h].w, d);
+                } else if (t < npos) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
-                d = group_sum_n(d, LP);
+                    for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
+                }
+                d = group_sum<LP>(d);
                 if (t < npos) {
                     lmax[h] = fmaxf(lmax[h], d);
                     if (dl == 0) scores[h * sstride + t] = d;
@@ -1247,7 +1286,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (h >= nh) break;
-            const float mn = fmaxf(M[h], slot_max(lmax[h], LP));
+            const float mn = fmaxf(M[h], slot_max_c<LP>(lmax[h]));
             if (mn != M[h]) {
                 const float c = __expf(M[h] - mn);  // 0 while M is -inf
                 l[h] *= c;
@@ -1279,9 +1318,9 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         if (h >= nh) break;
-        l[h] = slot_sum(l[h], LP);
+        l[h] = slot_sum_c<LP>(l[h]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum(acc[h][e], LP);
+        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum_c<LP>(acc[h][e]);
         if (slot == 0) {
             float *r = scr + ((size_t)cw * G + h) * stride;
             if (dl == 0) {
@@ -1297,7 +1336,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         // log-sum-exp combination of the wave partials, one head dimension per lane (a wave without
         // positions has max -inf)
         for (int u = lane; u < nh * hd; u += 64) {
-            const int h = u >> p.hd_shift, d = u & (hd - 1);
+            const int h = u / hd, d = u % hd;
             float mw = -INFINITY;
             for (int w = 0; w < kCW; ++w) mw = fmaxf(mw, scr[((size_t)w * G + h) * stride]);
             float ll = 0.f, a = 0.f;
@@ -1349,7 +1388,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
                 *(u32x4 *)(scr + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
             cw_barrier(p, ctl, sc.gen);
             for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
-                const int h = idx >> p.hd_shift, e = idx & (hd - 1);
+                const int h = idx / hd, e = idx % hd;
                 float mm = -INFINITY, ll = 0.f, a0 = 0.f, a1 = 0.f;
                 for (int q = 0; q < nsplit; ++q) {
                     const float *r = scr + ((size_t)q * G + h) * stride;
@@ -1460,7 +1499,12 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                     if (attn_item(T).s < sc.ss.nsplit) {
                         read_prog(ctl, rp.seen);
                         interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
-                        attention_task<G>(p, iv, ivi, T, lds, ctl, rp, sc);
+                        switch (p.hd_shift) {  // head size 16, 32, 64 or 128
+                        case 4: attention_task<G, 2>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                        case 5: attention_task<G, 4>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                        case 6: attention_task<G, 8>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                        default: attention_task<G, 16>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                    }
                     }
                     ++k;
                     if (T.flags & TASK_LAST) break;
