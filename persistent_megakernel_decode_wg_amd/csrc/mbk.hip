@@ -343,16 +343,12 @@ std::string build_plan(mbk_model *m) {
     const size_t in_block = a16((size_t)(G + 2) * hd * 4) + (c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0) +
                             a16((size_t)kmax * 4) + a16((size_t)max_rows * 4);
     {
-        // the second copy costs ring space; that matters most where the ring would otherwise hold most
-        // of a layer's weights per workgroup (then the loader runs ahead across whole intervals).
+        // the second copy costs ring space: it is kept only while it is small.  Where the weights per
+        // workgroup and interval exceed the ring (streaming-bound shapes) the ring is worth more: the
+        // bytes in flight per workgroup are bounded by its free part.
         // fixed holds one copy already: left is what a second copy leaves.
         const size_t left = kLdsMax - kLdsStatic - task_slot - fixed - in_block;
-        const LayerPlan &L0 = P.layers[0];
-        const uint64_t layer_bytes = ((uint64_t)L0.qkv.ntiles * L0.qkv.IT + (uint64_t)L0.o.ntiles * L0.o.IT +
-                                      (uint64_t)L0.gu.ntiles * L0.gu.IT + (uint64_t)L0.down.ntiles * L0.down.IT) *
-                                     kChunk / (uint64_t)n_wg;
-        const bool ring_holds_layer = (uint64_t)(left + in_block) * 4 >= layer_bytes * 3;  // with one copy
-        P.in_double = left > (size_t)64 * 16 + 64 * 1024 && (in_block <= 16 * 1024 || !ring_holds_layer) ? 1 : 0;
+        P.in_double = left > (size_t)64 * 16 + 64 * 1024 && in_block <= 16 * 1024 ? 1 : 0;
         if (P.in_double) fixed += in_block;
     }
 
@@ -380,7 +376,9 @@ std::string build_plan(mbk_model *m) {
                         P.task_list.push_back(Task{i, it, attn_task_item(it, P.max_splits, G, P.attn_hpi), 0});
                 } else {
                     const int b0 = block_begin(v.n_items, k, v.nwg), b1 = block_begin(v.n_items, k + 1, v.nwg);
-                    const int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
+                    // runs of whole rounds of the compute waves (a multiple of kCW tiles) where they fit
+                    int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
+                    if (per >= kCW && b1 - b0 > per) per -= per % kCW;
                     for (int t = b0; t < b1; t += per)
                         P.task_list.push_back(Task{i, t, std::min(per, b1 - t), b1 << 8});
                 }
