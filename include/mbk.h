@@ -144,8 +144,10 @@ int mbk_set_debug(mbk_model *m, int32_t spin_limit, int32_t skip_wg, int32_t ski
  * writes the device wall clock (100 MHz) into buf as uint64
  * [interval][workgroup][4]: [0] interval start, [1] inputs loaded (written only by
  * workgroups with work in the interval), [2] body
- * done, [3] grid barrier passed (barrier mode only).  buf must hold
- * n_intervals * n_CUs * 32 bytes; NULL switches the timer off. */
+ * done, [3] grid barrier passed (barrier mode only); entries of intervals
+ * where a workgroup has no work are 0.  The stamps are stores issued during
+ * the step (the timer takes no LDS).  buf must hold n_intervals * n_CUs * 32
+ * bytes; NULL switches the timer off. */
 int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
 
 /* Attention split policy: each split of the cached context covers at least

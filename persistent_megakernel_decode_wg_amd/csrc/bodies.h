@@ -75,7 +75,7 @@ struct Params {
     int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
     int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
     // LDS offsets in bytes of the dynamic area
-    int32_t lds_ivtab, lds_tasks, lds_trace, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
+    int32_t lds_ivtab, lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
     int32_t ring_bytes, max_tasks;
     int32_t in_bytes, in_double;  // LDS input block [qkv | bias | xs | xres] size; 1: two copies used in turn
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
@@ -192,12 +192,13 @@ MBK_DEV bool aborted(const Params &p, int it) {
 }
 
 // ---- phase timer -----------------------------------------------------------------------------------
-// Compute wave 0 stamps the device wall clock (100 MHz) into LDS; the stamps
-// are copied to the trace buffer when the workgroup leaves, so the timer adds
-// no memory traffic to the step.
+// Compute wave 0 stores the device wall clock (100 MHz) to the trace buffer:
+// [interval][workgroup][4].  Off unless a trace buffer is bound (then the
+// prologue clears this workgroup's entries first); it takes no LDS.
 
 MBK_DEV void stamp(const Params &p, uint8_t *lds, int ivi, int k) {
-    if (p.trace && threadIdx.x == 0) ((uint64_t *)(lds + p.lds_trace))[ivi * 4 + k] = wall_clock64();
+    (void)lds;
+    if (p.trace && threadIdx.x == 0) p.trace[((size_t)ivi * p.n_wg + blockIdx.x) * 4 + k] = wall_clock64();
 }
 
 // ---- tagged activations --------------------------------------------------------------------------
@@ -1535,7 +1536,7 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
     return true;
 }
 
-// ---- launch prologue / epilogue -------------------------------------------------------------------
+// ---- launch prologue -------------------------------------------------------------------------
 
 // Copies the interval table, this workgroup's tasks of [first_iv, last_iv)
 // and this step's RoPE row into LDS and clears the control words.  Returns
@@ -1555,8 +1556,11 @@ MBK_DEV int prologue(const Params &p, uint8_t *lds, Ctl &ctl, int pos) {
     float *rope = (float *)(lds + p.lds_rope);
     for (int i = threadIdx.x; i < 2 * half; i += kThreads) rope[i] = p.rope[(size_t)pos * 2 * half + i];
     if (p.trace) {
-        uint64_t *tr = (uint64_t *)(lds + p.lds_trace);
-        for (int i = threadIdx.x; i < p.n_intervals * 4; i += kThreads) tr[i] = 0;
+        // this workgroup's stamps of [first_iv, last_iv) start at zero; the stores are complete before
+        // the barrier below, so no stamp can be overtaken by them
+        for (int i = threadIdx.x; i < (p.last_iv - p.first_iv) * 4; i += kThreads)
+            p.trace[((size_t)(p.first_iv + i / 4) * p.n_wg + blockIdx.x) * 4 + (i % 4)] = 0;
+        __builtin_amdgcn_s_waitcnt(0);
     }
     if (threadIdx.x == 0) {
         for (int w = 0; w < kLW; ++w) ctl.prog[w] = 0;
@@ -1566,15 +1570,6 @@ MBK_DEV int prologue(const Params &p, uint8_t *lds, Ctl &ctl, int pos) {
     }
     __syncthreads();
     return nt;
-}
-
-// Writes the phase-timer stamps of this workgroup.  All threads.
-MBK_DEV void epilogue(const Params &p, const uint8_t *lds) {
-    __syncthreads();
-    if (!p.trace) return;
-    const uint64_t *tr = (const uint64_t *)(lds + p.lds_trace);
-    for (int i = threadIdx.x; i < p.n_intervals * 4; i += kThreads)
-        if (i / 4 >= p.first_iv && i / 4 < p.last_iv) p.trace[((size_t)(i / 4) * p.n_wg + blockIdx.x) * 4 + (i % 4)] = tr[i];
 }
 
 // The step body shared by both executors.
@@ -1607,7 +1602,6 @@ MBK_DEV void run_step(const Params &p) {
         }
         if (!compute<G>(p, lds, ctl, nt, sc)) lds_st(&ctl.abort, 1u);
     }
-    epilogue(p, lds);
 }
 
 }  // namespace mbk

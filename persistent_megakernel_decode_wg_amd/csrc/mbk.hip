@@ -115,7 +115,7 @@ struct Plan {
     std::vector<int32_t> task_index;   // [n_wg][n_iv + 1]
     int max_splits = 1, piece_pos = 1, max_tasks = 0, in_bytes = 0, in_double = 0, attn_hpi = 1;
     // LDS layout (bytes of the dynamic area)
-    int lds_ivtab = 0, lds_tasks = 0, lds_trace = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
+    int lds_ivtab = 0, lds_tasks = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
         lds_xres = 0, lds_attn = 0, lds_score = 0, lds_ring = 0, ring_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
@@ -328,9 +328,8 @@ std::string build_plan(mbk_model *m) {
     P.lds_ivtab = (int)off; off = a16(off + (size_t)n_iv * sizeof(Interval));
     const size_t task_slot = off;
     // tasks are laid out below, once their count is known; reserve after the fixed parts
-    P.lds_trace = 0; P.lds_rope = 0;
+    P.lds_rope = 0;
     size_t fixed = 0;
-    fixed += a16((size_t)n_iv * 32);                               // trace
     fixed += a16((size_t)4 * hd);                                  // RoPE row
     fixed += a16((size_t)(G + 2) * hd * 4);                        // attention inputs
     fixed += c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0;       // Q/K/V bias
@@ -406,7 +405,6 @@ std::string build_plan(mbk_model *m) {
     build_tasks(ring);
     off = task_slot;
     P.lds_tasks = (int)off; off = a16(off + (size_t)P.max_tasks * 16);
-    P.lds_trace = (int)off; off = a16(off + (size_t)n_iv * 32);
     P.lds_rope = (int)off; off = a16(off + (size_t)4 * hd);
     P.lds_qkv = (int)off; off = a16(off + (size_t)(G + 2) * hd * 4);
     P.lds_bias = (int)off; off = c.qkv_bias ? a16(off + (size_t)(Q + 2 * KV) * 4) : off;
@@ -422,7 +420,7 @@ std::string build_plan(mbk_model *m) {
     if (ring < (size_t)kMinRing || ring < 3 * max_tile) return "not enough LDS for the weight ring";
     // task runs were cut for the ring size used by build_tasks; re-cut if the ring shrank
     build_tasks(ring);
-    if (P.lds_tasks + (size_t)P.max_tasks * 16 > (size_t)P.lds_trace) return "task list does not fit its LDS slot";
+    if (P.lds_tasks + (size_t)P.max_tasks * 16 > (size_t)P.lds_rope) return "task list does not fit its LDS slot";
     P.ring_bytes = (int)ring;
     P.lds_bytes = off + ring;
     // attention pieces: at most a third of the ring, keys and values each rounded up to whole chunks
@@ -531,7 +529,6 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     while ((1 << p.hd_shift) < c.head_dim) ++p.hd_shift;
     p.lds_ivtab = P.lds_ivtab;
     p.lds_tasks = P.lds_tasks;
-    p.lds_trace = P.lds_trace;
     p.lds_rope = P.lds_rope;
     p.lds_qkv = P.lds_qkv;
     p.lds_bias = P.lds_bias;
