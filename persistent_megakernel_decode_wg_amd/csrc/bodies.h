@@ -128,6 +128,10 @@ MBK_DEV uint32_t to_bf16x2(float a, float b) {
 }
 
 MBK_DEV uint32_t ldc_u(const uint32_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// The same for a word every lane of the wave reads at once: lane 0's value, known to the compiler as
+// wave-uniform (an atomic load is otherwise taken to differ between lanes, and every branch and loop
+// that depends on it becomes an exec-mask construct).
+MBK_DEV uint32_t ldc_uni(const uint32_t *p) { return __builtin_amdgcn_readfirstlane(ldc_u(p)); }
 MBK_DEV void stc_u(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MBK_DEV uint32_t atom_add(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -188,7 +192,7 @@ MBK_DEV void lds_st(uint32_t *p, uint32_t v) { *(volatile lds_u32 *)(lds_u32 *)p
 // Error word: set when a bounded wait expires; every wait of every workgroup gives up soon after.
 MBK_DEV void set_error(const Params &p) { stc_u(ws_ptr<uint32_t>(p, p.wl.ctrl), 1u); }
 MBK_DEV bool aborted(const Params &p, int it) {
-    return (it & 255) == 255 && ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl)) != 0u;
+    return (it & 255) == 255 && ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl)) != 0u;
 }
 
 // ---- phase timer -----------------------------------------------------------------------------------
@@ -204,7 +208,7 @@ MBK_DEV void stamp(const Params &p, uint8_t *lds, int ivi, int k) {
 // ---- tagged activations --------------------------------------------------------------------------
 
 MBK_DEV uint32_t step_seq(const Params &p) {
-    return p.step_from_ws ? ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 5) : p.seq;
+    return p.step_from_ws ? ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 5) : p.seq;
 }
 
 // Tag of what interval ivi writes during step seq.  Nonzero (a zeroed
@@ -407,12 +411,12 @@ MBK_DEV float group_sum_n(float v, int n) {
 // ---- step inputs -----------------------------------------------------------------------------------
 
 MBK_DEV int step_token(const Params &p) {
-    int t = p.step_from_ws ? (int)ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 3) : p.token;
-    if (t < 0) t = (int)ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 1);
+    int t = p.step_from_ws ? (int)ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 3) : p.token;
+    if (t < 0) t = (int)ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 1);
     return t;
 }
 MBK_DEV int step_pos(const Params &p) {
-    return p.step_from_ws ? (int)ldc_u(ws_ptr<uint32_t>(p, p.wl.ctrl) + 4) : p.pos;
+    return p.step_from_ws ? (int)ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 4) : p.pos;
 }
 
 // ---- ring allocations ------------------------------------------------------------------------------
