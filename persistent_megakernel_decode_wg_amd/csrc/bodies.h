@@ -75,7 +75,7 @@ struct Params {
     int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
     int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
     // LDS offsets in bytes of the dynamic area
-    int32_t lds_ivtab, lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_score, lds_ring;
+    int32_t lds_ivtab, lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_ring;
     int32_t ring_bytes, max_tasks;
     int32_t in_bytes, in_double;  // LDS input block [qkv | bias | xs | xres] size; 1: two copies used in turn
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
@@ -1128,21 +1128,24 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
 // takes one position per block and head dims dl*8 .. dl*8+7 (LP = hd/8
 // lanes per position); the compute waves take alternate blocks.  Positions
 // arrive in segments (the ring pieces, the last one extended by the position
-// appended this step).  Each compute wave keeps its own running maximum, sum
-// and weighted values over its positions (online softmax: a segment that
-// raises the maximum rescales them once), so the waves never wait for one
-// another inside an item; at its end the wave partials meet in LDS and are
-// combined with the log-sum-exp rule, like the partials of different splits.
+// appended this step).  Every lane keeps the running maximum, sum and
+// weighted values of its own positions (online softmax in one pass over the
+// keys and values: a score above the maximum rescales what the lane holds),
+// so neither the lanes nor the waves wait for one another inside an item; at
+// its end the slots of a wave, then the waves in LDS, are combined with the
+// log-sum-exp rule, like the partials of different splits.
 
 // Key (or value) of position t of a segment: ring positions t < nring
 // (bf16), then the appended position (fp32 in LDS at cur).
+// 8 floats from LDS.
+MBK_DEV void load8f(const float *src, float *f) {
+    const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
 MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int hd, int dl, float *f) {
-    if (t < nring) {
-        unpack8(*(const u32x4 *)(rb + (size_t)t * hd * 2 + dl * 16), f);
-    } else {
-        const float4 a = *(const float4 *)(cur + dl * 8), b = *(const float4 *)(cur + dl * 8 + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    }
+    if (t < nring) unpack8(*(const u32x4 *)(rb + (size_t)t * hd * 2 + dl * 16), f);
+    else load8f(cur + dl * 8, f);
 }
 
 // Sum (max) over the slots of a wave: the lanes with the same lane % LP.
@@ -1208,24 +1211,14 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
     const int nsplit = sc.ss.nsplit;
     const float *qkv = (const float *)(lds + p.lds_qkv + sc.in);
     const float *cur = qkv + G * hd;        // this step's key, then value
-    float *scores = (float *)(lds + p.lds_score);   // [G][piece_pos + 1]
-    const int sstride = p.piece_pos + 1;
-    float qf[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        if (h >= nh) break;
-        const float4 a = *(const float4 *)(qkv + h * hd + dl * 8), b = *(const float4 *)(qkv + h * hd + dl * 8 + 4);
-        qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
-        qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
-    }
-    // the queries as hi/lo bf16 pairs for the cached (bf16) keys: dot2 on the packed keys
+    // the queries as hi/lo bf16 pairs for the cached (bf16) keys: dot2 on the packed keys (this step's
+    // key, in fp32, meets the fp32 queries, read again from LDS)
     u32x4 qh[G], ql[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         if (h >= nh) break;
         float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = qf[h][e];
+        load8f(qkv + h * hd + dl * 8, v);
         qh[h].x = to_bf16x2(v[0], v[1]); qh[h].y = to_bf16x2(v[2], v[3]);
         qh[h].z = to_bf16x2(v[4], v[5]); qh[h].w = to_bf16x2(v[6], v[7]);
         ql[h].x = to_bf16x2(v[0] - bf_lo(qh[h].x), v[1] - bf_hi(qh[h].x));
@@ -1256,18 +1249,22 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
             nring = (int)(A.b0 / (uint32_t)(hd * 2));
         }
         const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
-        // this wave's scores of the segment (to LDS, read back by the same lanes) and their maximum
-        float lmax[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
+        // one pass over the segment: every lane keeps the running maximum, sum and weighted values of
+        // its own positions (a raised maximum rescales what the lane holds)
         for (int b = cw; b * PPW < npos; b += kCW) {
             const int t = b * PPW + slot;
-            // a cached key (bf16 in the ring), this step's key (fp32 in LDS), or nothing past the segment
-            u32x4 kw = {0u, 0u, 0u, 0u};
-            float kf[8];
-            const bool cached = t < nring;
-            if (cached) kw = *(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16);
-            else if (t < npos) seg_row(t, nring, kb, cur, hd, dl, kf);
+            const bool valid = t < npos, cached = t < nring;
+            // a cached key and value (bf16 in the ring), this step's (fp32 in LDS), or nothing past the segment
+            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+            float kf[8], vf[8];
+            if (cached) {
+                kw = *(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16);
+                vw = *(const u32x4 *)(vb + (size_t)t * hd * 2 + dl * 16);
+            } else if (valid) {
+                seg_row(t, nring, kb, cur, hd, dl, kf);
+                seg_row(t, nring, vb, cur + hd, hd, dl, vf);
+            }
+            if (cached) unpack8(vw, vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 if (h >= nh) break;
@@ -1277,59 +1274,46 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
                     d = dot2(kw.z, qh[h].z, d); d = dot2(kw.w, qh[h].w, d);
                     d = dot2(kw.x, ql[h].x, d); d = dot2(kw.y, ql[h].y, d);
                     d = dot2(kw.z, ql[h].z, d); d = dot2(kw.w, ql[h].w, d);
-                } else if (t < npos) {
+                } else if (valid) {
+                    float qf[8];
+                    load8f(qkv + h * hd + dl * 8, qf);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
+                    for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
                 }
                 d = group_sum<LP>(d);
-                if (t < npos) {
-                    lmax[h] = fmaxf(lmax[h], d);
-                    if (dl == 0) scores[h * sstride + t] = d;
+                if (valid) {
+                    if (d > M[h]) {
+                        const float c = __expf(M[h] - d);  // 0 while M is -inf
+                        l[h] *= c;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[h][e] *= c;
+                        M[h] = d;
+                    }
+                    const float w = __expf(d - M[h]);
+                    l[h] += w;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
                 }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (h >= nh) break;
-            const float mn = fmaxf(M[h], slot_max_c<LP>(lmax[h]));
-            if (mn != M[h]) {
-                const float c = __expf(M[h] - mn);  // 0 while M is -inf
-                l[h] *= c;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= c;
-                M[h] = mn;
-            }
-        }
-        // weights and values
-        for (int b = cw; b * PPW < npos; b += kCW) {
-            const int t = b * PPW + slot;
-            if (t >= npos) continue;
-            float vf[8];
-            seg_row(t, nring, vb, cur + hd, hd, dl, vf);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                if (h >= nh) break;
-                const float w = __expf(scores[h * sstride + t] - M[h]);
-                l[h] += w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
             }
         }
         if (k < na) ring_release(ctl, rp);
     }
-    // wave partials {max, sum, -, -, acc[hd]} to LDS; compute wave 0 combines them
+    // wave partials {max, sum, -, -, acc[hd]} to LDS (the slots of the wave combined by the log-sum-exp
+    // rule); compute wave 0 combines them
     const int stride = hd + 4;
     float *scr = (float *)(lds + p.lds_attn);  // [kCW][G][stride]
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         if (h >= nh) break;
-        l[h] = slot_sum_c<LP>(l[h]);
+        const float mw = slot_max_c<LP>(M[h]);
+        const float c = M[h] == -INFINITY ? 0.f : __expf(M[h] - mw);  // a slot without positions adds nothing
+        l[h] = slot_sum_c<LP>(l[h] * c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum_c<LP>(acc[h][e]);
+        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum_c<LP>(acc[h][e] * c);
         if (slot == 0) {
             float *r = scr + ((size_t)cw * G + h) * stride;
             if (dl == 0) {
-                r[0] = M[h];
+                r[0] = mw;
                 r[1] = l[h];
             }
             store8(r + 4 + dl * 8, acc[h]);

@@ -116,7 +116,7 @@ struct Plan {
     int max_splits = 1, piece_pos = 1, max_tasks = 0, in_bytes = 0, in_double = 0, attn_hpi = 1;
     // LDS layout (bytes of the dynamic area)
     int lds_ivtab = 0, lds_tasks = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
-        lds_xres = 0, lds_attn = 0, lds_score = 0, lds_ring = 0, ring_bytes = 0;
+        lds_xres = 0, lds_attn = 0, lds_ring = 0, ring_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
 };
@@ -336,7 +336,6 @@ std::string build_plan(mbk_model *m) {
     fixed += a16((size_t)kmax * 4);                                // GEMV input (hi/lo pairs)
     fixed += a16((size_t)max_rows * 4);                            // residual rows
     fixed += a16((size_t)std::max(kCW, ms) * G * stride * 4);      // attention merge scratch
-    fixed += a16(((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);  // attention scores and maxima
     // input block [attention inputs | bias | GEMV input | residual rows]; a second copy lets an
     // interval's inputs load while other compute waves still read the previous interval's
     const size_t in_block = a16((size_t)(G + 2) * hd * 4) + (c.qkv_bias ? a16((size_t)(Q + 2 * KV) * 4) : 0) +
@@ -375,9 +374,11 @@ std::string build_plan(mbk_model *m) {
                         P.task_list.push_back(Task{i, it, attn_task_item(it, P.max_splits, G, P.attn_hpi), 0});
                 } else {
                     const int b0 = block_begin(v.n_items, k, v.nwg), b1 = block_begin(v.n_items, k + 1, v.nwg);
-                    // runs of whole rounds of the compute waves (a multiple of kCW tiles) where they fit
+                    // a block longer than one run goes in runs of one tile per compute wave (where that
+                    // fits): the ring then holds several runs, and the bytes in flight are what the run
+                    // being computed leaves free
                     int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
-                    if (per >= kCW && b1 - b0 > per) per -= per % kCW;
+                    if (per >= kCW && b1 - b0 > per) per = kCW;
                     for (int t = b0; t < b1; t += per)
                         P.task_list.push_back(Task{i, t, std::min(per, b1 - t), b1 << 8});
                 }
@@ -413,7 +414,6 @@ std::string build_plan(mbk_model *m) {
     P.in_bytes = (int)(off - (size_t)P.lds_qkv);
     if (P.in_double) off += P.in_bytes;
     P.lds_attn = (int)off; off = a16(off + (size_t)std::max(kCW, ms) * G * stride * 4);
-    P.lds_score = (int)off; off = a16(off + ((size_t)G * (kPiecePos + 1) + 2 * kCW * G) * 4);
     off = (off + kChunk - 1) / kChunk * kChunk;
     P.lds_ring = (int)off;
     if (off + ring + kLdsStatic > kLdsMax) ring = (kLdsMax - kLdsStatic - off) / kChunk * kChunk;
@@ -535,7 +535,6 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.lds_xs = P.lds_xs;
     p.lds_xres = P.lds_xres;
     p.lds_attn = P.lds_attn;
-    p.lds_score = P.lds_score;
     p.lds_ring = P.lds_ring;
     p.ring_bytes = P.ring_bytes;
     p.in_bytes = P.in_bytes;
