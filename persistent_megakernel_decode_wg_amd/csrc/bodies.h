@@ -1378,16 +1378,16 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
             cw_barrier(p, ctl, sc.gen);
             for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
                 const int h = idx / hd, e = idx % hd;
-                float mm = -INFINITY, ll = 0.f, a0 = 0.f, a1 = 0.f;
+                // the largest split maximum first: then the splits' weights are independent of each other
+                float mm = -INFINITY;
+                for (int q = 0; q < nsplit; ++q) mm = fmaxf(mm, scr[((size_t)q * G + h) * stride]);
+                float ll = 0.f, a0 = 0.f, a1 = 0.f;
                 for (int q = 0; q < nsplit; ++q) {
                     const float *r = scr + ((size_t)q * G + h) * stride;
-                    const float m2 = r[0], mn = fmaxf(mm, m2);
-                    if (mn == -INFINITY) continue;
-                    const float c1 = __expf(mm - mn), c2 = __expf(m2 - mn);
-                    ll = ll * c1 + r[1] * c2;
-                    a0 = a0 * c1 + r[4 + e] * c2;
-                    a1 = a1 * c1 + r[5 + e] * c2;
-                    mm = mn;
+                    const float c = r[0] == -INFINITY ? 0.f : __expf(r[0] - mm);  // a split without positions
+                    ll = fmaf(r[1], c, ll);
+                    a0 = fmaf(r[4 + e], c, a0);
+                    a1 = fmaf(r[5 + e], c, a1);
                 }
                 put2(p, p.wl.o, (j * G + h) * hd + e, a0 / ll, a1 / ll, tag);
             }
