@@ -265,6 +265,30 @@ MBK_DEV bool poll8(const Params &p, uint64_t base, int g, uint32_t tag, float *v
     }
 }
 
+// Groups g[0 .. n) (n <= N) of the tagged vector at base: every load of a
+// round is in flight at once, a round reloads only the groups still pending,
+// and v[i] receives group g[i] once it carries `tag`.  Bounded like poll8.
+template <int N>
+MBK_DEV void poll8n(const Params &p, uint64_t base, const int *g, int n, uint32_t tag, float (*v)[8]) {
+    uint32_t pending = (1u << n) - 1u;
+    Group8 a[N];
+    for (int it = 0;; ++it) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((pending >> i) & 1u) a[i] = load8(p, (uint32_t)(base + 64u * (uint32_t)g[i]));
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (((pending >> i) & 1u) && tagged8(a[i], tag)) pending &= ~(1u << i);
+        if (!pending || it >= p.spin_limit || aborted(p, it)) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) values8(a[i], v[i]);
+            if (pending && it >= p.spin_limit) set_error(p);
+            return;
+        }
+        reread();
+    }
+}
+
 // One entry of a tagged vector.
 MBK_DEV bool poll1(const Params &p, uint64_t base, int i, uint32_t tag, float &v) {
     const uint64_t *e = ws_ptr<uint64_t>(p, base) + i;
@@ -790,12 +814,33 @@ MBK_DEV float norm_input(const Params &p, float *xs, bool from_embed, int token,
     return ss;
 }
 
-// xs <- hi/lo pairs of the tagged vector at base (threads [tid, nt)).
+// xs <- hi/lo pairs of the tagged vector at base (threads [tid, nt)).  A
+// thread polls all its groups (up to 4 per round: the widest inputs, 8192
+// entries over 256 threads, have 4) at once, so a wide input costs one wait
+// for its last group rather than one per group.
 MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag, int K, int tid, int nt) {
-    for (int g = tid; g < K / 8; g += nt) {
-        float v[8];
-        poll8(p, base, g, tag, v);
-        split8_store(xs + 8 * g, v);
+    constexpr int kG = 4;
+    const int ng = K / 8;
+    if (ng <= nt) {  // one group per thread at most
+        if (tid < ng) {
+            float v[8];
+            poll8(p, base, tid, tag, v);
+            split8_store(xs + 8 * tid, v);
+        }
+        return;
+    }
+    for (int g0 = tid; g0 < ng; g0 += kG * nt) {
+        int g[kG], n = 0;
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+            g[i] = g0 + i * nt;
+            if (g[i] < ng) n = i + 1;
+        }
+        float v[kG][8];
+        poll8n<kG>(p, base, g, n, tag, v);
+#pragma unroll
+        for (int i = 0; i < kG; ++i)
+            if (i < n) split8_store(xs + 8 * g[i], v[i]);
     }
 }
 
