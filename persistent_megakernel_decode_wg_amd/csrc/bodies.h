@@ -450,10 +450,11 @@ MBK_DEV int step_pos(const Params &p) {
 // compute waves derive the same sequence of allocations from the task list
 // and the step's position.  An allocation is placed at the current virtual
 // ring offset, or at the next multiple of the ring size if it would straddle
-// the ring's end.  A GEMV task's weights take at most half the ring (one
-// run streams in while the previous one is consumed), an attention piece at
-// most a third; a loader waiting for space only ever waits for allocations
-// it has already issued, which the compute waves consume and release.
+// the ring's end.  A GEMV task's weights take at most half the ring (a
+// block longer than that goes in runs of one tile per compute wave, so the
+// ring holds several runs), an attention piece at most a third; a loader
+// waiting for space only ever waits for allocations it has already issued,
+// which the compute waves consume and release.
 
 // Attention split of this step: positions [0, pos] in nsplit splits of at
 // most chunk positions (computed once per step: the divisions stay out of

@@ -110,6 +110,26 @@ def test_smollm135m_kv4096_prefilled_long_context():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
 
 
+def test_smollm135m_kv128_split_attention_merged_by_output_projection():
+    """A 32-position attention split on the 128-slot cache (up to 4 splits per query head): the split
+    partials are tagged and merged by the output projection's workgroups while they load their input.
+    Parity with the oracle over the prompt and the first greedy steps, and every executor gives the
+    same bits."""
+    wl = synth.get("smollm135m-kv128")
+    p = Pair(wl)
+    p.dec.set_attention_split(32)
+    d = p.dec.describe()
+    assert d["max_splits"] >= 4
+    positions = list(range(80))
+    worst = teacher_forced(p, positions, list(synth.prompt_tokens(wl)), check_every=4, label="smollm135m-split32")
+    log("smollm135m-kv128 split 32: worst max|dlogit|/std = %.3g" % worst)
+    tok = int(synth.prompt_tokens(wl)[5])
+    a, ia = p.gpu_step(tok, 100, "mega")
+    for mode in ("barrier", "ablation"):
+        b, ib = p.gpu_step(tok, 100, mode)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
+
+
 @pytest.mark.parametrize("mode", ["mega", "barrier"])
 def test_watchdog_expires_and_recovers(mode):
     """Workgroup 0 leaves the persistent kernel before interval 0 (host-set debug switch, tiny spin
