@@ -152,11 +152,20 @@ int mbk_set_phase_trace(mbk_model *m, void *buf, size_t bytes);
 
 /* Attention split policy: each split of the cached context covers at least
  * min_positions positions (default 128); contexts up to that length run
- * unsplit.  Short caches whose keys and values of one head fit in 64 KiB get one
- * work item per query head, longer ones one per KV head (all its query heads).
- * The number of splits is bounded by the plan (at most one per 32 cached
- * positions and per workgroup of a KV head's share of the device). */
+ * unsplit.  The number of splits is bounded by the plan (at most one per 32
+ * cached positions, per workgroup of an item group's share of the device, and
+ * as many as the 16 KiB merge scratch holds). */
 int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
+
+/* Attention work items (the GQA packing of the flash-decoding step, README
+ * mirror "Current status"): heads_per_item = 1 gives one item per (query head,
+ * split); G = n_heads / n_kv_heads packs the G query heads of a KV head into
+ * one item, so each cached key and value is read once; 0 (default) chooses one
+ * query head per item unless there are more query heads than workgroups (on
+ * MI355X the shorter per-item chain wins: the G readers of a KV head mostly
+ * hit the caches).  Only before the schedule is planned (as
+ * mbk_set_workgroups); MBK_ERR_ARG for any other value. */
+int mbk_set_attention_items(mbk_model *m, int32_t heads_per_item);
 
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */
 int mbk_set_sync_mode(mbk_model *m, int32_t mode);

@@ -66,12 +66,13 @@ def lib():
         L.mbk_set_sync_mode.argtypes = [vp, i32]
         L.mbk_set_launch_mode.argtypes = [vp, i32]
         L.mbk_set_workgroups.argtypes = [vp, i32]
+        L.mbk_set_attention_items.argtypes = [vp, i32]
         L.mbk_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
                   "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
-                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_describe"):
+                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -198,6 +199,11 @@ class Decoder:
 
     def set_workgroups(self, n: int) -> None:
         _chk(lib().mbk_set_workgroups(self.h, n))
+
+    def set_attention_items(self, heads_per_item: int) -> None:
+        """0 (automatic), 1 (one query head per item) or n_heads / n_kv_heads (a KV head's query heads
+        packed); before the schedule is planned."""
+        _chk(lib().mbk_set_attention_items(self.h, int(heads_per_item)))
 
     def describe(self) -> dict:
         import json

@@ -140,6 +140,7 @@ struct mbk_model {
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
     int32_t attn_min_chunk = 128;
     int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
+    int32_t attn_items_set = 0;  // mbk_set_attention_items (0: automatic)
     bool kernels_ready = false;
     uint64_t *trace = nullptr;
     // graph replay of the ablation
@@ -275,9 +276,11 @@ std::string build_plan(mbk_model *m) {
     // one KV head fits the LDS merge scratch
     const int stride = hd + 4;
     const size_t merge_budget = 16 * 1024;
-    // attention items: one per query head when a head's cached keys and values are small (every item
-    // then reads its group's keys and values, from the caches), else the query heads of a KV head packed
-    P.attn_hpi = (size_t)c.kv_capacity * hd * 4 <= 64 * 1024 ? 1 : G;
+    // attention items: one per query head unless there are more query heads than workgroups (the G
+    // items of a KV head then read its keys and values G times, mostly from the caches, but each
+    // item's chain of dependent steps is G times shorter), else the query heads of a KV head packed
+    // so each key and value is read once; mbk_set_attention_items overrides the choice
+    P.attn_hpi = m->attn_items_set ? m->attn_items_set : (c.n_heads <= n_wg ? 1 : G);
     const int item_heads = P.attn_hpi == 1 ? c.n_heads : c.n_kv_heads;
     int ms = std::max(1, n_wg / item_heads);
     ms = std::min<int>(ms, (int)(merge_budget / ((size_t)G * stride * 4)));
@@ -880,6 +883,17 @@ int mbk_set_workgroups(mbk_model *m, int32_t n) {
     return MBK_OK;
 }
 
+int mbk_set_attention_items(mbk_model *m, int32_t heads_per_item) {
+    if (!m) return fail(MBK_ERR_ARG, "bad arguments");
+    const int G = m->c.n_heads / m->c.n_kv_heads;
+    if (heads_per_item != 0 && heads_per_item != 1 && heads_per_item != G)
+        return fail(MBK_ERR_ARG, "heads_per_item must be 0, 1 or %d (the query heads of a KV head)", G);
+    if (m->planned && heads_per_item != m->attn_items_set)
+        return fail(MBK_ERR_STATE, "the schedule is already planned");
+    m->attn_items_set = heads_per_item;
+    return MBK_OK;
+}
+
 int mbk_describe(mbk_model *m, char *buf, size_t len) {
     if (!m || !buf || len == 0) return fail(MBK_ERR_ARG, "bad arguments");
     int rc = ensure_plan(m);
@@ -894,9 +908,10 @@ int mbk_describe(mbk_model *m, char *buf, size_t len) {
         "{\"workgroups\": %d, \"threads\": %d, \"compute_waves\": %d, \"loader_waves\": %d, \"intervals\": %zu, "
         "\"packed_bytes\": %llu, \"workspace_bytes\": %llu, \"lds_bytes\": %zu, \"ring_bytes\": %d, "
         "\"max_tasks\": %d, \"tasks\": %zu, \"max_task_bytes\": %zu, \"max_tile_bytes\": %zu, "
-        "\"max_splits\": %d, \"piece_positions\": %d, \"double_inputs\": %d}",
+        "\"max_splits\": %d, \"piece_positions\": %d, \"double_inputs\": %d, \"attention_heads_per_item\": %d}",
         m->n_wg, kThreads, kCW, kLW, P.iv.size(), (unsigned long long)P.total, (unsigned long long)P.ws.total,
-        P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos, P.in_double);
+        P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos, P.in_double,
+        P.attn_hpi);
     if (n < 0 || (size_t)n >= len) return fail(MBK_ERR_SIZE, "description needs %d bytes", n + 1);
     return MBK_OK;
 }

@@ -32,7 +32,8 @@ def upload(W):
 class Pair:
     """A GPU decoder and the oracle on the same workload, weights and KV prefix."""
 
-    def __init__(self, wl, W=None, kv_prefix=None):
+    def __init__(self, wl, W=None, kv_prefix=None, setup=None):
+        """setup(decoder), if given, runs before the weights are packed (plan-time settings)."""
         import torch
         from persistent_megakernel_decode_wg_amd import Decoder
         from persistent_megakernel_decode_wg_amd import build as mbk_build
@@ -40,6 +41,8 @@ class Pair:
         self.wl = wl
         self.W = synth.make_weights(wl) if W is None else W
         self.dec = Decoder(wl)
+        if setup is not None:
+            setup(self.dec)
         self.dec.pack_weights(upload(self.W))
         self.dec.alloc_kv()
         self.ref = oracle.Model(wl, self.W)

@@ -122,3 +122,31 @@ def test_set_workgroups_after_planning_is_a_state_error():
         d.set_workgroups(64)
     assert e.value.code == MBK_ERR_STATE
     d.close()
+
+
+def test_attention_items_policy():
+    """One query head per attention item by default (fewer query heads than workgroups); the packed
+    choice (a KV head's G query heads per item) on request; other values are argument errors, and a
+    change after planning is a state error."""
+    from persistent_megakernel_decode_wg_amd import Decoder, MbkError, MBK_ERR_ARG, MBK_ERR_STATE
+    wl = synth.get("smollm135m-kv4096")
+    G = wl.n_heads // wl.n_kv_heads
+    d = Decoder(wl)
+    d.set_workgroups(256)
+    for bad in (-1, 2, G + 1):
+        with pytest.raises(MbkError) as e:
+            d.set_attention_items(bad)
+        assert e.value.code == MBK_ERR_ARG
+    assert d.describe()["attention_heads_per_item"] == 1
+    with pytest.raises(MbkError) as e:
+        d.set_attention_items(G)
+    assert e.value.code == MBK_ERR_STATE
+    d.set_attention_items(0)      # unchanged: allowed
+    d.close()
+    d = Decoder(wl)
+    d.set_workgroups(256)
+    d.set_attention_items(G)
+    info = d.describe()
+    assert info["attention_heads_per_item"] == G and info["max_splits"] >= 1
+    d.close()
+

@@ -130,6 +130,23 @@ def test_smollm135m_kv128_split_attention_merged_by_output_projection():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
 
 
+def test_smollm135m_kv4096_packed_gqa_items():
+    """The query heads of a KV head packed into one attention item (each cached key and value read
+    once), with the split merge by the last split to arrive: parity and equal bits across executors."""
+    wl = synth.get("smollm135m-kv4096")
+    G = wl.n_heads // wl.n_kv_heads
+    p = Pair(wl, kv_prefix=synth.kv_prefill(wl), setup=lambda d: d.set_attention_items(G))
+    assert p.dec.describe()["attention_heads_per_item"] == G
+    positions = synth.decode_schedule(wl)
+    worst = teacher_forced(p, positions[:4], [synth.first_token(wl)], label="smollm135m-4k-packed")
+    log("smollm135m-kv4096 packed items: worst max|dlogit|/std = %.3g" % worst)
+    pos, tok = positions[8], synth.first_token(wl)
+    a, ia = p.gpu_step(tok, pos, "mega")
+    for mode in ("barrier", "ablation"):
+        b, ib = p.gpu_step(tok, pos, mode)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
+
+
 @pytest.mark.parametrize("mode", ["mega", "barrier"])
 def test_watchdog_expires_and_recovers(mode):
     """Workgroup 0 leaves the persistent kernel before interval 0 (host-set debug switch, tiny spin
