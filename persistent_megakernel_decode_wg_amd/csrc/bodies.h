@@ -1401,13 +1401,14 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         }
     }
     if (nsplit > 1 && !p.merge_in_o) {
-        // the last split to arrive (one atomic per split) merges all partials in
-        // split order, so the result does not depend on arrival order
+        // the last split to arrive (one atomic per split) merges the partials in split order, so the
+        // result does not depend on arrival order.  A merge group is the query head of a single-head
+        // item (gh = 1 head, counter j * G + h0), else the KV head (gh = G heads, counter j)
+        const int gh = nh == 1 ? 1 : G, hb = nh == 1 ? h0 : 0, grp = nh == 1 ? j * G + h0 : j;
         if (threadIdx.x == 0) {
             __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
-            uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.merge_cnt + 256u * j);
-            // every item of the group arrives: splits x (query heads / heads per item)
-            const bool last = atom_add(cnt, 1u) == (uint32_t)(nsplit * (nh == 1 ? G : 1)) - 1u;
+            uint32_t *cnt = ws_ptr<uint32_t>(p, p.wl.merge_cnt + 256u * (uint32_t)grp);
+            const bool last = atom_add(cnt, 1u) == (uint32_t)nsplit - 1u;
             if (last) {
                 stc_u(cnt, 0u);
                 __builtin_amdgcn_s_waitcnt(0);  // the reset lands before this group's output does
@@ -1416,26 +1417,29 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         }
         cw_barrier(p, ctl, sc.gen);
         if (lds_ld((const uint32_t *)&ctl.last_s)) {
-            // every partial of head group j into LDS (scratch holds max_splits * G * stride floats)
-            const uint64_t gbase = p.wl.part + ((uint64_t)(j * p.max_splits) * G) * stride * 4u;
-            const int n16 = nsplit * G * stride / 4;
-            for (int idx = threadIdx.x; idx < n16; idx += kCW * 64)
-                *(u32x4 *)(scr + 4 * idx) = ldc16(p.ws, (uint32_t)(gbase + 16u * idx));
+            // the group's partials into LDS: scr[(q * gh + h) * stride] for split q, head hb + h (the
+            // scratch holds max_splits * G * stride floats)
+            constexpr int c16 = (hd + 4) / 4;  // 16-byte chunks of one partial
+            for (int idx = threadIdx.x; idx < nsplit * gh * c16; idx += kCW * 64) {
+                const int qh = idx / c16, c = idx - qh * c16, q = qh / gh, h = qh - q * gh;
+                const uint64_t src = p.wl.part + (((uint64_t)(j * p.max_splits + q) * G + hb + h) * stride + 4u * c) * 4u;
+                *(u32x4 *)(scr + (size_t)qh * stride + 4 * c) = ldc16(p.ws, (uint32_t)src);
+            }
             cw_barrier(p, ctl, sc.gen);
-            for (int idx = 2 * threadIdx.x; idx < G * hd; idx += 2 * kCW * 64) {
+            for (int idx = 2 * threadIdx.x; idx < gh * hd; idx += 2 * kCW * 64) {
                 const int h = idx / hd, e = idx % hd;
                 // the largest split maximum first: then the splits' weights are independent of each other
                 float mm = -INFINITY;
-                for (int q = 0; q < nsplit; ++q) mm = fmaxf(mm, scr[((size_t)q * G + h) * stride]);
+                for (int q = 0; q < nsplit; ++q) mm = fmaxf(mm, scr[((size_t)q * gh + h) * stride]);
                 float ll = 0.f, a0 = 0.f, a1 = 0.f;
                 for (int q = 0; q < nsplit; ++q) {
-                    const float *r = scr + ((size_t)q * G + h) * stride;
+                    const float *r = scr + ((size_t)q * gh + h) * stride;
                     const float c = r[0] == -INFINITY ? 0.f : __expf(r[0] - mm);  // a split without positions
                     ll = fmaf(r[1], c, ll);
                     a0 = fmaf(r[4 + e], c, a0);
                     a1 = fmaf(r[5 + e], c, a1);
                 }
-                put2(p, p.wl.o, (j * G + h) * hd + e, a0 / ll, a1 / ll, tag);
+                put2(p, p.wl.o, (j * G + hb + h) * hd + e, a0 / ll, a1 / ll, tag);
             }
         }
     }

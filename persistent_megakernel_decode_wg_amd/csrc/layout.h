@@ -153,7 +153,7 @@ struct WsLayout {
     uint64_t bar_global;
     uint64_t bar_group; // kGroups lines: arrival counters
     uint64_t bar_rel;   // kGroups lines: release epochs
-    uint64_t merge_cnt; // n_kv lines: attention split arrivals
+    uint64_t merge_cnt; // n_heads lines: attention split arrivals per merge group
     uint64_t x;         // [hidden] residual stream
     uint64_t q;         // [n_heads * hd] rotated queries
     uint64_t k, v;      // [n_kv * hd] this step's rotated keys / values (fp32)

@@ -447,7 +447,7 @@ std::string build_plan(mbk_model *m) {
     W.bar_global = w; w += 256;
     W.bar_group = w; w += 256 * kGroups;
     W.bar_rel = w; w += 256 * kGroups;
-    W.merge_cnt = w; w += 256u * c.n_kv_heads;
+    W.merge_cnt = w; w += 256u * c.n_heads;   // one line per merge group (query head or KV head)
     // tagged activations: 8 bytes per entry
     W.x = w; w = align256(w + 8u * c.hidden);
     W.q = w; w = align256(w + 8u * Q);
