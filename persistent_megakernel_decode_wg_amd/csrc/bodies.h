@@ -178,8 +178,6 @@ MBK_DEV void lds_st_opaque(void *p, uint32_t v) {
 
 // Control words read by every lane of a wave: the value goes to a scalar
 // register, so the branches and loops that test it stay wave-uniform.
-// True when c holds in any lane of the wave (a wave-uniform condition).
-MBK_DEV bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 MBK_DEV uint32_t lds_ld(const uint32_t *p) { return __builtin_amdgcn_readfirstlane(*(volatile lds_u32 *)(lds_u32 *)p); }
 MBK_DEV u32x4 lds_ld16(const void *p) { return *(volatile lds_u32x4 *)(lds_u32x4 *)p; }
@@ -1197,44 +1195,19 @@ MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int 
 // Sum (max) over the slots of a wave: the lanes with the same lane % LP.
 // Inside a 16-lane row the slots are combined by rotating the row by 2, 4
 // and 8 lanes (each step doubles the slots covered), then rows by the lane
-// swaps.
-// LP known at compile time: only the steps needed.
-template <int LP> MBK_DEV float slot_sum_c(float v) {
+// swaps (only the steps LP needs).
+template <int LP> MBK_DEV float slot_sum(float v) {
     if constexpr (LP <= 1) v += dpp<0x121>(v);   // row_ror:1
     if constexpr (LP <= 2) v += dpp<0x122>(v);   // row_ror:2
     if constexpr (LP <= 4) v += dpp<0x124>(v);   // row_ror:4
     if constexpr (LP <= 8) v += dpp<0x128>(v);   // row_ror:8
     return xsum32(xsum16(v));
 }
-template <int LP> MBK_DEV float slot_max_c(float v) {
+template <int LP> MBK_DEV float slot_max(float v) {
     if constexpr (LP <= 1) v = fmaxf(v, dpp<0x121>(v));
     if constexpr (LP <= 2) v = fmaxf(v, dpp<0x122>(v));
     if constexpr (LP <= 4) v = fmaxf(v, dpp<0x124>(v));
     if constexpr (LP <= 8) v = fmaxf(v, dpp<0x128>(v));
-    return xmax32(xmax16(v));
-}
-
-// LP is wave-uniform: each step is computed and kept by a select (no branches).
-MBK_DEV float slot_sum(float v, int LP) {
-    float t = dpp<0x121>(v);   // row_ror:1
-    v = LP <= 1 ? v + t : v;
-    t = dpp<0x122>(v);         // row_ror:2
-    v = LP <= 2 ? v + t : v;
-    t = dpp<0x124>(v);         // row_ror:4
-    v = LP <= 4 ? v + t : v;
-    t = dpp<0x128>(v);         // row_ror:8
-    v = LP <= 8 ? v + t : v;
-    return xsum32(xsum16(v));
-}
-MBK_DEV float slot_max(float v, int LP) {
-    float t = dpp<0x121>(v);
-    v = LP <= 1 ? fmaxf(v, t) : v;
-    t = dpp<0x122>(v);
-    v = LP <= 2 ? fmaxf(v, t) : v;
-    t = dpp<0x124>(v);
-    v = LP <= 4 ? fmaxf(v, t) : v;
-    t = dpp<0x128>(v);
-    v = LP <= 8 ? fmaxf(v, t) : v;
     return xmax32(xmax16(v));
 }
 
@@ -1351,11 +1324,11 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         if (h >= nh) break;
-        const float mw = slot_max_c<LP>(M[h]);
+        const float mw = slot_max<LP>(M[h]);
         const float c = M[h] == -INFINITY ? 0.f : __expf(M[h] - mw);  // a slot without positions adds nothing
-        l[h] = slot_sum_c<LP>(l[h] * c);
+        l[h] = slot_sum<LP>(l[h] * c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum_c<LP>(acc[h][e] * c);
+        for (int e = 0; e < 8; ++e) acc[h][e] = slot_sum<LP>(acc[h][e] * c);
         if (slot == 0) {
             float *r = scr + ((size_t)cw * G + h) * stride;
             if (dl == 0) {
@@ -1539,11 +1512,11 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                         read_prog(ctl, rp.seen);
                         interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
                         switch (p.hd_shift) {  // head size 16, 32, 64 or 128
-                        case 4: attention_task<G, 2>(p, iv, ivi, T, lds, ctl, rp, sc); break;
-                        case 5: attention_task<G, 4>(p, iv, ivi, T, lds, ctl, rp, sc); break;
-                        case 6: attention_task<G, 8>(p, iv, ivi, T, lds, ctl, rp, sc); break;
-                        default: attention_task<G, 16>(p, iv, ivi, T, lds, ctl, rp, sc); break;
-                    }
+                            case 4: attention_task<G, 2>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                            case 5: attention_task<G, 4>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                            case 6: attention_task<G, 8>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                            default: attention_task<G, 16>(p, iv, ivi, T, lds, ctl, rp, sc); break;
+                        }
                     }
                     ++k;
                     if (T.flags & TASK_LAST) break;
