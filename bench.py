@@ -6,7 +6,8 @@ Workload: the SmolLM-135M-shaped decoder (30 layers, hidden 576, 9/3 heads of
 weights and a static 128-slot KV cache: the 64 prompt tokens are stepped at
 positions 0..63 (setup), then greedy steps run at positions 64..127 with the
 token fed back on the device (MBK_TOKEN_PREV), cycling over that range.
-One timed step = one cooperative launch = the whole decode step.
+One timed step = one launch of the persistent kernel (plain launch, one
+workgroup per compute unit) = the whole decode step.
 
 Prints ONE JSON line (rank 0).  `value` is tok/s over the K timed steps.
 `roofline.achieved` = algorithmic bytes per step / mean kernel duration from
@@ -217,7 +218,16 @@ def main():
         dec.check()
 
     if args.phase:
-        extra["phase"] = phase_breakdown(dec, wl, positions, logits, am, dump=args.phase_dump)
+        ph = phase_breakdown(dec, wl, positions, logits, am, dump=args.phase_dump)
+        extra["phase"] = ph
+        # the step as hops x (hand-over + body) against bytes / peak bandwidth
+        hops = sum(v["count_per_step"] for v in ph.values())
+        sync = sum(v["wait_us"] * v["count_per_step"] for v in ph.values())
+        body = sum(v["comp_us"] * v["count_per_step"] for v in ph.values())
+        extra["decomposition"] = {
+            "hops": hops, "handover_us_per_hop": round(sync / hops, 3), "body_us_per_hop": round(body / hops, 3),
+            "hops_x_handover_plus_body_us": round(sync + body, 1),
+            "bytes_over_peak_us": round(bytes_mean / (PEAK_HBM_GBS * 1e3), 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
