@@ -449,8 +449,8 @@ MBK_DEV int step_pos(const Params &p) {
 // and the step's position.  An allocation is placed at the current virtual
 // ring offset, or at the next multiple of the ring size if it would straddle
 // the ring's end.  A GEMV task's weights take at most half the ring (a
-// block longer than that goes in runs of one tile per compute wave, so the
-// ring holds several runs), an attention piece at most a third; a loader
+// block longer than that goes in runs of whole rounds of the compute waves
+// of at most a third of the ring), an attention piece at most a third; a loader
 // waiting for space only ever waits for allocations it has already issued,
 // which the compute waves consume and release.
 

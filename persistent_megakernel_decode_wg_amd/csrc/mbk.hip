@@ -377,11 +377,13 @@ std::string build_plan(mbk_model *m) {
                         P.task_list.push_back(Task{i, it, attn_task_item(it, P.max_splits, G, P.attn_hpi), 0});
                 } else {
                     const int b0 = block_begin(v.n_items, k, v.nwg), b1 = block_begin(v.n_items, k + 1, v.nwg);
-                    // a block longer than one run goes in runs of one tile per compute wave (where that
-                    // fits): the ring then holds several runs, and the bytes in flight are what the run
-                    // being computed leaves free
+                    // a block longer than one run goes in runs of whole rounds of the compute waves (a
+                    // multiple of kCW tiles, at least one round) of at most a third of the ring: the ring
+                    // then holds three runs or more, so the bytes in flight are what the run being
+                    // computed leaves free, and each run still gives every compute wave several tiles
                     int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
-                    if (per >= kCW && b1 - b0 > per) per = kCW;
+                    if (per >= kCW && b1 - b0 > per)
+                        per = std::max<int>(kCW, (int)(ring / 3 / ((size_t)kCW * v.mat.IT * kChunk)) * kCW);
                     for (int t = b0; t < b1; t += per)
                         P.task_list.push_back(Task{i, t, std::min(per, b1 - t), b1 << 8});
                 }

@@ -155,9 +155,19 @@ WORKLOADS: Dict[str, Workload] = {
 }
 WORKLOAD_ORDER: List[str] = list(WORKLOADS)
 
+# A measurement shape, not a parity workload: one SmolLM-1.7B-sized layer and a
+# 262,144-row tied vocabulary projection (1.07 GB of bf16), so a step is
+# dominated by the GEMV body streaming a packed matrix of more than 1 GB.
+MEASUREMENT_WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        Workload("stream-1l-v262144", 1, 2048, 32, 32, 64, 8192, 262144, 128, False, 1e-5, 1e4,
+                 n_prompt=8, kv_prefill=0, n_decode=64),
+    ]
+}
+
 
 def get(name: str) -> Workload:
-    return WORKLOADS[name]
+    return WORKLOADS[name] if name in WORKLOADS else MEASUREMENT_WORKLOADS[name]
 
 
 def _shape_key(w: Workload) -> str:
