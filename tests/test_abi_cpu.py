@@ -91,7 +91,7 @@ def test_no_device_is_reported_as_hip_error(L):
 
 
 @pytest.mark.parametrize("name", ["tiny-2L-h64-kv32", "smollm135m-kv128", "smollm135m-kv4096", "qwen2-0.5b-kv128",
-                                  "smollm1.7b-kv4096"])
+                                  "smollm1.7b-kv4096", "stream-1l-v262144"])
 def test_plan_fits_lds_and_ring_rules(name):
     """The host planner (no device: workgroups fixed) keeps every workgroup inside the 160 KiB of LDS, every
     GEMV task run within half the ring, every attention piece within a third, and the packed payload at
