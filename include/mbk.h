@@ -1,6 +1,6 @@
 /*
  * mbk.h -- C ABI of libmbk: one batch-1 decode step of a pre-norm Llama-style
- * decoder, run on an AMD MI355X (gfx950) as ONE persistent cooperative kernel.
+ * decoder, run on an AMD MI355X (gfx950) as ONE persistent kernel launch.
  *
  * What a step computes (MegaBake article, "What a megakernel is, and why
  * small models want one": per layer RMSNorm, Q/K/V projections, RoPE,
@@ -110,7 +110,8 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
  * writes fp32 logits[vocab] (if logits != NULL) and the greedy argmax
  * (lowest index among equal maxima) to argmax[0] (device int32).  Re-running
  * a step at the same pos overwrites slot pos before reading it.
- * One cooperative launch of one workgroup per CU. */
+ * One launch of one workgroup per CU (plain by default; see
+ * mbk_set_launch_mode). */
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream);
 
 /* Same bodies and results (bitwise), one kernel launch per interval

@@ -1165,10 +1165,12 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
 }
 
 // ---- attention ---------------------------------------------------------------------------------------
-// Decode attention for KV head j over the cached positions of one split, the
-// G query heads of the group packed together so each key and value is read
-// once (README mirror, "Current status": flash decoding, query heads sharing
-// a KV head packed at long context).  Lane (slot, dl) of a compute wave
+// Decode attention for KV head j over the cached positions of one split, for
+// one of its query heads (the default item) or for all G of them packed
+// together so each key and value is read once (README mirror, "Current
+// status": flash decoding, query heads sharing a KV head packed at long
+// context; the planner chooses, see the attention items rule in mbk.hip).
+// Lane (slot, dl) of a compute wave
 // takes one position per block and head dims dl*8 .. dl*8+7 (LP = hd/8
 // lanes per position); the compute waves take alternate blocks.  Positions
 // arrive in segments (the ring pieces, the last one extended by the position

@@ -3,8 +3,8 @@
 // Executors (MegaBake article, section "How a model gets in": phases grouped
 // into barrier intervals, a table-driven persistent loop that dispatches a
 // body per phase row):
-//   k_persistent  one cooperative launch, one workgroup per CU, walks the
-//                 static interval table; intervals hand activations over as
+//   k_persistent  one launch (plain by default, cooperative on request), one
+//                 workgroup per CU, walks the static interval table; intervals hand activations over as
 //                 tagged entries (dataflow), or -- in barrier mode -- close
 //                 with a counting grid barrier as in the article;
 //   k_interval    the same bodies, one launch per interval (the ablation).
