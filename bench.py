@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--phase-dump", default="", help="also save the raw phase-timer arrays (.npy) to this path")
     ap.add_argument("--attn-split", type=int, default=0, help="attention split size in positions (0: library default)")
     ap.add_argument("--no-other-mode", action="store_true", help="skip timing the other sync mode")
+    ap.add_argument("--cold", type=int, default=0, metavar="N",
+                    help="also time N steps each preceded by a 1 GiB device write (caches cold: extra.cold_us_per_token_p50)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -214,8 +216,28 @@ def main():
             torch.cuda.synchronize()
             extra[mode + "_us_per_token"] = round((time.perf_counter() - s0) / n * 1e6, 2)
         extra["ablation_launches_per_token"] = dec.num_intervals()
+        # what one launch boundary costs the ablation over the persistent kernel (the pages' per-kernel gap)
+        extra["ablation_graph_us_per_launch_over_persistent"] = round(
+            (extra["ablation_graph_us_per_token"] - extra["us_per_token_p50"]) / dec.num_intervals(), 3)
         extra["barrier_us"] = round(dec.barrier_bench(10000), 3)
         dec.check()
+
+    if args.cold:
+        # every timed step follows a 1 GiB write, which leaves neither the weights nor the KV cache in L2 or the
+        # last-level cache; the step alone is timed
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold = []
+        for i in range(args.cold):
+            flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dec.decode_step(MBK_TOKEN_PREV, positions(i), logits, am)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        dec.check()
+        del flush
+        extra["cold_us_per_token_p50"] = round(pct(cold, 0.5), 2)
 
     if args.phase:
         ph = phase_breakdown(dec, wl, positions, logits, am, dump=args.phase_dump)
