@@ -45,14 +45,19 @@ def _per_dispatch(path: str, counter: str):
 
 
 def _copy_kernel(vals, copy_kib: float):
-    """The dispatch series closest to the calibration copy (largest counter among non-decode kernels)."""
+    """The calibration copy: the largest dispatch of the runtime's device-to-device copy kernel (a same-type,
+    contiguous tensor copy goes through hipMemcpy), else the largest non-decode dispatch.  Other copies in the
+    same program (weight uploads, a KV prefix converted on the device) run through other kernels."""
     best = None
-    for name, v in vals.items():
-        if KERNEL in name:
-            continue
-        m = max(v)
-        if best is None or m > best[1]:
-            best = (name, m)
+    for prefer in (True, False):
+        for name, v in vals.items():
+            if KERNEL in name or (prefer and "copyBuffer" not in name):
+                continue
+            m = max(v)
+            if best is None or m > best[1]:
+                best = (name, m)
+        if best is not None:
+            return best
     return best
 
 
