@@ -147,6 +147,33 @@ def test_smollm135m_kv4096_packed_gqa_items():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib, mode
 
 
+def test_phase_timer_stamps(tiny):
+    """The phase timer: a workgroup with work in an interval stamps start <= inputs loaded <= body done; the
+    launch clears every workgroup's entries first (stale values never survive); the results are the same
+    bits as without the timer."""
+    import torch
+    wl = tiny.wl
+    tok = int(synth.prompt_tokens(wl)[0])
+    a, ia = tiny.gpu_step(tok, 0)
+    tr = tiny.dec.set_phase_trace(True)
+    try:
+        tr.fill_(-1)       # stale values: the launch clears this workgroup's entries first
+        b, ib = tiny.gpu_step(tok, 0)
+        torch.cuda.synchronize()
+        t = tr.cpu().numpy()
+    finally:
+        tiny.dec.set_phase_trace(False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and ia == ib
+    assert not (t == -1).any()
+    work = t[:, :, 1] > 0
+    assert work.any(axis=1).all(), "every interval has a working workgroup"
+    tw = t[work]
+    assert (tw[:, 0] > 0).all() and (tw[:, 0] <= tw[:, 1]).all() and (tw[:, 1] <= tw[:, 2]).all()
+    # no work: nothing stamped, or (only split items beyond this step's split count) start and done
+    idle = t[~work]
+    assert (((idle[:, 0] == 0) & (idle[:, 2] == 0)) | ((idle[:, 0] > 0) & (idle[:, 2] >= idle[:, 0]))).all()
+
+
 @pytest.mark.parametrize("mode", ["mega", "barrier"])
 def test_watchdog_expires_and_recovers(mode):
     """Workgroup 0 leaves the persistent kernel before interval 0 (host-set debug switch, tiny spin
