@@ -81,23 +81,49 @@ typedef struct {
 
 typedef struct mbk_model mbk_model; /* opaque host handle */
 
-/* Validates the shape and creates a handle. No device work. */
+/* Validates the shape and creates a handle. No device work.
+ * Passage: the MegaBake README mirror, "The compilation path" (strict
+ * compilation: a shape outside what the bodies handle is an error,
+ * MBK_ERR_UNSUPPORTED, not a fallback) and "Current status" (the limits it
+ * lists: bf16, static shapes, decode KV capacity <= 8,192).
+ * Errors: MBK_ERR_ARG (null pointer, a non-positive dimension, eps or theta,
+ * qkv_bias not 0/1), MBK_ERR_UNSUPPORTED (a shape outside the list above).
+ * *out receives a handle the caller releases with mbk_destroy. */
 int mbk_create(const mbk_config *cfg, mbk_model **out);
 
-/* Frees the handle only (never caller memory). NULL is a no-op. */
+/* Frees the handle only (never caller memory). NULL is a no-op.  Makes a HIP
+ * call only when the ablation's hipGraph was instantiated (it is destroyed
+ * here), so release handles before the process tears the HIP runtime down.
+ * Passage: none on the pages; this repository's host-side design. */
 void mbk_destroy(mbk_model *m);
 
 /* Packs the weights into the streaming layout the kernels read.
+ * Passage: none on the pages defines a packed layout (the article, "How a
+ * model gets in", step 3, has the GEMM body read weight tiles directly; the
+ * article's "What a megakernel is" fixes what is read: every weight once per
+ * token, ~269 MB for SmolLM-135M).  The layout is this repository's design.
  * dst == NULL: writes the required size to *dst_bytes and returns.
  * Otherwise packs device-to-device on `stream` into dst (>= *dst_bytes bytes,
  * 256-byte aligned); the handle keeps dst, which the caller keeps alive.
+ * src: bf16 device pointers, each 16-byte aligned, read only; the call
+ * synchronises `stream` before it returns, so src may be freed afterwards.
  * Every matrix is stored as tiles of RT rows in which each wave-wide 16-byte
- * load reads 1 KiB of contiguous memory; the packed payload is exactly
- * 2 bytes per parameter when no tile padding is needed (all the supported
- * leaderboard shapes).  Also builds the fp32 RoPE table inside dst. */
+ * load reads 1 KiB of contiguous memory.  The payload is 2 bytes per
+ * parameter plus the zero rows padding the last tile of a matrix and, where
+ * the planner widens a matrix with few tiles to one row per tile, zero
+ * input groups up to a multiple of 512 inputs (at most 15 % of that matrix:
+ * the Qwen2-0.5B-shaped output projection gains 14 %).  Also builds the fp32
+ * RoPE table and the schedule (interval table, task lists) inside dst.
+ * Errors: MBK_ERR_ARG (null or misaligned pointer), MBK_ERR_SIZE (dst too
+ * small), MBK_ERR_UNSUPPORTED (no schedule fits the device), MBK_ERR_HIP. */
 int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *dst_bytes, void *stream);
 
 /* Binds the KV cache and the workspace.
+ * Passage: the project site, "Integration & evaluation" (bounded contiguous
+ * decode KV state), and the README mirror, "Current status" (the kernel
+ * performs the KV-cache updates; decode KV capacity <= 8,192).  The
+ * workspace (tagged activations, barrier and merge counters) is this
+ * repository's design.
  * kv == NULL or ws == NULL: writes the required sizes and returns.
  * Otherwise zero-fills both on `stream` and keeps them.
  * KV layout: bf16 [n_layers][2 (K, V)][n_kv_heads][kv_capacity][head_dim],
@@ -106,7 +132,13 @@ int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *ds
 int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_bytes, void *stream);
 
 /* One decode step at position `pos` (0-based) for `token`, asynchronous on
- * `stream`: writes KV slot `pos` of every layer, attends positions 0..pos,
+ * `stream`.  Passage: the MegaBake article, "What a megakernel is, and why
+ * small models want one" (the per-layer operations, in order) and "How a
+ * model gets in" (one persistent launch walking a table of phases); the
+ * README mirror, "Current status" (embedding, final norm, vocabulary
+ * projection and KV update inside the kernel; flash-decoding attention); the
+ * project site, "Decode leaderboard" (batch 1, one token per call).
+ * Writes KV slot `pos` of every layer, attends positions 0..pos,
  * writes fp32 logits[vocab] (if logits != NULL) and the greedy argmax
  * (lowest index among equal maxima) to argmax[0] (device int32).  Re-running
  * a step at the same pos overwrites slot pos before reading it.
@@ -116,23 +148,38 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
 
 /* Same bodies and results (bitwise), one kernel launch per interval
  * (the per-operator ablation).  use_graph = 1 replays the launches as a
- * hipGraph instantiated once per handle. */
+ * hipGraph instantiated once per handle (re-instantiated when logits or
+ * argmax change).  Passage: the MegaBake article, "What a megakernel is, and
+ * why small models want one" (separate launches, and CUDA graphs that replay
+ * them with a small gap between kernels, as the alternative to one launch).
+ * Errors as mbk_decode_step. */
 int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax,
                              int32_t use_graph, void *stream);
 
 /* Synchronises `stream` and reports device-side errors (MBK_ERR_TIMEOUT
  * when a bounded wait expired; the KV/workspace must then be re-bound with
- * mbk_alloc_kv). */
+ * mbk_alloc_kv).  Passage: none on the pages (their barrier waits are
+ * unbounded); the bounded waits and this report are this repository's
+ * failure detection. */
 int mbk_check(mbk_model *m, void *stream);
 
 /* Grid-barrier microbenchmark: one cooperative launch running n barriers with
- * empty bodies; *us_per_barrier = (t(n) - t(0)) / n from HIP events. */
+ * empty bodies; *us_per_barrier = (t(n) - t(0)) / n from HIP events.
+ * Passage: the MegaBake article, "How a model gets in" (the counting grid
+ * barrier: one release-add per block, acquire loads until the count reaches
+ * (ordinal + 1) * workers) and the README mirror, "Current status" (its cost
+ * at 60 blocks).  Needs packed weights and a bound workspace (MBK_ERR_STATE);
+ * n > 0 (MBK_ERR_ARG). */
 int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier);
 
-/* Number of intervals (and ablation launches) per step: 5 per layer + 1. */
+/* Number of intervals (and ablation launches) per step: 5 per layer + 1.
+ * Passage: the MegaBake article, "What I ran, on a CPU" (intervals per layer
+ * after folding small producers into their consumers, plus the ones for the
+ * embedding and the vocabulary head); here the embedding is folded too. */
 int mbk_num_intervals(const mbk_model *m, int32_t *n);
 
-/* Test hook: limit every bounded wait to `spin_limit` polls (0 = default,
+/* Passage: none on the pages; a test hook of this repository.
+ * Test hook: limit every bounded wait to `spin_limit` polls (0 = default,
  * 2^22) and make workgroup `skip_wg` (-1 = none) of the persistent kernel
  * leave at interval `skip_interval` without running it, so a test can force
  * the watchdog from the host: the waits of the workgroups that need its
@@ -168,7 +215,9 @@ int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
  * mbk_set_workgroups); MBK_ERR_ARG for any other value. */
 int mbk_set_attention_items(mbk_model *m, int32_t heads_per_item);
 
-/* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps. */
+/* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps
+ * (the passages are given with the enum above).  MBK_ERR_ARG for any other
+ * value. */
 int mbk_set_sync_mode(mbk_model *m, int32_t mode);
 
 /* How mbk_decode_step launches the persistent kernel.  Every workgroup of it
@@ -180,24 +229,33 @@ int mbk_set_sync_mode(mbk_model *m, int32_t mode);
  * *   when that kernel ends; the bounded waits report MBK_ERR_TIMEOUT if that
  *   takes too long).
  * COOPERATIVE: a cooperative launch, which the runtime admits only when all
- *   workgroups can be resident; about 15 us more per step on MI355X. */
+ *   workgroups can be resident; about 15 us more per step on MI355X.
+ * Passage: the MegaBake article, "How a model gets in", step 6 (the plan is
+ * compiled into a single cooperative kernel); the plain launch is this
+ * repository's choice.  MBK_ERR_ARG for any other value. */
 enum { MBK_LAUNCH_PLAIN = 0, MBK_LAUNCH_COOPERATIVE = 1 };
 int mbk_set_launch_mode(mbk_model *m, int32_t mode);
 
-/* Number of workgroups of the persistent kernel (one per compute unit); n = 0
+/* Passage: the MegaBake article, "What a megakernel is" (one resident block
+ * per streaming multiprocessor working through a task list).
+ * Number of workgroups of the persistent kernel (one per compute unit); n = 0
  * (default) uses every compute unit of the current device.  Only before the
  * schedule is planned (the first mbk_pack_weights / mbk_alloc_kv /
  * mbk_describe); a launch on a device with fewer compute units fails with
  * MBK_ERR_UNSUPPORTED.  With n > 0 the handle plans without touching a device. */
 int mbk_set_workgroups(mbk_model *m, int32_t n);
 
-/* Plans the schedule if needed and writes a NUL-terminated JSON summary of it
+/* Passage: none on the pages; this repository's introspection of its plan.
+ * Plans the schedule if needed and writes a NUL-terminated JSON summary of it
  * (workgroups, threads, waves per role, intervals, packed/workspace/LDS/ring
  * bytes, task counts and sizes, attention splits and piece size) into buf.
  * MBK_ERR_SIZE if len is too small. */
 int mbk_describe(mbk_model *m, char *buf, size_t len);
 
-/* Message for the last non-zero status returned on this thread. */
+/* Message for the last non-zero status returned on this thread (valid
+ * until the next failing call on the thread).  Passage: none on the pages;
+ * the README mirror, "The compilation path", asks for errors rather than
+ * silent fallbacks, and this carries their text. */
 const char *mbk_last_error(void);
 
 #ifdef __cplusplus

@@ -1,8 +1,11 @@
 """ctypes binding with the same names as the C ABI in include/mbk.h."""
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from typing import Dict, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,8 +98,31 @@ def make_config(wl) -> mbk_config:
                       wl.kv_capacity, int(wl.qkv_bias), wl.rms_eps, wl.rope_theta)
 
 
+# Handles still open when the interpreter exits are closed by an atexit hook, which runs before the HIP
+# runtime's own exit-time teardown; after it no handle makes a library (and so HIP) call, so nothing
+# reaches HIP from a finalizer or garbage collection during interpreter shutdown.
+_live = weakref.WeakSet()
+_shutting_down = False
+
+
+def _close_all() -> None:
+    global _shutting_down
+    for d in list(_live):
+        try:
+            d.close()
+        except Exception:
+            pass
+    _shutting_down = True
+
+
+atexit.register(_close_all)
+
+
 class Decoder:
-    """One handle: packed weights, KV cache and workspace (torch tensors), decode steps."""
+    """One handle: packed weights, KV cache and workspace (torch tensors), decode steps.
+
+    Call close() when done (or let the atexit hook do it); the destructor closes only while the
+    interpreter is not shutting down."""
 
     def __init__(self, cfg):
         self.cfg = cfg
@@ -106,13 +132,16 @@ class Decoder:
         self.h = h
         self.packed = self.kv = self.ws = None
         self._keep = []
+        _live.add(self)
 
     def close(self):
-        if getattr(self, "h", None):
+        if getattr(self, "h", None) and not _shutting_down:
             lib().mbk_destroy(self.h)
-            self.h = None
+        self.h = None
 
     def __del__(self):
+        if _shutting_down or sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

@@ -12,6 +12,10 @@ import synth
 # equal wherever the oracle's top-1/top-2 margin exceeds MARGIN.
 LOGIT_TOL = 2e-2
 MARGIN = 5e-2
+# The cache slot written by a step: every bf16 value within this many units in the last place of the
+# oracle's (both round a float to bf16; the two floats differ by far less than one bf16 step, so the
+# roundings can land on neighbouring values but no further apart).
+KV_ULP = 1
 
 
 def log(msg: str) -> None:
@@ -27,6 +31,16 @@ def to_dev(a):
 def upload(W):
     return {"embed": to_dev(W["embed"]), "final_norm": to_dev(W["final_norm"]),
             "layers": [{k: to_dev(v) for k, v in L.items()} for L in W["layers"]]}
+
+
+def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 steps between two arrays of bf16 bit patterns (sign-magnitude mapped onto a
+    line, so +0 and -0 are 0 apart)."""
+    def line(u):
+        u = np.asarray(u, dtype=np.uint16).astype(np.int32)
+        mag = u & 0x7FFF
+        return np.where(u & 0x8000, -mag, mag)
+    return np.abs(line(a) - line(b))
 
 
 class Pair:
@@ -52,12 +66,22 @@ class Pair:
             self.ref.prefill_kv(kv_prefix)
         self.logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
         self.am = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.kv_slot = None
         torch.cuda.synchronize()
 
-    def gpu_step(self, token, pos, mode="mega"):
+    def close(self):
+        """Releases the handle (no HIP call is left for interpreter exit)."""
+        if self.dec is not None:
+            self.dec.close()
+            self.dec = None
+
+    def gpu_step(self, token, pos, mode="mega", kv_check=False):
         """mode: mega (persistent kernel, dataflow), cooperative (the same, cooperative launch),
         barrier (persistent kernel, grid barriers), ablation (one launch per interval) or graph
-        (the ablation replayed as a hipGraph)."""
+        (the ablation replayed as a hipGraph).  kv_check: assert that the step changed no cache slot
+        but `pos` and keep that slot (bf16 bits [NL][2][nkv][hd]) in self.kv_slot."""
+        import torch
+        before = self.dec.kv.clone() if kv_check else None
         if mode == "mega":
             self.dec.decode_step(token, pos, self.logits, self.am)
         elif mode == "cooperative":
@@ -77,32 +101,71 @@ class Pair:
         else:
             self.dec.decode_step_ablation(token, pos, self.logits, self.am, use_graph=True)
         self.dec.check()
+        if kv_check:
+            after = self.dec.kv
+            self.kv_slot = after[:, :, :, pos, :].cpu().numpy().view(np.uint16).copy()
+            a = after.clone()
+            a[:, :, :, pos, :] = 0
+            before[:, :, :, pos, :] = 0
+            assert torch.equal(a, before), "pos %d: the step changed cache slots other than its own" % pos
+            del a, before
         return self.logits.cpu().numpy().copy(), int(self.am.item())
+
+    def check_kv_slot(self, pos, label=""):
+        """The slot the last kv_check step wrote, every layer, K and V, against the oracle's cache."""
+        want = self.ref.kv[:, :, :, pos, :]
+        d = bf16_ulp_distance(self.kv_slot, want)
+        worst = int(d.max())
+        if worst > KV_ULP:
+            l, c, j, e = np.unravel_index(int(d.argmax()), d.shape)
+            raise AssertionError("%s pos %d: cache slot differs by %d bf16 steps at layer %d %s head %d dim %d"
+                                 % (label, pos, worst, l, "KV"[c], j, e))
+        return worst
 
 
 def compare(lg, am, lo, ao):
-    """Returns (max|dlogit| / std, margin, argmax_ok)."""
+    """Checks one step's logits and argmax against the oracle; returns (max|dlogit| / std, margin).
+
+    * the GPU argmax is the lowest index attaining the maximum of the GPU's own logits (index work:
+      exact at every step);
+    * where the oracle's top-1/top-2 margin exceeds MARGIN it is the oracle's argmax;
+    * elsewhere it is one of the oracle's near-ties: its oracle logit lies within the two-sided logit
+      tolerance (2 * LOGIT_TOL * std) of the oracle's maximum.
+    """
     lo64 = lo.astype(np.float64)
     std = float(lo64.std())
     err = float(np.max(np.abs(lg.astype(np.float64) - lo64)))
     top = np.sort(lo64)[-2:]
     margin = float(top[1] - top[0])
-    return err / std, margin, (am == ao) or margin <= MARGIN
+    own = int(np.argmax(lg))   # numpy returns the first (lowest) index among equal maxima
+    assert am == own, "GPU argmax %d is not the lowest-index maximum %d of the GPU's own logits" % (am, own)
+    if margin > MARGIN:
+        assert am == ao, "argmax %d != oracle %d with margin %.3g" % (am, ao, margin)
+    else:
+        assert lo64[am] >= top[1] - 2 * LOGIT_TOL * std, (
+            "low-margin step: GPU argmax %d has oracle logit %.5g, below the oracle maximum %.5g by more than "
+            "2 * %.3g * std" % (am, lo64[am], top[1], LOGIT_TOL))
+    return err / std, margin
 
 
-def teacher_forced(pair: Pair, positions, first_tokens, mode="mega", check_every=1, label=""):
-    """Runs both sides over `positions`, feeding the GPU the oracle's tokens. Returns worst err/std."""
+def teacher_forced(pair: Pair, positions, first_tokens, mode="mega", check_every=1, label="", kv_check=True):
+    """Runs both sides over `positions`, feeding the GPU the oracle's tokens. Every step at index
+    i % check_every == 0, and the last one, compares logits, argmax and (kv_check) the cache slot the
+    step wrote. Returns the worst max|dlogit|/std."""
     worst = 0.0
     tok = None
+    n = len(positions)
     for i, pos in enumerate(positions):
         t_in = int(first_tokens[i]) if i < len(first_tokens) else tok
-        lg, am = pair.gpu_step(t_in, pos, mode)
+        checked = i % check_every == 0 or i == n - 1
+        lg, am = pair.gpu_step(t_in, pos, mode, kv_check=kv_check and checked)
         lo, ao, _ = pair.ref.step(t_in, pos)
-        if i % check_every == 0 or i == len(positions) - 1:
-            rel, margin, ok = compare(lg, am, lo, ao)
-            worst = max(worst, rel)
+        if checked:
             assert np.all(np.isfinite(lg)), "%s pos %d: non-finite logits" % (label, pos)
+            rel, margin = compare(lg, am, lo, ao)
+            worst = max(worst, rel)
             assert rel <= LOGIT_TOL, "%s pos %d: max|dlogit| = %.4g std > %.3g" % (label, pos, rel, LOGIT_TOL)
-            assert ok, "%s pos %d: argmax %d != oracle %d with margin %.3g" % (label, pos, am, ao, margin)
+            if kv_check:
+                pair.check_kv_slot(pos, label)
         tok = ao
     return worst
