@@ -12,10 +12,18 @@ import synth
 # equal wherever the oracle's top-1/top-2 margin exceeds MARGIN.
 LOGIT_TOL = 2e-2
 MARGIN = 5e-2
-# The cache slot written by a step: every bf16 value within this many units in the last place of the
-# oracle's (both round a float to bf16; the two floats differ by far less than one bf16 step, so the
-# roundings can land on neighbouring values but no further apart).
-KV_ULP = 1
+# The cache slot written by a step, checked per layer and per K / V:
+#  * layer 0 reads the same input on both sides (the embedding row), so there every bf16 entry lies within
+#    one bf16 step (of the larger magnitude) plus KV_REL times the RMS of the layer's key (or value) vector
+#    of the oracle's: both sides round an fp32 value to bf16, and those values differ by the GPU's own
+#    arithmetic (its ~16-bit input representation, fp32 accumulation order), which in entries much smaller
+#    than the RMS (cancellation) can exceed the entry's own bf16 step;
+#  * every layer's key and value vectors lie within LOGIT_TOL of the oracle's in relative L2 norm.  From
+#    layer 1 on the inputs differ by what earlier layers carried forward: bf16 cache roundings that land on
+#    neighbouring values move later layers by far more than their own rounding.  An emulation of the GPU's
+#    input representation on the CPU (SmolLM-135M shape, positions 0..23) stays at <= 3.1e-3; a wrong
+#    rotation pair or sign, head, slot or bias moves a vector by a sizeable fraction of its norm.
+KV_REL = 2.0 ** -10
 
 
 def log(msg: str) -> None:
@@ -33,14 +41,21 @@ def upload(W):
             "layers": [{k: to_dev(v) for k, v in L.items()} for L in W["layers"]]}
 
 
-def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """Distance in bf16 steps between two arrays of bf16 bit patterns (sign-magnitude mapped onto a
-    line, so +0 and -0 are 0 apart)."""
-    def line(u):
-        u = np.asarray(u, dtype=np.uint16).astype(np.int32)
-        mag = u & 0x7FFF
-        return np.where(u & 0x8000, -mag, mag)
-    return np.abs(line(a) - line(b))
+def bf16_step(m: np.ndarray) -> np.ndarray:
+    """The spacing of bf16 values at magnitude m (8 significant bits)."""
+    m = np.maximum(np.abs(m), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(m)) - 7)
+
+
+def kv_slot_check(gpu: np.ndarray, want: np.ndarray):
+    """For bf16 bit patterns [NL][2][nkv][hd]: (layer-0 |gpu - want| / (bf16 step + KV_REL * rms) per entry
+    [2][nkv][hd], relative L2 difference per layer and K/V [NL][2])."""
+    a = synth.bf16_to_f32(gpu).astype(np.float64)
+    b = synth.bf16_to_f32(want).astype(np.float64)
+    rms = np.sqrt(np.mean(b * b, axis=(2, 3), keepdims=True))
+    tol0 = bf16_step(np.maximum(np.abs(a[0]), np.abs(b[0]))) + KV_REL * rms[0]
+    rel = np.sqrt(np.sum((a - b) ** 2, axis=(2, 3)) / np.maximum(np.sum(b * b, axis=(2, 3)), 1e-300))
+    return np.abs(a[0] - b[0]) / tol0, rel
 
 
 class Pair:
@@ -112,15 +127,20 @@ class Pair:
         return self.logits.cpu().numpy().copy(), int(self.am.item())
 
     def check_kv_slot(self, pos, label=""):
-        """The slot the last kv_check step wrote, every layer, K and V, against the oracle's cache."""
+        """The slot the last kv_check step wrote, every layer, K and V, against the oracle's cache.
+        Returns (layer-0 worst |difference| / tolerance, worst relative L2 difference over the layers)."""
         want = self.ref.kv[:, :, :, pos, :]
-        d = bf16_ulp_distance(self.kv_slot, want)
-        worst = int(d.max())
-        if worst > KV_ULP:
-            l, c, j, e = np.unravel_index(int(d.argmax()), d.shape)
-            raise AssertionError("%s pos %d: cache slot differs by %d bf16 steps at layer %d %s head %d dim %d"
-                                 % (label, pos, worst, l, "KV"[c], j, e))
-        return worst
+        x0, rel = kv_slot_check(self.kv_slot, want)
+        if x0.max() > 1.0:
+            c, j, e = np.unravel_index(int(x0.argmax()), x0.shape)
+            g, o = synth.bf16_to_f32(self.kv_slot[0, c, j, e]), synth.bf16_to_f32(want[0, c, j, e])
+            raise AssertionError("%s pos %d: cache slot layer 0 %s head %d dim %d: GPU %.6g oracle %.6g (%.3g x the "
+                                 "tolerance)" % (label, pos, "KV"[c], j, e, g, o, x0.max()))
+        if rel.max() > LOGIT_TOL:
+            l, c = np.unravel_index(int(rel.argmax()), rel.shape)
+            raise AssertionError("%s pos %d: cache slot layer %d %s differs from the oracle's by %.3g in relative L2 "
+                                 "norm (> %.3g)" % (label, pos, l, "KV"[c], rel.max(), LOGIT_TOL))
+        return float(x0.max()), float(rel.max())
 
 
 def compare(lg, am, lo, ao):
@@ -152,7 +172,7 @@ def teacher_forced(pair: Pair, positions, first_tokens, mode="mega", check_every
     """Runs both sides over `positions`, feeding the GPU the oracle's tokens. Every step at index
     i % check_every == 0, and the last one, compares logits, argmax and (kv_check) the cache slot the
     step wrote. Returns the worst max|dlogit|/std."""
-    worst = 0.0
+    worst = kv0 = kvrel = 0.0
     tok = None
     n = len(positions)
     for i, pos in enumerate(positions):
@@ -166,6 +186,10 @@ def teacher_forced(pair: Pair, positions, first_tokens, mode="mega", check_every
             worst = max(worst, rel)
             assert rel <= LOGIT_TOL, "%s pos %d: max|dlogit| = %.4g std > %.3g" % (label, pos, rel, LOGIT_TOL)
             if kv_check:
-                pair.check_kv_slot(pos, label)
+                x0, rel = pair.check_kv_slot(pos, label)
+                kv0, kvrel = max(kv0, x0), max(kvrel, rel)
         tok = ao
+    if kv_check:
+        log("%s: cache slots: layer 0 worst difference / tolerance %.3g; worst relative L2 over layers %.3g"
+            % (label, kv0, kvrel))
     return worst
