@@ -146,6 +146,27 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
  * mbk_set_launch_mode). */
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step of
+ * mbk_decode_step with the library's static scratch as its workspace, so no
+ * workspace is bound and nothing is allocated.  Same kernels and bitwise the
+ * same logits, argmax and cache contents as mbk_decode_step.
+ * kv: the caller's cache in the layout of mbk_alloc_kv (bf16
+ * [n_layers][2][n_kv_heads][kv_capacity][head_dim], 256-byte aligned),
+ * read and written at slot pos; mbk_alloc_kv is not needed.  Needs packed
+ * weights (MBK_ERR_STATE).  The scratch is a file-scope device array of
+ * 512 KiB; each GPU the library runs on holds its own copy until the process
+ * ends.  A shape whose workspace exceeds it is rejected with MBK_ERR_SIZE
+ * before anything runs (every shape up to the SmolLM-1.7B one fits: 296 KB).
+ * Every handle on a GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (two streams, two threads) race, and MBK_TOKEN_PREV reads the argmax of
+ * the last static step on the GPU, whichever handle ran it.  The scratch is
+ * cleared (by a kernel, not a memset) on first use and after mbk_check has
+ * reported MBK_ERR_TIMEOUT for it; its activation tags never repeat between
+ * clears.  Errors otherwise as mbk_decode_step. */
+int mbk_decode_step_static(mbk_model *m, void *kv, int32_t token, int32_t pos, float *logits, int32_t *argmax,
+                           void *stream);
+
 /* Same bodies and results (bitwise), one kernel launch per interval
  * (the per-operator ablation).  use_graph = 1 replays the launches as a
  * hipGraph instantiated once per handle (re-instantiated when logits or

@@ -60,6 +60,7 @@ def lib():
         L.mbk_alloc_kv.argtypes = [vp, vp, P(sz), vp, P(sz), vp]
         L.mbk_decode_step.argtypes = [vp, i32, i32, vp, vp, vp]
         L.mbk_decode_step_ablation.argtypes = [vp, i32, i32, vp, vp, i32, vp]
+        L.mbk_decode_step_static.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.mbk_check.argtypes = [vp, vp]
         L.mbk_barrier_bench.argtypes = [vp, i32, vp, P(ctypes.c_float)]
         L.mbk_num_intervals.argtypes = [vp, P(i32)]
@@ -74,7 +75,7 @@ def lib():
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
-                  "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
+                  "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
                   "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -200,6 +201,16 @@ class Decoder:
                                    ctypes.c_void_p(logits.data_ptr()) if logits is not None else None,
                                    ctypes.c_void_p(argmax.data_ptr()) if argmax is not None else None,
                                    _stream(stream)))
+        return logits, argmax
+
+    def decode_step_static(self, kv, token: int, pos: int, logits=None, argmax=None, stream=None):
+        """The step on the library's static scratch (no workspace): `kv` is a cache tensor in the layout of
+        alloc_kv(), which this call does not need."""
+        _chk(lib().mbk_decode_step_static(self.h, ctypes.c_void_p(kv.data_ptr()) if kv is not None else None,
+                                          int(token), int(pos),
+                                          ctypes.c_void_p(logits.data_ptr()) if logits is not None else None,
+                                          ctypes.c_void_p(argmax.data_ptr()) if argmax is not None else None,
+                                          _stream(stream)))
         return logits, argmax
 
     def decode_step_ablation(self, token: int, pos: int, logits=None, argmax=None, use_graph: bool = False,

@@ -81,8 +81,8 @@ struct Params {
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
     float inv_h;              // 1 / hidden
     int32_t token, pos;       // token < 0: previous device argmax
-    uint32_t seq;             // step number: tags of this step's activations
-    int32_t step_from_ws;     // 1: read token/pos/seq from the workspace (graph replay)
+    uint32_t tag0;            // tag of this step's interval 0; interval i writes tag0 + i (nonzero)
+    int32_t step_from_ws;     // 1: read token/pos/tag0 from the workspace (graph replay)
     int32_t barrier;          // 1: counting grid barrier between intervals
     uint32_t epoch_base;      // grid barriers completed on this workspace before the call
     int32_t spin_limit, skip_wg, skip_interval;
@@ -205,15 +205,15 @@ MBK_DEV void stamp(const Params &p, uint8_t *lds, int ivi, int k) {
 
 // ---- tagged activations --------------------------------------------------------------------------
 
-MBK_DEV uint32_t step_seq(const Params &p) {
-    return p.step_from_ws ? ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 5) : p.seq;
+MBK_DEV uint32_t step_tag0(const Params &p) {
+    return p.step_from_ws ? ldc_uni(ws_ptr<uint32_t>(p, p.wl.ctrl) + 5) : p.tag0;
 }
 
-// Tag of what interval ivi writes during step seq.  Nonzero (a zeroed
-// workspace never matches) as the host keeps seq * n_intervals in range.
-MBK_DEV uint32_t tag_of(const Params &p, uint32_t seq, int ivi) {
-    return seq * (uint32_t)p.n_intervals + (uint32_t)ivi + 1u;
-}
+// Tag of what interval ivi writes during the step whose interval 0 writes
+// tag0.  The host hands out tags so that they are nonzero (a zeroed
+// workspace never matches) and never repeat on one workspace before it is
+// cleared again.
+MBK_DEV uint32_t tag_of(uint32_t tag0, int ivi) { return tag0 + (uint32_t)ivi; }
 
 // Polling loops read memory that other workgroups write: the buffer loads
 // they use are not atomic, so without this compiler barrier between two
@@ -953,7 +953,7 @@ MBK_DEV float gemv_tile(const MatGeom &g, const uint8_t *wt, const float *xs) {
 struct StepCtx {
     int pos, token;
     StepSplit ss;    // this step's attention split
-    uint32_t seq;
+    uint32_t tag0;   // tag of this step's interval 0
     float rnorm;     // 1/rms of the interval's normalised input (1 when not normalised)
     uint32_t gen;    // compute-wave barrier generation
     uint64_t best;   // this lane's argmax key (LM head)
@@ -1083,7 +1083,7 @@ template <int G>
 MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, int ivi, uint8_t *lds, StepCtx &sc) {
     const int tid = threadIdx.x, nt = kCW * 64;
     float *xs = (float *)(lds + p.lds_xs + sc.in);
-    const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(p, sc.seq, iv.x_src);
+    const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(sc.tag0, iv.x_src);
     // groups past the input (padding of widened tiles) are zero
     for (int g = iv.mat.K / 8 + tid; g < iv.mat.IT * iv.mat.L; g += nt) {
         *(u32x4 *)(xs + 8 * g) = (u32x4){0u, 0u, 0u, 0u};
@@ -1108,9 +1108,9 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
                     poll1(p, p.wl.x, r, xtag, xres[r - r0]);
                 }
             }
-            if (iv.op == OP_O && p.merge_in_o) merge_input<G>(p, xs, tag_of(p, sc.seq, ivi - 1), sc.ss.nsplit, tid, nt);
-            else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(p, sc.seq, ivi - 1), p.nq * p.hd, tid, nt);
-            else plain_input(p, xs, p.wl.a, tag_of(p, sc.seq, ivi - 1), p.I, tid, nt);
+            if (iv.op == OP_O && p.merge_in_o) merge_input<G>(p, xs, tag_of(sc.tag0, ivi - 1), sc.ss.nsplit, tid, nt);
+            else if (iv.op == OP_O) plain_input(p, xs, p.wl.o, tag_of(sc.tag0, ivi - 1), p.nq * p.hd, tid, nt);
+            else plain_input(p, xs, p.wl.a, tag_of(sc.tag0, ivi - 1), p.I, tid, nt);
             return 0.f;
         }
         case OP_QKV: {
@@ -1143,7 +1143,7 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
     const int tid = threadIdx.x, nt = kCW * 64;
     const AttnItem it = attn_item(T);
     const int hd = p.hd, kg = hd >> 3, qg = it.nh * kg;
-    const uint32_t tag = tag_of(p, sc.seq, ivi - 1);
+    const uint32_t tag = tag_of(sc.tag0, ivi - 1);
     float *dst = (float *)(lds + p.lds_qkv + sc.in);
     for (int g = tid; g < qg + 2 * kg; g += nt) {
         float v[8];
@@ -1341,7 +1341,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
         }
     }
     cw_barrier(p, ctl, sc.gen);
-    const uint32_t tag = tag_of(p, sc.seq, ivi);
+    const uint32_t tag = tag_of(sc.tag0, ivi);
     if (cw == 0) {
         // log-sum-exp combination of the wave partials, one head dimension per lane (a wave without
         // positions has max -inf)
@@ -1503,7 +1503,7 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
         if (tiv == ivi) {
             const Interval iv = interval_at(p, lds, ivi);
             stamp(p, lds, ivi, 0);
-            const uint32_t tag = tag_of(p, sc.seq, ivi);
+            const uint32_t tag = tag_of(sc.tag0, ivi);
             if (iv.op == OP_ATTN) {
                 // items of the interval, each with its own inputs (an item that is not the interval's
                 // last ends with a compute-wave barrier)
@@ -1599,7 +1599,7 @@ MBK_DEV void run_step(const Params &p) {
         sc.pos = pos;
         sc.ss = step_split(p, pos);
         sc.token = step_token(p);
-        sc.seq = step_seq(p);
+        sc.tag0 = step_tag0(p);
         sc.rnorm = 1.f;
         sc.gen = 0;
         sc.best = 0;
@@ -1611,7 +1611,7 @@ MBK_DEV void run_step(const Params &p) {
             uint32_t *ctrl = ws_ptr<uint32_t>(p, p.wl.ctrl);
             stc_u(ctrl + 3, (uint32_t)p.token);
             stc_u(ctrl + 4, (uint32_t)p.pos);
-            stc_u(ctrl + 5, p.seq);
+            stc_u(ctrl + 5, p.tag0);
         }
         if (!compute<G>(p, lds, ctl, nt, sc)) lds_st(&ctl.abort, 1u);
     }

@@ -148,7 +148,7 @@ MBK_HD int participant(const Interval &iv, int w, int n_wg) {
 // value, so a reader polls for exactly the version it needs.
 struct WsLayout {
     uint64_t ctrl;      // [0] error flag, [1] previous argmax token, [2] LM-head arrivals,
-                        // [3] token, [4] pos, [5] step sequence (for launches reading them here)
+                        // [3] token, [4] pos, [5] the step's first tag (for launches reading them here)
     uint64_t argkey;    // u64 argmax key
     uint64_t bar_global;
     uint64_t bar_group; // kGroups lines: arrival counters

@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cstdarg>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -78,6 +79,21 @@ __global__ void k_pack(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16
     }
 }
 
+// ---- the workspace of callers that cannot allocate ----------------------------------------------------
+// mbk_decode_step_static runs the step with this array as its workspace.  Every device holds its own
+// copy until the process ends; host code reaches it only through the device address that
+// hipGetSymbolAddress returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kStaticScratchBytes = 512u << 10;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Clears n bytes (a multiple of 16) at p.  A kernel rather than a memset node, so a caller may capture
+// the call into a graph.
+__global__ void k_zero16(uint8_t *p, uint64_t n) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 16u;
+    for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16u; i < n; i += stride)
+        *(u32x4 *)(p + i) = (u32x4){0u, 0u, 0u, 0u};
+}
+
 // ---- host side --------------------------------------------------------------------------------------
 
 namespace {
@@ -121,6 +137,16 @@ struct Plan {
     WsLayout ws{};
 };
 
+// State of one device's static scratch, shared by every handle that runs mbk_decode_step_static there.
+struct StaticScratch {
+    uint8_t *ptr = nullptr;   // device address of this device's `scratch`
+    uint32_t next_tag = 1;    // first tag of the next step run on it (tags never repeat until it is cleared)
+    uint32_t epoch = 0;       // grid barriers completed on it
+    bool clean = false;       // cleared since first use and since the last error mbk_check saw
+};
+std::mutex g_static_mu;
+std::vector<StaticScratch> g_static;   // by device index
+
 }  // namespace
 
 struct mbk_model {
@@ -134,7 +160,7 @@ struct mbk_model {
     uint16_t *kv = nullptr;
     uint8_t *ws = nullptr;
     uint32_t epoch = 0;   // grid barriers completed on the bound workspace
-    uint32_t seq = 0;     // decode steps run on the bound workspace (activation tags)
+    uint32_t seq = 0;     // decode steps run on the bound workspace (their tags: seq * intervals + 1 on)
     int32_t sync_mode = MBK_SYNC_DATAFLOW;
     int32_t launch_mode = MBK_LAUNCH_PLAIN;
     int32_t spin_limit = 1 << 22, skip_wg = -1, skip_interval = -1;
@@ -149,6 +175,7 @@ struct mbk_model {
     hipGraphNode_t node0 = nullptr;
     float *g_logits = nullptr;
     int32_t *g_argmax = nullptr;
+    int static_dev = -1;   // device whose static scratch this handle last stepped on (mbk_check reads it)
 };
 
 namespace {
@@ -487,7 +514,8 @@ int ensure_plan(mbk_model *m) {
     return MBK_OK;
 }
 
-// Next step number: tags seq * n_intervals + i + 1 must stay below 2^32.
+// Next step number on the bound workspace: its tags seq * n_intervals + 1 + i
+// must stay below 2^32.
 uint32_t next_seq(mbk_model *m) {
     const uint32_t n = (uint32_t)m->plan.iv.size();
     m->seq = (m->seq + 1u >= 0xffffffffu / n - 1u) ? 1u : m->seq + 1u;
@@ -551,7 +579,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.inv_h = 1.0f / (float)c.hidden;
     p.token = token;
     p.pos = pos;
-    p.seq = m->seq;
+    p.tag0 = m->seq * (uint32_t)P.iv.size() + 1u;
     p.step_from_ws = 0;
     p.barrier = m->sync_mode == MBK_SYNC_BARRIER;
     p.epoch_base = m->epoch;
@@ -574,6 +602,20 @@ int check_step_args(const mbk_model *m, int32_t token, int32_t pos, const int32_
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// One launch of the persistent kernel for p, as the handle's launch mode says.
+int launch_persistent(const mbk_model *m, Params &p, void *stream) {
+    if (m->launch_mode == MBK_LAUNCH_COOPERATIVE) {
+        void *args[] = {&p};
+        HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
+                                          (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
+    } else {
+        hipLaunchKernelGGL(kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), (unsigned)m->plan.lds_bytes,
+                           (hipStream_t)stream, p);
+        HIPCHK(hipGetLastError());
+    }
+    return MBK_OK;
+}
 
 int pack_matrix(mbk_model *m, const MatGeom &g, const void *s0, const void *s1, const void *s2, hipStream_t st) {
     const int hd = m->c.head_dim;
@@ -730,16 +772,56 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
     if (rc || (rc = ensure_kernels(m))) return rc;
     next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
-    if (m->launch_mode == MBK_LAUNCH_COOPERATIVE) {
-        void *args[] = {&p};
-        HIPCHK(hipLaunchCooperativeKernel((const void *)kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), args,
-                                          (unsigned)m->plan.lds_bytes, (hipStream_t)stream));
-    } else {
-        hipLaunchKernelGGL(kPersistent[p.gqa - 1], dim3(m->n_wg), dim3(kThreads), (unsigned)m->plan.lds_bytes,
-                           (hipStream_t)stream, p);
-        HIPCHK(hipGetLastError());
-    }
+    if ((rc = launch_persistent(m, p, stream))) return rc;
     if (p.barrier) m->epoch += (uint32_t)(p.n_intervals - 1);
+    return MBK_OK;
+}
+
+int mbk_decode_step_static(mbk_model *m, void *kv, int32_t token, int32_t pos, float *logits, int32_t *argmax,
+                           void *stream) {
+    if (!m) return fail(MBK_ERR_ARG, "null model");
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    if (m->plan.ws.total > kStaticScratchBytes)
+        return fail(MBK_ERR_SIZE, "this shape needs a %llu-byte workspace; the static scratch holds %zu bytes "
+                    "(use mbk_decode_step with a caller workspace)", (unsigned long long)m->plan.ws.total,
+                    kStaticScratchBytes);
+    if (!m->blob) return fail(MBK_ERR_STATE, "weights not packed");
+    if (!kv || !aligned(kv, 256)) return fail(MBK_ERR_ARG, "KV cache null or not 256-byte aligned");
+    if (!argmax) return fail(MBK_ERR_ARG, "argmax output is null");
+    if (token != MBK_TOKEN_PREV && (token < 0 || token >= m->c.vocab))
+        return fail(MBK_ERR_ARG, "token %d outside [0, %d)", token, m->c.vocab);
+    if (pos < 0 || pos >= m->c.kv_capacity) return fail(MBK_ERR_RANGE, "pos %d outside [0, %d)", pos, m->c.kv_capacity);
+    if ((rc = ensure_kernels(m))) return rc;
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if ((int)g_static.size() <= dev) g_static.resize((size_t)dev + 1);
+    StaticScratch &S = g_static[(size_t)dev];
+    if (!S.ptr) {
+        void *ptr = nullptr;
+        HIPCHK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        S.ptr = (uint8_t *)ptr;
+    }
+    const uint32_t n_iv = (uint32_t)m->plan.iv.size();
+    hipStream_t st = (hipStream_t)stream;
+    if (!S.clean || S.next_tag > 0xffffffffu - 2u * n_iv) {
+        // first use, an error seen by mbk_check, or tags about to wrap: start from a zeroed workspace
+        hipLaunchKernelGGL(k_zero16, dim3(128), dim3(256), 0, st, S.ptr, (uint64_t)kStaticScratchBytes);
+        HIPCHK(hipGetLastError());
+        S.next_tag = 1;
+        S.epoch = 0;
+        S.clean = true;
+    }
+    Params p = make_params(m, token, pos, logits, argmax);
+    p.kv = (uint16_t *)kv;
+    p.ws = S.ptr;
+    p.tag0 = S.next_tag;
+    p.epoch_base = S.epoch;
+    if ((rc = launch_persistent(m, p, stream))) return rc;
+    S.next_tag += n_iv;
+    if (p.barrier) S.epoch += n_iv - 1u;
+    m->static_dev = dev;
     return MBK_OK;
 }
 
@@ -804,6 +886,21 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
 int mbk_check(mbk_model *m, void *stream) {
     if (!m) return fail(MBK_ERR_ARG, "null model");
     HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+    if (m->static_dev >= 0) {
+        // the static scratch this handle last stepped on (its error word is the first word)
+        uint8_t *ptr = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(g_static_mu);
+            ptr = g_static[(size_t)m->static_dev].ptr;
+        }
+        uint32_t err = 0;
+        HIPCHK(hipMemcpy(&err, ptr + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));
+        if (err) {
+            std::lock_guard<std::mutex> lock(g_static_mu);
+            g_static[(size_t)m->static_dev].clean = false;   // the next static step clears it first
+            return fail(MBK_ERR_TIMEOUT, "a bounded device wait expired in a static-scratch step");
+        }
+    }
     if (!m->ws) return MBK_OK;
     uint32_t err = 0;
     HIPCHK(hipMemcpy(&err, m->ws + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));

@@ -150,3 +150,25 @@ def test_attention_items_policy():
     assert info["attention_heads_per_item"] == G and info["max_splits"] >= 1
     d.close()
 
+
+def test_static_scratch_step_rejects_oversized_workspace_and_checks_state(L):
+    """mbk_decode_step_static: a shape whose workspace exceeds the 512 KiB static scratch is a size error
+    before anything runs; a shape that fits but has no packed weights is a state error; every workload
+    of the repository fits."""
+    from persistent_megakernel_decode_wg_amd import Decoder, MBK_ERR_ARG, MBK_ERR_SIZE, MBK_ERR_STATE
+    am = ctypes.c_int32()
+    big = synth.get("smollm1.7b-kv4096").replace(hidden=4096, n_heads=64, n_kv_heads=64, head_dim=128,
+                                                 intermediate=8192, vocab=1024, n_layers=1)
+    d = Decoder(big)
+    d.set_workgroups(256)
+    assert d.describe()["workspace_bytes"] > 512 * 1024
+    assert L.mbk_decode_step_static(d.h, None, 0, 0, None, ctypes.byref(am), None) == MBK_ERR_SIZE
+    assert b"static scratch" in L.mbk_last_error()
+    d.close()
+    for name in synth.WORKLOAD_ORDER:
+        d = Decoder(synth.get(name))
+        d.set_workgroups(256)
+        assert d.describe()["workspace_bytes"] <= 512 * 1024, name
+        assert L.mbk_decode_step_static(d.h, None, 0, 0, None, ctypes.byref(am), None) == MBK_ERR_STATE
+        d.close()
+    assert L.mbk_decode_step_static(None, None, 0, 0, None, ctypes.byref(am), None) == MBK_ERR_ARG
