@@ -140,10 +140,12 @@ class Decoder:
             lib().mbk_destroy(self.h)
         self.h = None
 
-    def __del__(self):
-        if _shutting_down or sys.is_finalizing():
-            return
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # during interpreter teardown module globals may already be None: then (and once the atexit hook
+        # has run) nothing is called
         try:
+            if _shutting_down is not False or _finalizing():
+                return
             self.close()
         except Exception:
             pass
@@ -247,7 +249,7 @@ class Decoder:
 
     def describe(self) -> dict:
         import json
-        buf = ctypes.create_string_buffer(4096)
+        buf = ctypes.create_string_buffer(8192)
         _chk(lib().mbk_describe(self.h, buf, len(buf)))
         return json.loads(buf.value.decode())
 
