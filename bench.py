@@ -81,6 +81,101 @@ def pct(xs, q):
     return xs[min(len(xs) - 1, int(q * (len(xs) - 1) + 0.5))]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def setup_workload(wl, W=None):
+    """Packs the workload's seeded weights into a Decoder and runs its setup (the prompt stepped from position 0,
+    or the N(0,1) KV prefix and the step after it).  Returns (dec, W, logits, argmax, g0, g1): greedy positions
+    g0 .. g1 - 1 follow."""
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_megakernel_decode_wg_amd import Decoder
+    W = synth.make_weights(wl) if W is None else W
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    Wt = {"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
+          "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]}
+    dec = Decoder(wl)
+    dec.pack_weights(Wt)
+    del Wt
+    dec.alloc_kv()
+    logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    if wl.kv_prefill:
+        pre = synth.kv_prefill(wl)
+        dec.kv[:, :, :, :wl.kv_prefill, :] = torch.from_numpy(pre.view(np.int16)).cuda()
+        del pre
+        dec.decode_step(synth.first_token(wl), wl.kv_prefill, logits, am)
+        g0 = wl.kv_prefill + 1
+    else:
+        for p, t in enumerate(synth.prompt_tokens(wl)):
+            dec.decode_step(int(t), p, logits, am)
+        g0 = wl.greedy_start
+    dec.check()
+    return dec, W, logits, am, g0, wl.greedy_start + wl.n_decode
+
+
+def timed_steps(dec, positions, n, logits, am, stream, fn=None):
+    """Kernel time (us) of n steps at positions(i), each bracketed by HIP events on the launch stream."""
+    import torch
+    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV
+    fn = fn or (lambda pos: dec.decode_step(MBK_TOKEN_PREV, pos, logits, am))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(positions(i))
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec.check()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def config_summary(wl, steps: int = 64):
+    """One workload measured the way the headline is (its greedy positions, the token fed back on the device):
+    p50 us/token of the persistent kernel, its fraction of the 8 TB/s roofline, the same kernel with a grid
+    barrier after every interval, and the per-operator ablation (plain launches and hipGraph replay)."""
+    import torch
+    from persistent_megakernel_decode_wg_amd import MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV
+    dec, W, logits, am, g0, g1 = setup_workload(wl)
+    del W
+    stream = torch.cuda.current_stream()
+    span = g1 - g0
+    positions = lambda i: g0 + (i % span)
+    timed_steps(dec, positions, 8, logits, am, stream)
+    us = timed_steps(dec, positions, steps, logits, am, stream)
+    p50 = pct(us, 0.5)
+    nb = sum(algorithmic_bytes(wl, positions(i)) for i in range(steps)) / steps
+    dec.set_sync_mode(MBK_SYNC_BARRIER)
+    timed_steps(dec, positions, 4, logits, am, stream)
+    bar = pct(timed_steps(dec, positions, min(steps, 32), logits, am, stream), 0.5)
+    dec.set_sync_mode(MBK_SYNC_DATAFLOW)
+    abl = {}
+    for mode, use_graph in (("plain", False), ("graph", True)):
+        f = lambda pos: dec.decode_step_ablation(MBK_TOKEN_PREV, pos, logits, am, use_graph=use_graph)
+        timed_steps(dec, positions, 4, logits, am, stream, f)
+        abl[mode] = pct(timed_steps(dec, positions, min(steps, 32), logits, am, stream, f), 0.5)
+    dec.close()
+    del dec, logits, am
+    torch.cuda.empty_cache()
+    return {"us_per_token_p50": round(p50, 2), "tok_s": round(1e6 / p50, 1),
+            "roofline_frac": round(nb / (p50 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes_per_token": int(nb),
+            "positions": "%d-%d" % (positions(0), positions(steps - 1)) if steps <= span else "%d-%d cycled" % (g0, g1 - 1),
+            "barrier_mode_us_per_token": round(bar, 2), "ablation_plain_us_per_token": round(abl["plain"], 2),
+            "ablation_graph_us_per_token": round(abl["graph"], 2),
+            "faster_than_both_ablations": bool(p50 < abl["plain"] and p50 < abl["graph"])}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +193,8 @@ def main():
     ap.add_argument("--no-other-mode", action="store_true", help="skip timing the other sync mode")
     ap.add_argument("--cold", type=int, default=0, metavar="N",
                     help="also time N steps each preceded by a 1 GiB device write (caches cold: extra.cold_us_per_token_p50)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config summary of every workload (extra.configs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -116,33 +213,13 @@ def main():
     mbk_build.ensure_built()
     torch.cuda.set_device(0)
     wl = synth.get(args.workload)
-    W = synth.make_weights(wl)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
-    Wt = {"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
-          "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]}
-    dec = Decoder(wl)
-    dec.pack_weights(Wt)
-    dec.alloc_kv()
+    dec, W, logits, am, g0, g1 = setup_workload(wl)
     if args.attn_split:
         dec.set_attention_split(args.attn_split)
     sync_modes = {"dataflow": MBK_SYNC_DATAFLOW, "barrier": MBK_SYNC_BARRIER}
     dec.set_sync_mode(sync_modes[args.sync])
     stream = torch.cuda.current_stream()
-    logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
-    am = torch.empty(1, dtype=torch.int32, device="cuda")
-
-    # setup: prefill prompt (or the N(0,1) KV prefix) -> state at the first greedy position
-    if wl.kv_prefill:
-        pre = synth.kv_prefill(wl)
-        dec.kv[:, :, :, :wl.kv_prefill, :] = torch.from_numpy(pre.view(np.int16)).cuda()
-        dec.decode_step(synth.first_token(wl), wl.kv_prefill, logits, am)
-    else:
-        for p, t in enumerate(synth.prompt_tokens(wl)):
-            dec.decode_step(int(t), p, logits, am)
-    dec.check()
-    g0 = wl.greedy_start if not wl.kv_prefill else wl.kv_prefill + 1
-    g1 = wl.greedy_start + wl.n_decode          # exclusive
-    span = g1 - g0
+    span = g1 - g0                              # greedy positions g0 .. g1 - 1, cycled
     positions = lambda i: g0 + (i % span)
 
     for i in range(args.warmup):
@@ -206,15 +283,10 @@ def main():
 
     if not args.no_ablation:
         for mode, use_graph in (("ablation_plain", False), ("ablation_graph", True)):
-            n = min(K, 128)
-            for i in range(8):
-                dec.decode_step_ablation(MBK_TOKEN_PREV, positions(i), logits, am, use_graph=use_graph)
-            torch.cuda.synchronize()
-            s0 = time.perf_counter()
-            for i in range(n):
-                dec.decode_step_ablation(MBK_TOKEN_PREV, positions(i), logits, am, use_graph=use_graph)
-            torch.cuda.synchronize()
-            extra[mode + "_us_per_token"] = round((time.perf_counter() - s0) / n * 1e6, 2)
+            f = lambda pos: dec.decode_step_ablation(MBK_TOKEN_PREV, pos, logits, am, use_graph=use_graph)
+            timed_steps(dec, positions, 8, logits, am, stream, f)
+            us = timed_steps(dec, positions, min(K, 128), logits, am, stream, f)
+            extra[mode + "_us_per_token"] = round(pct(us, 0.5), 2)
         extra["ablation_launches_per_token"] = dec.num_intervals()
         # what one launch boundary costs the ablation over the persistent kernel (the pages' per-kernel gap)
         extra["ablation_graph_us_per_launch_over_persistent"] = round(
@@ -270,7 +342,9 @@ def main():
         cs = time.perf_counter() - c0
         cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "%d greedy steps at positions %d..%d after the %s setup, fp64-accumulating C oracle" % (
-                   n, g0, g0 + n - 1, "prefill" if wl.kv_prefill else "64-token prompt")}
+                   n, g0, g0 + n - 1, "prefill" if wl.kv_prefill else "64-token prompt"),
+               "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+        del ref
 
     # HBM bytes per launch from the committed counter summary, while it matches these kernel sources
     from persistent_megakernel_decode_wg_amd import profile_traffic
@@ -279,6 +353,16 @@ def main():
     if rec:
         extra["traffic_fetch_bytes"] = round(rec["fetch_bytes"])
         extra["traffic_write_bytes"] = round(rec["write_bytes"])
+    dec.close()
+    del dec, W, logits, am
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        # every workload, measured the same way (the headline one again, so the table is self-consistent)
+        extra["configs"] = {}
+        for name in synth.WORKLOAD_ORDER:
+            extra["configs"][name] = config_summary(synth.get(name))
+            print("config %s: %s" % (name, json.dumps(extra["configs"][name])), file=sys.stderr, flush=True)
+    timed = "%d-%d" % (g0, g0 + K - 1) if K <= span else "%d-%d cycled over %d steps" % (g0, g1 - 1, K)
     out = {
         "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",
         "value": round(K / elapsed, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -287,7 +371,7 @@ def main():
         "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": wl.n_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "intermediate": wl.intermediate,
                    "vocab": wl.vocab, "kv_capacity": wl.kv_capacity, "batch": 1,
-                   "positions": "%d-%d" % (g0, g1 - 1), "parallelism": "none (1 GPU)"},
+                   "positions": timed, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -295,7 +379,6 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
-    dec.close()
 
 
 if __name__ == "__main__":
