@@ -118,6 +118,28 @@ void mbk_destroy(mbk_model *m);
  * small), MBK_ERR_UNSUPPORTED (no schedule fits the device), MBK_ERR_HIP. */
 int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *dst_bytes, void *stream);
 
+/* Where one packed matrix sits in the blob of mbk_pack_weights, so callers
+ * (and tests) can read the packed layout.  Passage: none on the pages; this
+ * repository's layout.  A matrix of `rows` rows (in packed order) and `cols`
+ * inputs is stored as `tiles` tiles of rows_per_tile rows; each row's inputs
+ * are cut in 8-element groups spread over lanes_per_row = 64 / rows_per_tile
+ * lanes, and the 16-byte group of packed row t * rows_per_tile + l /
+ * lanes_per_row, group (l % lanes_per_row) + s * lanes_per_row sits at byte
+ * offset + ((t * steps + s) * 64 + l) * 16 (s < steps; groups from cols / 8
+ * on, and rows from `rows` on, are zero).  kind 0: packed row r is source row
+ * r; kind 1 (Q/K/V): rows [0, n_heads * head_dim) are queries, then keys, then
+ * values, and inside each query or key head packed rows 2m, 2m + 1 are head
+ * dims m, m + head_dim / 2; kind 2 (gate/up): packed row 2i is gate row i and
+ * 2i + 1 up row i.  which: 0 Q/K/V, 1 output projection, 2 gate/up, 3 down
+ * projection of `layer`; layer = -1, which = 0: the tied embedding.
+ * Errors: MBK_ERR_ARG (null pointer), MBK_ERR_RANGE (layer or which out of
+ * range), MBK_ERR_UNSUPPORTED / MBK_ERR_HIP as when planning. */
+typedef struct {
+    uint64_t offset;
+    int32_t rows, cols, lanes_per_row, rows_per_tile, steps, tiles, kind;
+} mbk_matrix_layout;
+int mbk_get_matrix_layout(mbk_model *m, int32_t layer, int32_t which, mbk_matrix_layout *out);
+
 /* Binds the KV cache and the workspace.
  * Passage: the project site, "Integration & evaluation" (bounded contiguous
  * decode KV state), and the README mirror, "Current status" (the kernel
@@ -192,6 +214,19 @@ int mbk_check(mbk_model *m, void *stream);
  * at 60 blocks).  Needs packed weights and a bound workspace (MBK_ERR_STATE);
  * n > 0 (MBK_ERR_ARG). */
 int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barrier);
+
+/* Grid-barrier validation: one cooperative launch running n rounds; in round
+ * i every workgroup writes i into its own epoch slot, passes the counting
+ * grid barrier, then reads every workgroup's slot, which must hold at least
+ * i.  first_bad (4 host int32): {round, reader workgroup, writer workgroup,
+ * value read} of the first failed check, round = 0 when every check of every
+ * round passed.  Passage: the MegaBake article, "How a model gets in" (the
+ * counting grid barrier whose correctness every interval relies on).  Needs
+ * packed weights and a bound workspace (MBK_ERR_STATE); n > 0
+ * (MBK_ERR_ARG); a barrier wait that expires gives MBK_ERR_TIMEOUT (the
+ * workspace must then be re-bound).  The debug hook's skip_wg makes that
+ * workgroup never arrive, to force the timeout from the host. */
+int mbk_barrier_stress(mbk_model *m, int32_t n, void *stream, int32_t *first_bad);
 
 /* Number of intervals (and ablation launches) per step: 5 per layer + 1.
  * Passage: the MegaBake article, "What I ran, on a CPU" (intervals per layer

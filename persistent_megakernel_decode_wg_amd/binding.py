@@ -41,15 +41,24 @@ class mbk_weights(ctypes.Structure):
                            "wdown")]
 
 
+class mbk_matrix_layout(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64)] + [(n, ctypes.c_int32) for n in (
+        "rows", "cols", "lanes_per_row", "rows_per_tile", "steps", "tiles", "kind")]
+
+
 _lib = None
 
 
 def lib():
-    """Load libmbk.so (built by __graft_entry__.build()); raises if it is missing."""
+    """Load libmbk.so (built by __graft_entry__.build()); raises if it is missing.
+
+    torch is imported first: its HIP runtime is then the one libmbk.so binds to (both name the same
+    runtime library), so the library and the tensors it is handed share one device context."""
     global _lib
     if _lib is None:
         if not os.path.exists(lib_path):
             raise RuntimeError("libmbk.so is not built (%s); run __graft_entry__.build()" % lib_path)
+        import torch  # noqa: F401  (loads the HIP runtime the library then shares)
         L = ctypes.CDLL(lib_path)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         P = ctypes.POINTER
@@ -63,6 +72,8 @@ def lib():
         L.mbk_decode_step_static.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.mbk_check.argtypes = [vp, vp]
         L.mbk_barrier_bench.argtypes = [vp, i32, vp, P(ctypes.c_float)]
+        L.mbk_barrier_stress.argtypes = [vp, i32, vp, P(i32)]
+        L.mbk_get_matrix_layout.argtypes = [vp, i32, i32, P(mbk_matrix_layout)]
         L.mbk_num_intervals.argtypes = [vp, P(i32)]
         L.mbk_set_debug.argtypes = [vp, i32, i32, i32]
         L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
@@ -75,7 +86,7 @@ def lib():
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
-                  "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
+                  "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_barrier_stress", "mbk_get_matrix_layout", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
                   "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -175,6 +186,12 @@ class Decoder:
         _chk(lib().mbk_pack_weights(self.h, ctypes.byref(w), ctypes.c_void_p(self.packed.data_ptr()),
                                     ctypes.byref(nbytes), _stream(stream)))
 
+    def matrix_layout(self, layer: int, which: int) -> dict:
+        """Layout of one packed matrix (include/mbk.h, mbk_get_matrix_layout) as a dict."""
+        g = mbk_matrix_layout()
+        _chk(lib().mbk_get_matrix_layout(self.h, int(layer), int(which), ctypes.byref(g)))
+        return {n: getattr(g, n) for n, _ in mbk_matrix_layout._fields_}
+
     def packed_bytes(self) -> int:
         nbytes = ctypes.c_size_t(0)
         _chk(lib().mbk_pack_weights(self.h, None, None, ctypes.byref(nbytes), None))
@@ -230,6 +247,13 @@ class Decoder:
         us = ctypes.c_float(0)
         _chk(lib().mbk_barrier_bench(self.h, int(n), _stream(stream), ctypes.byref(us)))
         return us.value
+
+    def barrier_stress(self, n: int, stream=None):
+        """Validated grid barriers: returns (round, reader, writer, value) of the first failed check, round 0
+        when all passed."""
+        out = (ctypes.c_int32 * 4)()
+        _chk(lib().mbk_barrier_stress(self.h, int(n), _stream(stream), out))
+        return tuple(out)
 
     def num_intervals(self) -> int:
         n = ctypes.c_int32(0)

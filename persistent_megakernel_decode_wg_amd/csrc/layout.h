@@ -160,6 +160,7 @@ struct WsLayout {
     uint64_t o;         // [n_heads * hd] attention output
     uint64_t a;         // [intermediate] silu(gate) * up
     uint64_t part;      // attention partials [n_kv][max_splits][g][hd + 4] (fp32)
+    uint64_t stress;    // grid-barrier validation: 4 result words, then one epoch slot per workgroup
     uint64_t total;
 };
 

@@ -58,6 +58,31 @@ __global__ __launch_bounds__(kThreads) void k_barrier_bench(Params p, int n) {
         if (!grid_barrier(p, p.epoch_base + (uint32_t)i + 1u)) return;
 }
 
+// Grid-barrier validation (the counting barrier of the article's executor): in round i every workgroup
+// writes i into its epoch slot, passes the barrier of epoch epoch_base + i, then reads every workgroup's
+// slot, which must hold at least i (the barrier orders every write of round i before every read after it).
+// The first failed check (lowest round) is recorded in res[0..3] = {round, reader, writer, value read};
+// no workgroup leaves a round early, so every barrier still completes.  A barrier that times out (the
+// bounded wait, reported through the error word) ends the workgroup's rounds.
+__global__ __launch_bounds__(kThreads) void k_barrier_stress(Params p, int n, uint32_t *res, uint32_t *slots) {
+    if ((int)blockIdx.x == p.skip_wg) return;   // test hook: this workgroup never arrives
+    for (int i = 1; i <= n; ++i) {
+        if (threadIdx.x == 0) stc_u(slots + blockIdx.x, (uint32_t)i);
+        if (!grid_barrier(p, p.epoch_base + (uint32_t)i)) return;
+        for (int w = threadIdx.x; w < p.n_wg; w += kThreads) {
+            const uint32_t v = ldc_u(slots + w);
+            if (v < (uint32_t)i) {
+                const uint32_t old = atomicMin(res, (uint32_t)i);
+                if (old > (uint32_t)i) {
+                    stc_u(res + 1, blockIdx.x);
+                    stc_u(res + 2, (uint32_t)w);
+                    stc_u(res + 3, v);
+                }
+            }
+        }
+    }
+}
+
 // Packer: one thread per 16-byte chunk of the packed matrix.
 __global__ void k_pack(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16_t *s1, const uint16_t *s2, int hd,
                        int nq_rows, int nkv_rows) {
@@ -489,6 +514,8 @@ std::string build_plan(mbk_model *m) {
     W.part = w;
     w = align256(w + std::max<uint64_t>(4u * (uint64_t)c.n_kv_heads * ms * G * stride,
                                         8u * (uint64_t)c.n_kv_heads * ms * G * (hd + 2)));
+    W.stress = w;
+    w = align256(w + 16u + 4u * (uint64_t)n_wg);
     W.total = w;
 
     // RoPE table: angle pos * theta^(-2i/hd), evaluated in double, stored fp32
@@ -970,6 +997,58 @@ int mbk_barrier_bench(mbk_model *m, int32_t n, void *stream, float *us_per_barri
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     *us_per_barrier = (t[1] - t[0]) * 1000.f / (float)n;
+    return MBK_OK;
+}
+
+int mbk_get_matrix_layout(mbk_model *m, int32_t layer, int32_t which, mbk_matrix_layout *out) {
+    if (!m || !out) return fail(MBK_ERR_ARG, "null argument");
+    int rc = ensure_plan(m);
+    if (rc) return rc;
+    const Plan &P = m->plan;
+    const MatGeom *g = nullptr;
+    if (layer == -1 && which == 0) g = &P.embed;
+    else if (layer >= 0 && layer < m->c.n_layers && which >= 0 && which < 4) {
+        const LayerPlan &L = P.layers[(size_t)layer];
+        g = which == 0 ? &L.qkv : which == 1 ? &L.o : which == 2 ? &L.gu : &L.down;
+    }
+    if (!g) return fail(MBK_ERR_RANGE, "no matrix (layer %d, which %d)", layer, which);
+    out->offset = g->off;
+    out->rows = g->rows;
+    out->cols = g->K;
+    out->lanes_per_row = g->L;
+    out->rows_per_tile = g->RT;
+    out->steps = g->IT;
+    out->tiles = g->ntiles;
+    out->kind = g->kind;
+    return MBK_OK;
+}
+
+int mbk_barrier_stress(mbk_model *m, int32_t n, void *stream, int32_t *first_bad) {
+    if (!m || !first_bad || n <= 0) return fail(MBK_ERR_ARG, "bad arguments");
+    if (!m->ws || !m->blob) return fail(MBK_ERR_STATE, "workspace not bound");
+    int rc = ensure_kernels(m);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *res = (uint32_t *)(m->ws + m->plan.ws.stress);
+    const uint32_t init[4] = {0xffffffffu, 0u, 0u, 0u};
+    HIPCHK(hipMemsetAsync(res + 4, 0, 4u * (size_t)m->n_wg, st));
+    HIPCHK(hipMemcpyAsync(res, init, sizeof init, hipMemcpyHostToDevice, st));
+    Params p = make_params(m, 0, 0, nullptr, nullptr);
+    int cnt = n;
+    uint32_t *slots = res + 4;
+    void *args[] = {&p, &cnt, &res, &slots};
+    HIPCHK(hipLaunchCooperativeKernel((const void *)k_barrier_stress, dim3(m->n_wg), dim3(kThreads), args, 0, st));
+    m->epoch += (uint32_t)n;
+    uint32_t out[4];
+    HIPCHK(hipMemcpyAsync(out, res, sizeof out, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    uint32_t err = 0;
+    HIPCHK(hipMemcpy(&err, m->ws + m->plan.ws.ctrl, 4, hipMemcpyDeviceToHost));
+    first_bad[0] = out[0] == 0xffffffffu ? 0 : (int32_t)out[0];
+    first_bad[1] = (int32_t)out[1];
+    first_bad[2] = (int32_t)out[2];
+    first_bad[3] = (int32_t)out[3];
+    if (err) return fail(MBK_ERR_TIMEOUT, "a grid barrier wait expired; re-bind KV/workspace");
     return MBK_OK;
 }
 
