@@ -168,6 +168,33 @@ int mbk_alloc_kv(mbk_model *m, void *kv, size_t *kv_bytes, void *ws, size_t *ws_
  * mbk_set_launch_mode). */
 int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int32_t *argmax, void *stream);
 
+/* Multi-token prefill: runs the decoder over the n_tokens prompt tokens at
+ * positions pos0 .. pos0 + n_tokens - 1 at once, writing their KV-cache slots
+ * (every layer), and the fp32 logits[vocab] (if logits != NULL) and greedy
+ * argmax (argmax[0], device int32) of the last position; a following
+ * mbk_decode_step with MBK_TOKEN_PREV continues from that argmax.  Equal, to
+ * rounding, to n_tokens decode steps at those positions.  The projections
+ * run as matrix-core GEMMs over the packed weights (activations as hi/lo bf16
+ * pairs, ~16 significant bits, fp32 accumulation); attention is causal over
+ * cache slots 0 .. pos0 + i for prompt position i, in fp32.  Passage: the
+ * MegaBake third-party article, "Where it breaks today" (prefill through the
+ * decode-shaped bodies is slow above ~64 tokens) and the project site, "Next"
+ * (fast long-prompt prefill).
+ * tokens: HOST array of n_tokens ids in [0, vocab) (copied before the call
+ * returns).  scratch: caller device buffer, 256-byte aligned, of at least
+ * mbk_prefill_scratch_bytes(n_tokens) bytes.  Needs packed weights and a
+ * bound KV cache (MBK_ERR_STATE).  Asynchronous on `stream`.
+ * Errors: MBK_ERR_ARG (null pointer, n_tokens < 1, a token out of range),
+ * MBK_ERR_RANGE (positions outside the cache), MBK_ERR_SIZE (scratch too
+ * small), MBK_ERR_HIP. */
+int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t pos0, void *scratch,
+                size_t scratch_bytes, float *logits, int32_t *argmax, void *stream);
+
+/* Scratch bytes mbk_prefill needs for n_tokens tokens (no device work).
+ * Passage: none on the pages; this repository's buffer contract.
+ * MBK_ERR_RANGE when n_tokens exceeds the cache. */
+int mbk_prefill_scratch_bytes(mbk_model *m, int32_t n_tokens, size_t *bytes);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the step of
  * mbk_decode_step with the library's static scratch as its workspace, so no

@@ -74,6 +74,8 @@ def lib():
         L.mbk_barrier_bench.argtypes = [vp, i32, vp, P(ctypes.c_float)]
         L.mbk_barrier_stress.argtypes = [vp, i32, vp, P(i32)]
         L.mbk_get_matrix_layout.argtypes = [vp, i32, i32, P(mbk_matrix_layout)]
+        L.mbk_prefill.argtypes = [vp, P(i32), i32, i32, vp, sz, vp, vp, vp]
+        L.mbk_prefill_scratch_bytes.argtypes = [vp, i32, P(sz)]
         L.mbk_num_intervals.argtypes = [vp, P(i32)]
         L.mbk_set_debug.argtypes = [vp, i32, i32, i32]
         L.mbk_set_phase_trace.argtypes = [vp, vp, sz]
@@ -86,7 +88,7 @@ def lib():
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
-                  "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_barrier_stress", "mbk_get_matrix_layout", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
+                  "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_barrier_stress", "mbk_get_matrix_layout", "mbk_prefill", "mbk_prefill_scratch_bytes", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
                   "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -221,6 +223,25 @@ class Decoder:
                                    ctypes.c_void_p(argmax.data_ptr()) if argmax is not None else None,
                                    _stream(stream)))
         return logits, argmax
+
+    def prefill_scratch_bytes(self, n_tokens: int) -> int:
+        n = ctypes.c_size_t(0)
+        _chk(lib().mbk_prefill_scratch_bytes(self.h, int(n_tokens), ctypes.byref(n)))
+        return n.value
+
+    def prefill(self, tokens, pos0: int = 0, logits=None, argmax=None, scratch=None, stream=None):
+        """Prompt tokens (a host sequence of ints) at positions pos0 .. pos0 + len - 1 in one call; logits and
+        argmax of the last position.  scratch: a uint8 device tensor of at least prefill_scratch_bytes(len)
+        bytes (allocated here when None)."""
+        import torch
+        toks = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        need = self.prefill_scratch_bytes(len(tokens))
+        if scratch is None or scratch.numel() < need:
+            scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+        _chk(lib().mbk_prefill(self.h, toks, len(tokens), int(pos0), ctypes.c_void_p(scratch.data_ptr()),
+                               scratch.numel(), ctypes.c_void_p(logits.data_ptr()) if logits is not None else None,
+                               ctypes.c_void_p(argmax.data_ptr()) if argmax is not None else None, _stream(stream)))
+        return scratch
 
     def decode_step_static(self, kv, token: int, pos: int, logits=None, argmax=None, stream=None):
         """The step on the library's static scratch (no workspace): `kv` is a cache tensor in the layout of

@@ -1,0 +1,286 @@
+// prefill.h -- multi-token prefill (gfx950): the decoder over P prompt positions at once, writing the same
+// KV cache the decode step reads and the logits / greedy argmax of the last position.
+//
+// At batch P the projections are dense contractions [P x K] x [K x N], so they run on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 takes, in every lane, 8 consecutive bf16 inputs of one row of each operand, which
+// is exactly one 16-byte group of the packed weight layout, so the GEMMs read the decode step's packed blob
+// in place.  Activations enter as hi/lo bf16 pairs (hi = bf16(x), lo = bf16(x - hi), two products per
+// tile), as in the decode step's dot products, so inputs carry ~16 significant bits and the products with
+// bf16 weights are exact in fp32.  Per layer: RMSNorm -> hi/lo; Q/K/V GEMM with bias, RoPE, the KV-cache
+// append of every position and the rotated queries; causal attention over the cache (fp32, online
+// softmax); output projection + residual; RMSNorm; gate/up GEMM with SiLU * up; down projection +
+// residual.  Then the final norm and the tied vocabulary projection of the last position, and its argmax.
+// (MegaBake third-party article, "Where it breaks today": prefill through the megakernel's decode-shaped
+// bodies is slow above ~64 tokens; project site, "Next": fast long-prompt prefill.)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace mbk {
+
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int pf_u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPfTileN = 64;    // packed rows per GEMM workgroup (4 waves x 16)
+constexpr int kPfTileP = 64;    // positions per GEMM workgroup (4 MFMA row blocks of 16)
+
+// Device buffers and shape of one prefill call (kernel argument, by value).
+struct PfParams {
+    const uint8_t *blob;     // packed weights (+ RoPE table)
+    uint16_t *kv;            // [NL][2][nkv][S][hd] bf16
+    const int32_t *tok;      // [P] token ids
+    float *x;                // [Pp][H] residual stream
+    float *q;                // [Pp][nq * hd] rotated queries
+    uint16_t *inh[2], *inl[2];  // GEMM inputs as hi/lo bf16 [Pp][ks] (two buffers, used in turn)
+    float *logits;           // [V]
+    int32_t *argmax_out;     // device int32
+    uint32_t *prev_token;    // the decode workspace's previous-argmax word, or null
+    MatGeom embed;
+    uint64_t rope;           // byte offset of the fp32 RoPE table [S][hd/2][2] in blob
+    int32_t P, Pp, ks, pos0;
+    int32_t H, nq, nkv, hd, I, V, S, gqa, hd_shift;
+    float eps, scale;
+};
+
+__device__ __forceinline__ float pf_bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t pf_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// dst[i] <- hi/lo of v[i] for the row's K entries; entries [K, ks) cleared (the GEMM's k tail reads them).
+__device__ __forceinline__ void pf_store_split(uint16_t *dh, uint16_t *dl, int i, float v) {
+    const uint16_t h = pf_to_bf16(v);
+    dh[i] = h;
+    dl[i] = pf_to_bf16(v - pf_bf16f(h));
+}
+
+// RMSNorm of x row r (or of the embedding row of its token when from_embed, which also sets x) times the
+// bf16 weight at norm_off, split into hi/lo row `dst_row` of input buffer `dst`.  One workgroup of 256
+// threads per row.
+__global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, int dst, int from_embed, int last_only) {
+    __shared__ float red[8];
+    const int r = last_only ? p.P - 1 : (int)blockIdx.x;
+    const int dst_row = last_only ? 0 : r;
+    float *xr = p.x + (size_t)r * p.H;
+    uint16_t *dh = p.inh[dst] + (size_t)dst_row * p.ks, *dl = p.inl[dst] + (size_t)dst_row * p.ks;
+    if (r >= p.P) {  // padding rows of the position tiles: zero inputs
+        for (int i = threadIdx.x; i < p.ks; i += 256) dh[i] = dl[i] = 0;
+        return;
+    }
+    if (from_embed) {
+        const int t = p.tok[r];
+        for (int i = threadIdx.x; i < p.H; i += 256) {
+            const uint16_t *e = (const uint16_t *)(p.blob + row_group_offset(p.embed, t, i >> 3));
+            xr[i] = pf_bf16f(e[i & 7]);
+        }
+        __syncthreads();
+    }
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < p.H; i += 256) ss += xr[i] * xr[i];
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float rn = rsqrtf(tot / (float)p.H + p.eps);
+    const uint16_t *w = (const uint16_t *)(p.blob + norm_off);
+    for (int i = threadIdx.x; i < p.ks; i += 256) {
+        if (i < p.H) pf_store_split(dh, dl, i, xr[i] * rn * pf_bf16f(w[i]));
+        else dh[i] = dl[i] = 0;
+    }
+    if (last_only) {
+        // rows 1 .. 15 of the vocabulary projection's position block
+        for (int i = threadIdx.x; i < 15 * p.ks; i += 256) {
+            p.inh[dst][p.ks + i] = 0;
+            p.inl[dst][p.ks + i] = 0;
+        }
+    }
+}
+
+// C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g: workgroup (bx, by) takes packed rows
+// [64 bx, 64 bx + 64) (wave w: 16 rows from 64 bx + 16 w) and positions [64 by, 64 by + 64) of the input
+// buffer `src` (np_rows rows in all).  Lane l feeds row l % 16 of each operand with input group
+// 4 s + l / 16 of step s and holds, after the k loop, C[pos0 + 4 (l / 16) + r][n] for the four r of each
+// position block.  Epilogue by op.
+template <int OP>
+__global__ __launch_bounds__(256) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
+                                                 uint64_t bias_off) {
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int n = blockIdx.x * kPfTileN + wv * 16 + (l & 15);
+    const int pb = blockIdx.y * kPfTileP;
+    const int nb = min(kPfTileP, np_rows - pb) >> 4;     // position blocks of 16 (np_rows is a multiple of 16)
+    const int kq = l >> 4, ngrp = g.K >> 3, nsteps = (ngrp + 3) >> 2;
+    const uint16_t *ah = p.inh[src], *al = p.inl[src];
+    pf_f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
+    const bool nrow = n < g.rows;
+    for (int s = 0; s < nsteps; ++s) {
+        const int kg = 4 * s + kq;
+        pf_u32x4 bw = {0u, 0u, 0u, 0u};
+        if (nrow && kg < ngrp) bw = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+        const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < nb) {
+                const size_t off = (size_t)(pb + 16 * j + (l & 15)) * p.ks + 8 * kg;
+                const pf_bf16x8 xh = __builtin_bit_cast(pf_bf16x8, *(const pf_u32x4 *)(ah + off));
+                const pf_bf16x8 xl = __builtin_bit_cast(pf_bf16x8, *(const pf_u32x4 *)(al + off));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n]
+    const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j >= nb) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int pos = pb + 16 * j + 4 * kq + r;
+            float y = acc[j][r];
+            if (OP == OP_QKV) {
+                // packed rows 2m, 2m+1 of a query or key head are its dims m, m + hd/2 (adjacent lanes)
+                const int which = n >= Q + KVr ? 2 : (n >= Q ? 1 : 0);
+                const int base = n - (which == 0 ? 0 : (which == 1 ? Q : Q + KVr));
+                const int i = base & (hd - 1);
+                const int srow = which == 2 ? base : (base & ~(hd - 1)) + ((i & 1) ? (i >> 1) + half : (i >> 1));
+                if (bias_off != ~(uint64_t)0 && nrow)
+                    y += pf_bf16f(((const uint16_t *)(p.blob + bias_off))[(which == 0 ? 0 : (which == 1 ? Q : Q + KVr)) + srow]);
+                const float partner = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
+                if (!nrow || pos >= p.P) continue;
+                const int slot = p.pos0 + pos;
+                if (which == 2) {
+                    const int jh = srow >> p.hd_shift, d = srow & (hd - 1);
+                    p.kv[((((size_t)layer * 2 + 1) * p.nkv + jh) * p.S + slot) * hd + d] = pf_to_bf16(y);
+                    continue;
+                }
+                if (i & 1) continue;  // the odd row is the partner of this pair
+                const int h = srow >> p.hd_shift, m = srow & (hd - 1);
+                const float2 cs = ((const float2 *)(p.blob + p.rope))[(size_t)slot * half + m];
+                const float r0 = y * cs.x - partner * cs.y, r1 = partner * cs.x + y * cs.y;
+                if (which == 0) {
+                    p.q[(size_t)pos * Q + h * hd + m] = r0;
+                    p.q[(size_t)pos * Q + h * hd + m + half] = r1;
+                } else {
+                    uint16_t *kc = p.kv + ((((size_t)layer * 2 + 0) * p.nkv + h) * p.S + slot) * hd;
+                    kc[m] = pf_to_bf16(r0);
+                    kc[m + half] = pf_to_bf16(r1);
+                }
+            } else if (OP == OP_O || OP == OP_DOWN) {
+                if (nrow && pos < p.P) p.x[(size_t)pos * p.H + n] += y;
+            } else if (OP == OP_GATEUP) {
+                // packed row 2i is gate row i, 2i + 1 up row i (adjacent lanes)
+                const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
+                if (!nrow || pos >= p.P || (n & 1)) continue;
+                pf_store_split(p.inh[dst] + (size_t)pos * p.ks, p.inl[dst] + (size_t)pos * p.ks, n >> 1,
+                               y / (1.f + __expf(-y)) * up);
+            } else {  // vocabulary projection of the last position (row 0 of the block)
+                if (nrow && pos == 0) p.logits[n] = y;
+            }
+        }
+    }
+}
+
+// Columns [K, ks) of the rows written by the gate/up epilogue (the down projection's k tail reads them).
+__global__ __launch_bounds__(256) void k_pf_clear_tail(PfParams p, int buf, int K) {
+    const int r = blockIdx.x;
+    for (int i = K + (int)threadIdx.x; i < p.ks; i += 256) {
+        p.inh[buf][(size_t)r * p.ks + i] = 0;
+        p.inl[buf][(size_t)r * p.ks + i] = 0;
+    }
+}
+
+// Causal attention of prompt position pos0 + qi, query head h, over cache positions 0 .. pos0 + qi (the
+// current one included, rounded to bf16 as the cache holds it): one wave.  Keys in passes of 64, one per
+// lane (full dot product over the head dims); a running maximum, sum and output per pass (online
+// softmax); the weighted values with lanes over the head dims.  Output hi/lo into input buffer dst.
+__global__ __launch_bounds__(64) void k_pf_attn(PfParams p, int layer, int dst) {
+    __shared__ float qs[128];
+    __shared__ float ps[64];
+    const int qi = blockIdx.x, h = blockIdx.y, l = threadIdx.x, hd = p.hd;
+    const int j = h / p.gqa, Lc = p.pos0 + qi + 1;
+    for (int d = l; d < hd; d += 64) qs[d] = p.q[(size_t)qi * p.nq * hd + h * hd + d] * p.scale;
+    __syncthreads();
+    const uint16_t *K = p.kv + (((size_t)layer * 2 + 0) * p.nkv + j) * p.S * hd;
+    const uint16_t *V = p.kv + (((size_t)layer * 2 + 1) * p.nkv + j) * p.S * hd;
+    float M = -INFINITY, Lsum = 0.f, o0 = 0.f, o1 = 0.f;   // o0: dim l, o1: dim l + 64 (head size 128)
+    for (int t0 = 0; t0 < Lc; t0 += 64) {
+        const int t = t0 + l;
+        float s = -INFINITY;
+        if (t < Lc) {
+            const uint16_t *kr = K + (size_t)t * hd;
+            float acc = 0.f;
+            for (int d = 0; d < hd; d += 8) {
+                const pf_u32x4 w = *(const pf_u32x4 *)(kr + d);
+                acc = fmaf(qs[d + 0], __uint_as_float(w.x << 16), acc);
+                acc = fmaf(qs[d + 1], __uint_as_float(w.x & 0xffff0000u), acc);
+                acc = fmaf(qs[d + 2], __uint_as_float(w.y << 16), acc);
+                acc = fmaf(qs[d + 3], __uint_as_float(w.y & 0xffff0000u), acc);
+                acc = fmaf(qs[d + 4], __uint_as_float(w.z << 16), acc);
+                acc = fmaf(qs[d + 5], __uint_as_float(w.z & 0xffff0000u), acc);
+                acc = fmaf(qs[d + 6], __uint_as_float(w.w << 16), acc);
+                acc = fmaf(qs[d + 7], __uint_as_float(w.w & 0xffff0000u), acc);
+            }
+            s = acc;
+        }
+        float mp = s;
+        for (int o = 32; o > 0; o >>= 1) mp = fmaxf(mp, __shfl_xor(mp, o));
+        const float mn = fmaxf(M, mp);
+        const float c = M == -INFINITY ? 0.f : __expf(M - mn);
+        const float pw = t < Lc ? __expf(s - mn) : 0.f;
+        float sp = pw;
+        for (int o = 32; o > 0; o >>= 1) sp += __shfl_xor(sp, o);
+        Lsum = Lsum * c + sp;
+        o0 *= c;
+        o1 *= c;
+        M = mn;
+        ps[l] = pw;
+        __syncthreads();
+        const int nk = min(64, Lc - t0);
+        for (int k = 0; k < nk; ++k) {
+            const float pk = ps[k];
+            const uint16_t *vr = V + (size_t)(t0 + k) * hd;
+            if (l < hd) o0 = fmaf(pk, pf_bf16f(vr[l]), o0);
+            if (l + 64 < hd) o1 = fmaf(pk, pf_bf16f(vr[l + 64]), o1);
+        }
+        __syncthreads();
+    }
+    const float inv = 1.f / Lsum;
+    uint16_t *dh = p.inh[dst] + (size_t)qi * p.ks + h * hd, *dl = p.inl[dst] + (size_t)qi * p.ks + h * hd;
+    if (l < hd) pf_store_split(dh, dl, l, o0 * inv);
+    if (l + 64 < hd) pf_store_split(dh, dl, l + 64, o1 * inv);
+}
+
+// Greedy argmax of the V logits (lowest index among equal maxima); also the decode step's previous token.
+__global__ __launch_bounds__(1024) void k_pf_argmax(PfParams p) {
+    __shared__ float bv[1024];
+    __shared__ int bi[1024];
+    float best = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int i = threadIdx.x; i < p.V; i += 1024) {
+        const float v = p.logits[i];
+        if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+    }
+    bv[threadIdx.x] = best;
+    bi[threadIdx.x] = idx;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+            const float v = bv[threadIdx.x + s];
+            const int i = bi[threadIdx.x + s];
+            if (v > bv[threadIdx.x] || (v == bv[threadIdx.x] && i < bi[threadIdx.x])) {
+                bv[threadIdx.x] = v;
+                bi[threadIdx.x] = i;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        p.argmax_out[0] = bi[0];
+        if (p.prev_token) *p.prev_token = (uint32_t)bi[0];
+    }
+}
+
+}  // namespace mbk

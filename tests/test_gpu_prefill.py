@@ -1,0 +1,156 @@
+"""Multi-token prefill (mbk_prefill) against the oracle stepped over the same positions, on the GPU.
+
+The oracle for a prefill of positions p0 .. p0 + n - 1 is the decode-step oracle run over those positions
+(itself pinned by stepwise decode = full-sequence recomputation).  Checked: the last position's logits
+(max |dlogit| <= 2e-2 * std) and argmax (the lowest-index maximum of the GPU's own logits; the oracle's where
+its margin exceeds 5e-2, else one of its near-ties), and every cache slot the prefill wrote, per layer, as for
+the decode step (layer 0 within one bf16 step plus 2^-10 of the RMS, every layer within 2e-2 in relative L2)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import LOGIT_TOL, compare, kv_slot_check, log, upload
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillPair:
+    def __init__(self, wl, W=None):
+        import torch
+        import oracle
+        from persistent_megakernel_decode_wg_amd import Decoder
+        self.wl = wl
+        self.W = synth.make_weights(wl) if W is None else W
+        self.dec = Decoder(wl)
+        self.dec.pack_weights(upload(self.W))
+        self.dec.alloc_kv()
+        self.ref = oracle.Model(wl, self.W)
+        self.logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
+        self.am = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def close(self):
+        self.dec.close()
+
+    def prefill(self, tokens, pos0):
+        self.dec.prefill(tokens, pos0, self.logits, self.am)
+        self.dec.check()
+        return self.logits.cpu().numpy().copy(), int(self.am.item())
+
+    def oracle_steps(self, tokens, pos0):
+        lo = ao = None
+        for i, t in enumerate(tokens):
+            lo, ao, _ = self.ref.step(int(t), pos0 + i)
+        return lo, ao
+
+    def check(self, tokens, pos0, label):
+        lg, am = self.prefill(tokens, pos0)
+        lo, ao = self.oracle_steps(tokens, pos0)
+        assert np.all(np.isfinite(lg)), label
+        rel, margin = compare(lg, am, lo, ao)
+        assert rel <= LOGIT_TOL, "%s: max|dlogit| = %.4g std" % (label, rel)
+        kv = self.dec.kv.cpu().numpy().view(np.uint16)
+        worst0 = worst_rel = 0.0
+        for slot in range(pos0, pos0 + len(tokens)):
+            x0, r = kv_slot_check(kv[:, :, :, slot, :], self.ref.kv[:, :, :, slot, :])
+            assert x0.max() <= 1.0, "%s slot %d: layer-0 cache entry off by %.3g x the tolerance" % (label, slot, x0.max())
+            assert r.max() <= LOGIT_TOL, "%s slot %d: layer %d cache off by %.3g (relative L2)" % (
+                label, slot, int(np.unravel_index(r.argmax(), r.shape)[0]), r.max())
+            worst0, worst_rel = max(worst0, float(x0.max())), max(worst_rel, float(r.max()))
+        log("%s: max|dlogit|/std %.3g, margin %.3g; cache: layer 0 %.3g of the tolerance, worst relative L2 %.3g"
+            % (label, rel, margin, worst0, worst_rel))
+        return lg, am, lo, ao
+
+
+@pytest.fixture
+def make():
+    made = []
+
+    def f(*a, **kw):
+        p = PrefillPair(*a, **kw)
+        made.append(p)
+        return p
+    yield f
+    for p in made:
+        p.close()
+
+
+def test_prefill_tiny_whole_cache(make):
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = make(wl)
+    toks = [int(t) for t in synth.tokens(11, "prefill", wl.kv_capacity, wl.vocab)]
+    p.check(toks, 0, "tiny prefill 0..31")
+
+
+def test_prefill_after_decode_steps_and_in_chunks(make):
+    """Decode steps at 0..4, then prefill 5..20 and 21..30 on the same cache: both match the oracle."""
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = make(wl)
+    toks = [int(t) for t in synth.tokens(12, "prefill", 31, wl.vocab)]
+    for pos in range(5):
+        p.dec.decode_step(toks[pos], pos, p.logits, p.am)
+        p.dec.check()
+        p.ref.step(toks[pos], pos)
+    p.check(toks[5:21], 5, "tiny prefill 5..20 after decode 0..4")
+    p.check(toks[21:31], 21, "tiny prefill 21..30")
+
+
+def test_prefill_chunked_equals_one_shot_bitwise(make):
+    """Every position's projections are independent rows of the GEMMs and its attention reads the same
+    cache slots, so prefilling 0..63 in one call or as 0..23, 24..63 gives the same bits (logits, argmax
+    and every cache slot)."""
+    import torch
+    wl = synth.get("smollm135m-kv128")
+    W = synth.make_weights(wl)
+    a, b = make(wl, W), make(wl, W)
+    toks = [int(t) for t in synth.prompt_tokens(wl)]
+    la, ia = a.prefill(toks, 0)
+    b.prefill(toks[:24], 0)
+    lb, ib = b.prefill(toks[24:], 24)
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+    assert torch.equal(a.dec.kv, b.dec.kv)
+
+
+def test_prefill_smollm135m_prompt_then_decode(make):
+    """The SmolLM-135M-shaped 64-token prompt in one prefill, then greedy decode steps 64..79 (the first
+    one fed the prefill's argmax through MBK_TOKEN_PREV), all against the oracle."""
+    from persistent_megakernel_decode_wg_amd import MBK_TOKEN_PREV
+    wl = synth.get("smollm135m-kv128")
+    p = make(wl)
+    toks = [int(t) for t in synth.prompt_tokens(wl)]
+    lg, am, lo, ao = p.check(toks, 0, "smollm135m prefill 0..63")
+    tok = ao
+    for pos in range(64, 80):
+        g_in = MBK_TOKEN_PREV if pos == 64 and am == ao else tok
+        p.dec.decode_step(g_in, pos, p.logits, p.am)
+        p.dec.check()
+        lg = p.logits.cpu().numpy()
+        lo, ao2, _ = p.ref.step(tok, pos)
+        rel, _ = compare(lg, int(p.am.item()), lo, ao2)
+        assert rel <= LOGIT_TOL, "decode after prefill, pos %d" % pos
+        tok = ao2
+
+
+def test_prefill_long_prompt_on_4096_slot_cache(make):
+    """512 seeded tokens at positions 0..511 of the 4096-slot SmolLM-135M-shaped cache."""
+    wl = synth.get("smollm135m-kv4096")
+    p = make(wl)
+    toks = [int(t) for t in synth.tokens(13, "long-prompt", 512, wl.vocab)]
+    p.check(toks, 0, "smollm135m-kv4096 prefill 0..511")
+
+
+def test_prefill_qwen2_bias(make):
+    """Q/K/V biases and a 7-way query group: the 64-token prompt of the Qwen2-0.5B-shaped decoder."""
+    wl = synth.get("qwen2-0.5b-kv128")
+    p = make(wl)
+    p.check([int(t) for t in synth.prompt_tokens(wl)], 0, "qwen2 prefill 0..63")
+
+
+def test_prefill_argument_errors(make):
+    from persistent_megakernel_decode_wg_amd import MBK_ERR_ARG, MBK_ERR_RANGE, MbkError
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = make(wl)
+    for toks, pos0, code in (([1, 2], wl.kv_capacity - 1, MBK_ERR_RANGE), ([1, wl.vocab], 0, MBK_ERR_ARG),
+                             ([-1], 0, MBK_ERR_ARG), ([1], -1, MBK_ERR_RANGE)):
+        with pytest.raises(MbkError) as e:
+            p.dec.prefill(toks, pos0, p.logits, p.am)
+        assert e.value.code == code
