@@ -141,6 +141,54 @@ def timed_steps(dec, positions, n, logits, am, stream, fn=None):
     return [a.elapsed_time(b) * 1e3 for a, b in ev]
 
 
+def prefill_flops(wl, n: int, pos0: int = 0) -> float:
+    """Algorithmic flops of a prefill of n tokens at positions pos0 .. pos0 + n - 1: every projection matrix
+    applied to every position (multiply-add = 2 flops), causal attention (scores and weighted values over
+    each position's pos + 1 cached positions), the vocabulary projection of the last position."""
+    H, hd, nq, nkv, I = wl.hidden, wl.head_dim, wl.n_heads, wl.n_kv_heads, wl.intermediate
+    per_layer = (nq * hd + 2 * nkv * hd) * H + H * nq * hd + 3 * I * H
+    attended = sum(pos0 + i + 1 for i in range(n))
+    return 2.0 * n * per_layer * wl.n_layers + 2.0 * 2 * hd * nq * attended * wl.n_layers + 2.0 * wl.vocab * H
+
+
+def prefill_summary(wl, n: int, decode_us: float, reps: int = 5):
+    """p50 time of one prefill of n seeded tokens at position 0 (HIP events on the stream), against n decode
+    steps of the same model (decode_us per step), and its algorithmic TFLOP/s against the bf16 matrix-core
+    peak (the hi/lo input pairs double the products actually executed)."""
+    import torch
+    import synth
+    from persistent_megakernel_decode_wg_amd import Decoder
+    W = synth.make_weights(wl)
+    dev = lambda a: torch.from_numpy(a.view("int16")).cuda()
+    dec = Decoder(wl)
+    dec.pack_weights({"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
+                      "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]})
+    del W
+    dec.alloc_kv()
+    toks = [int(t) for t in synth.tokens(13, "bench-prompt", n, wl.vocab)]
+    logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    scratch = dec.prefill(toks, 0, logits, am)
+    stream = torch.cuda.current_stream()
+    us = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dec.prefill(toks, 0, logits, am, scratch=scratch)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    dec.check()
+    dec.close()
+    del dec, scratch
+    torch.cuda.empty_cache()
+    t = pct(us, 0.5)
+    fl = prefill_flops(wl, n)
+    return {"tokens": n, "us_p50": round(t, 1), "us_per_token": round(t / n, 2), "tok_s": round(n / t * 1e6, 1),
+            "decode_steps_us": round(decode_us * n, 1), "speedup_over_decode_steps": round(decode_us * n / t, 2),
+            "algorithmic_tflops": round(fl / t * 1e-6, 2), "frac_of_bf16_mfma_peak": round(fl / t * 1e-6 / 2500.0, 4)}
+
+
 def config_summary(wl, steps: int = 64):
     """One workload measured the way the headline is (its greedy positions, the token fed back on the device):
     p50 us/token of the persistent kernel, its fraction of the 8 TB/s roofline, the same kernel with a grid
@@ -362,6 +410,14 @@ def main():
         for name in synth.WORKLOAD_ORDER:
             extra["configs"][name] = config_summary(synth.get(name))
             print("config %s: %s" % (name, json.dumps(extra["configs"][name])), file=sys.stderr, flush=True)
+        # multi-token prefill: the 64-token prompt of the SmolLM-135M shape and a 512-token prompt on its
+        # 4096-slot cache, against as many decode steps
+        extra["prefill"] = {}
+        for name, n in (("smollm135m-kv128", 64), ("smollm135m-kv4096", 512)):
+            dus = extra["configs"][name]["us_per_token_p50"]
+            extra["prefill"]["%s/%d" % (name, n)] = prefill_summary(synth.get(name), n, dus)
+            print("prefill %s/%d: %s" % (name, n, json.dumps(extra["prefill"]["%s/%d" % (name, n)])),
+                  file=sys.stderr, flush=True)
     timed = "%d-%d" % (g0, g0 + K - 1) if K <= span else "%d-%d cycled over %d steps" % (g0, g1 - 1, K)
     out = {
         "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",

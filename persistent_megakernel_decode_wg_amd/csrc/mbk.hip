@@ -1051,8 +1051,8 @@ PfLayout pf_layout(const mbk_config &c, int n) {
 
 template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
-    const dim3 grid((unsigned)((g.rows + kPfTileN - 1) / kPfTileN), (unsigned)((np_rows + kPfTileP - 1) / kPfTileP));
-    hipLaunchKernelGGL(k_pf_gemm<OP>, grid, dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    const dim3 grid((unsigned)((g.rows + kPfRows - 1) / kPfRows), (unsigned)((np_rows + kPfPos - 1) / kPfPos));
+    hipLaunchKernelGGL(k_pf_gemm<OP>, grid, dim3(64), 0, st, pp, g, layer, src, dst, np_rows, bias);
 }
 
 }  // namespace
@@ -1119,7 +1119,7 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
         const LayerPlan &Y = P.layers[(size_t)l];
         hipLaunchKernelGGL(k_pf_norm, dim3((unsigned)L.Pp), dim3(256), 0, st, pp, Y.attn_norm, 0, l == 0 ? 1 : 0, 0);
         pf_gemm<OP_QKV>(pp, Y.qkv, l, 0, 0, L.Pp, Y.bias, st);
-        hipLaunchKernelGGL(k_pf_attn, dim3((unsigned)n_tokens, (unsigned)c.n_heads), dim3(64), 0, st, pp, l, 1);
+        hipLaunchKernelGGL(k_pf_attn, dim3((unsigned)((n_tokens + kPfAttnQ - 1) / kPfAttnQ), (unsigned)c.n_heads), dim3(256), 0, st, pp, l, 1);
         if (Q % 32) hipLaunchKernelGGL(k_pf_clear_tail, dim3((unsigned)L.Pp), dim3(256), 0, st, pp, 1, Q);
         pf_gemm<OP_O>(pp, Y.o, l, 1, 0, L.Pp, none, st);
         hipLaunchKernelGGL(k_pf_norm, dim3((unsigned)L.Pp), dim3(256), 0, st, pp, Y.mlp_norm, 0, 0, 0);

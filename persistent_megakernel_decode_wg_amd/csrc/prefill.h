@@ -24,8 +24,7 @@ typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int pf_u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPfTileN = 64;    // packed rows per GEMM workgroup (4 waves x 16)
-constexpr int kPfTileP = 64;    // positions per GEMM workgroup (4 MFMA row blocks of 16)
+constexpr int kPfTileP = 64;    // prompt positions are padded to a multiple of this
 
 // Device buffers and shape of one prefill call (kernel argument, by value).
 struct PfParams {
@@ -97,44 +96,56 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
     }
 }
 
-// C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g: workgroup (bx, by) takes packed rows
-// [64 bx, 64 bx + 64) (wave w: 16 rows from 64 bx + 16 w) and positions [64 by, 64 by + 64) of the input
-// buffer `src` (np_rows rows in all).  Lane l feeds row l % 16 of each operand with input group
-// 4 s + l / 16 of step s and holds, after the k loop, C[pos0 + 4 (l / 16) + r][n] for the four r of each
-// position block.  Epilogue by op.
+// C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  One wave per workgroup: packed rows
+// [16 bx, 16 bx + 16) and positions [32 by, 32 by + 32) of input buffer `src` (np_rows rows in all, a
+// multiple of 16).  Lane l feeds row l % 16 of each operand with input group 4 s + l / 16 of k step s (32
+// inputs); the k steps go in batches of 8 whose weight and activation loads are all issued before the
+// batch's products, so a batch costs one memory latency rather than eight.  After the k loop lane l holds
+// C[32 by + 16 j + 4 (l / 16) + r][16 bx + l % 16] in acc[j][r].  Epilogue by op.
+constexpr int kPfRows = 16, kPfPos = 32, kPfBatch = 8;
 template <int OP>
-__global__ __launch_bounds__(256) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
-                                                 uint64_t bias_off) {
-    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int n = blockIdx.x * kPfTileN + wv * 16 + (l & 15);
-    const int pb = blockIdx.y * kPfTileP;
-    const int nb = min(kPfTileP, np_rows - pb) >> 4;     // position blocks of 16 (np_rows is a multiple of 16)
+__global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
+                                                uint64_t bias_off) {
+    const int l = threadIdx.x;
+    const int n = blockIdx.x * kPfRows + (l & 15);
+    const int pb = blockIdx.y * kPfPos;
+    const int nb = min(kPfPos, np_rows - pb) >> 4;       // position blocks of 16: 1 or 2
     const int kq = l >> 4, ngrp = g.K >> 3, nsteps = (ngrp + 3) >> 2;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
-    pf_f32x4 acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
+    const size_t arow0 = (size_t)(pb + (l & 15)) * p.ks, arow1 = arow0 + (size_t)16 * p.ks;
+    pf_f32x4 acc[2];
+    acc[0] = acc[1] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
     const bool nrow = n < g.rows;
-    for (int s = 0; s < nsteps; ++s) {
-        const int kg = 4 * s + kq;
-        pf_u32x4 bw = {0u, 0u, 0u, 0u};
-        if (nrow && kg < ngrp) bw = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
-        const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw);
+    for (int s0 = 0; s0 < nsteps; s0 += kPfBatch) {
+        pf_u32x4 bw[kPfBatch], a0h[kPfBatch], a0l[kPfBatch], a1h[kPfBatch], a1l[kPfBatch];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < nb) {
-                const size_t off = (size_t)(pb + 16 * j + (l & 15)) * p.ks + 8 * kg;
-                const pf_bf16x8 xh = __builtin_bit_cast(pf_bf16x8, *(const pf_u32x4 *)(ah + off));
-                const pf_bf16x8 xl = __builtin_bit_cast(pf_bf16x8, *(const pf_u32x4 *)(al + off));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, b, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, b, acc[j], 0, 0, 0);
+        for (int i = 0; i < kPfBatch; ++i) {
+            const int kg = 4 * (s0 + i) + kq;
+            bw[i] = (pf_u32x4){0u, 0u, 0u, 0u};
+            a0h[i] = a0l[i] = a1h[i] = a1l[i] = (pf_u32x4){0u, 0u, 0u, 0u};
+            if (s0 + i < nsteps) {
+                if (nrow && kg < ngrp) bw[i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+                a0h[i] = *(const pf_u32x4 *)(ah + arow0 + 8 * kg);
+                a0l[i] = *(const pf_u32x4 *)(al + arow0 + 8 * kg);
+                if (nb > 1) {
+                    a1h[i] = *(const pf_u32x4 *)(ah + arow1 + 8 * kg);
+                    a1l[i] = *(const pf_u32x4 *)(al + arow1 + 8 * kg);
+                }
             }
+        }
+#pragma unroll
+        for (int i = 0; i < kPfBatch; ++i) {
+            const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw[i]);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a0h[i]), b, acc[0], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a0l[i]), b, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a1h[i]), b, acc[1], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a1l[i]), b, acc[1], 0, 0, 0);
         }
     }
     // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n]
     const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
         if (j >= nb) break;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -192,65 +203,121 @@ __global__ __launch_bounds__(256) void k_pf_clear_tail(PfParams p, int buf, int 
     }
 }
 
-// Causal attention of prompt position pos0 + qi, query head h, over cache positions 0 .. pos0 + qi (the
-// current one included, rounded to bf16 as the cache holds it): one wave.  Keys in passes of 64, one per
-// lane (full dot product over the head dims); a running maximum, sum and output per pass (online
-// softmax); the weighted values with lanes over the head dims.  Output hi/lo into input buffer dst.
-__global__ __launch_bounds__(64) void k_pf_attn(PfParams p, int layer, int dst) {
-    __shared__ float qs[128];
-    __shared__ float ps[64];
-    const int qi = blockIdx.x, h = blockIdx.y, l = threadIdx.x, hd = p.hd;
-    const int j = h / p.gqa, Lc = p.pos0 + qi + 1;
-    for (int d = l; d < hd; d += 64) qs[d] = p.q[(size_t)qi * p.nq * hd + h * hd + d] * p.scale;
-    __syncthreads();
+// Causal attention of prompt positions pos0 + 16 bx .. pos0 + 16 bx + 15, query head h, each over cache
+// positions 0 .. its own (the current one included, rounded to bf16 as the cache holds it).  Four waves,
+// four queries each; keys in blocks of 64 aligned at cache position 0, shared by the 16 queries: a block's
+// keys and values are staged in LDS with one batch of 16-byte loads (the key rows' 16-byte chunks rotated
+// by row so that lanes reading chunk c of different rows hit different banks).  Lane t of a wave scores key
+// t of the block for the wave's four queries (full dot product over the head dims); per query a running
+// maximum, sum and output (online softmax; a block wholly past a query's position leaves its state exactly
+// unchanged, so the result does not depend on how the prompt is split into calls); the weighted values
+// with lanes over the head dims, from LDS.  Output hi/lo into input buffer dst.
+constexpr int kPfAttnQ = 16, kPfAttnQW = 4;
+__global__ __launch_bounds__(256) void k_pf_attn(PfParams p, int layer, int dst) {
+    __shared__ float qs[kPfAttnQ * 128];
+    __shared__ float ps[kPfAttnQ * 64];
+    __shared__ pf_u32x4 kb[64 * 16], vb[64 * 16];   // up to 64 keys x 128 dims of bf16 each
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hd = p.hd, c16 = hd >> 3;
+    const int h = blockIdx.y, j = h / p.gqa, q0 = blockIdx.x * kPfAttnQ;
+    const int nqb = min(kPfAttnQ, p.P - q0);
+    for (int i = tid; i < kPfAttnQ * hd; i += 256) {
+        const int qr = i >> p.hd_shift, d = i & (hd - 1);
+        qs[i] = qr < nqb ? p.q[(size_t)(q0 + qr) * p.nq * hd + h * hd + d] * p.scale : 0.f;
+    }
     const uint16_t *K = p.kv + (((size_t)layer * 2 + 0) * p.nkv + j) * p.S * hd;
     const uint16_t *V = p.kv + (((size_t)layer * 2 + 1) * p.nkv + j) * p.S * hd;
-    float M = -INFINITY, Lsum = 0.f, o0 = 0.f, o1 = 0.f;   // o0: dim l, o1: dim l + 64 (head size 128)
-    for (int t0 = 0; t0 < Lc; t0 += 64) {
-        const int t = t0 + l;
-        float s = -INFINITY;
-        if (t < Lc) {
-            const uint16_t *kr = K + (size_t)t * hd;
-            float acc = 0.f;
-            for (int d = 0; d < hd; d += 8) {
-                const pf_u32x4 w = *(const pf_u32x4 *)(kr + d);
-                acc = fmaf(qs[d + 0], __uint_as_float(w.x << 16), acc);
-                acc = fmaf(qs[d + 1], __uint_as_float(w.x & 0xffff0000u), acc);
-                acc = fmaf(qs[d + 2], __uint_as_float(w.y << 16), acc);
-                acc = fmaf(qs[d + 3], __uint_as_float(w.y & 0xffff0000u), acc);
-                acc = fmaf(qs[d + 4], __uint_as_float(w.z << 16), acc);
-                acc = fmaf(qs[d + 5], __uint_as_float(w.z & 0xffff0000u), acc);
-                acc = fmaf(qs[d + 6], __uint_as_float(w.w << 16), acc);
-                acc = fmaf(qs[d + 7], __uint_as_float(w.w & 0xffff0000u), acc);
+    const int Lmax = p.pos0 + q0 + nqb;           // keys the block's last query sees
+    int lim[kPfAttnQW];                            // keys 0 .. lim - 1 for this wave's queries
+    float M[kPfAttnQW], Ls[kPfAttnQW], o0[kPfAttnQW], o1[kPfAttnQW];
+#pragma unroll
+    for (int u = 0; u < kPfAttnQW; ++u) {
+        const int qr = w * kPfAttnQW + u;
+        lim[u] = p.pos0 + q0 + min(qr, nqb - 1) + 1;
+        M[u] = -INFINITY;
+        Ls[u] = o0[u] = o1[u] = 0.f;
+    }
+    for (int t0 = 0; t0 < Lmax; t0 += 64) {
+        const int nk = min(64, Lmax - t0);
+        {
+            pf_u32x4 kw[4], vw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = tid + 256 * u, r = i / c16, c = i & (c16 - 1);
+                if (i < 64 * c16 && r < nk) {
+                    kw[u] = ((const pf_u32x4 *)(K + (size_t)(t0 + r) * hd))[c];
+                    vw[u] = ((const pf_u32x4 *)(V + (size_t)(t0 + r) * hd))[c];
+                }
             }
-            s = acc;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = tid + 256 * u, r = i / c16, c = i & (c16 - 1);
+                if (i < 64 * c16 && r < nk) {
+                    kb[r * c16 + (c ^ (r & (c16 - 1)))] = kw[u];
+                    vb[i] = vw[u];
+                }
+            }
         }
-        float mp = s;
-        for (int o = 32; o > 0; o >>= 1) mp = fmaxf(mp, __shfl_xor(mp, o));
-        const float mn = fmaxf(M, mp);
-        const float c = M == -INFINITY ? 0.f : __expf(M - mn);
-        const float pw = t < Lc ? __expf(s - mn) : 0.f;
-        float sp = pw;
-        for (int o = 32; o > 0; o >>= 1) sp += __shfl_xor(sp, o);
-        Lsum = Lsum * c + sp;
-        o0 *= c;
-        o1 *= c;
-        M = mn;
-        ps[l] = pw;
         __syncthreads();
-        const int nk = min(64, Lc - t0);
+        const int t = t0 + l;
+        float s[kPfAttnQW];
+#pragma unroll
+        for (int u = 0; u < kPfAttnQW; ++u) s[u] = 0.f;
+        if (l < nk) {
+            for (int c = 0; c < c16; ++c) {
+                const pf_u32x4 kw = kb[l * c16 + (c ^ (l & (c16 - 1)))];
+                float kf[8];
+                kf[0] = __uint_as_float(kw.x << 16); kf[1] = __uint_as_float(kw.x & 0xffff0000u);
+                kf[2] = __uint_as_float(kw.y << 16); kf[3] = __uint_as_float(kw.y & 0xffff0000u);
+                kf[4] = __uint_as_float(kw.z << 16); kf[5] = __uint_as_float(kw.z & 0xffff0000u);
+                kf[6] = __uint_as_float(kw.w << 16); kf[7] = __uint_as_float(kw.w & 0xffff0000u);
+#pragma unroll
+                for (int u = 0; u < kPfAttnQW; ++u) {
+                    const float *qd = qs + (w * kPfAttnQW + u) * hd + 8 * c;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s[u] = fmaf(qd[e], kf[e], s[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPfAttnQW; ++u) {
+            const float sv = t < lim[u] ? s[u] : -INFINITY;
+            float mp = sv;
+            for (int o = 32; o > 0; o >>= 1) mp = fmaxf(mp, __shfl_xor(mp, o));
+            const float mn = fmaxf(M[u], mp);
+            const float cf = M[u] == -INFINITY ? 0.f : __expf(M[u] - mn);
+            const float pw = t < lim[u] ? __expf(sv - mn) : 0.f;
+            float sp = pw;
+            for (int o = 32; o > 0; o >>= 1) sp += __shfl_xor(sp, o);
+            Ls[u] = Ls[u] * cf + sp;
+            o0[u] *= cf;
+            o1[u] *= cf;
+            M[u] = mn;
+            ps[(w * kPfAttnQW + u) * 64 + l] = pw;
+        }
+        __syncthreads();
+        const uint16_t *vs = (const uint16_t *)vb;
+        const float *pw4 = ps + w * kPfAttnQW * 64;
         for (int k = 0; k < nk; ++k) {
-            const float pk = ps[k];
-            const uint16_t *vr = V + (size_t)(t0 + k) * hd;
-            if (l < hd) o0 = fmaf(pk, pf_bf16f(vr[l]), o0);
-            if (l + 64 < hd) o1 = fmaf(pk, pf_bf16f(vr[l + 64]), o1);
+            const float v0 = l < hd ? pf_bf16f(vs[k * hd + l]) : 0.f;
+            const float v1 = l + 64 < hd ? pf_bf16f(vs[k * hd + l + 64]) : 0.f;
+#pragma unroll
+            for (int u = 0; u < kPfAttnQW; ++u) {
+                const float pk = pw4[u * 64 + k];
+                o0[u] = fmaf(pk, v0, o0[u]);
+                o1[u] = fmaf(pk, v1, o1[u]);
+            }
         }
         __syncthreads();
     }
-    const float inv = 1.f / Lsum;
-    uint16_t *dh = p.inh[dst] + (size_t)qi * p.ks + h * hd, *dl = p.inl[dst] + (size_t)qi * p.ks + h * hd;
-    if (l < hd) pf_store_split(dh, dl, l, o0 * inv);
-    if (l + 64 < hd) pf_store_split(dh, dl, l + 64, o1 * inv);
+#pragma unroll
+    for (int u = 0; u < kPfAttnQW; ++u) {
+        const int qr = w * kPfAttnQW + u;
+        if (qr >= nqb) break;
+        const float inv = 1.f / Ls[u];
+        uint16_t *dh = p.inh[dst] + (size_t)(q0 + qr) * p.ks + h * hd, *dl = p.inl[dst] + (size_t)(q0 + qr) * p.ks + h * hd;
+        if (l < hd) pf_store_split(dh, dl, l, o0[u] * inv);
+        if (l + 64 < hd) pf_store_split(dh, dl, l + 64, o1[u] * inv);
+    }
 }
 
 // Greedy argmax of the V logits (lowest index among equal maxima); also the decode step's previous token.
