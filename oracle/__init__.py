@@ -18,6 +18,11 @@ Pins (each checked by a ``-m "not gpu"`` test):
   * decode step: stepwise decode equals an independent float64 full-sequence
     causal forward; zero output projections give a closed-form logit vector
     whose argmax is the input token.
+  * FP8 (E4M3) quantiser: every finite code encodes back to itself, every
+    midpoint of neighbouring codes goes to the even one, nearest-value brute
+    force over all codes on random inputs, the OCP format's fixed points (448,
+    2^-6, 2^-9, the NaN patterns), the row exponent against its defining
+    inequality, and the dequantised weights exactly representable in bf16.
 Nothing here is "parity unpinned".
 """
 from __future__ import annotations
@@ -57,7 +62,7 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 class Weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p)] + [
         (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "wo", "mlp_norm", "wgate", "wup",
-                           "wdown")]
+                           "wdown")] + [("lm_head", ctypes.c_void_p)]
 
 
 class Trace(ctypes.Structure):
@@ -89,6 +94,14 @@ def _load():
                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(Trace)]
         lib.orc_decode_step.restype = i
         lib.orc_num_threads.restype = i
+        lib.orc_e4m3_value.argtypes = [i]
+        lib.orc_e4m3_value.restype = d
+        lib.orc_e4m3_encode.argtypes = [d]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_fp8_row_exponent.argtypes = [vp, i]
+        lib.orc_fp8_row_exponent.restype = i
+        lib.orc_quantize_rows_e4m3.argtypes = [vp, i, i, vp, vp]
+        lib.orc_dequantize_rows_e4m3.argtypes = [vp, vp, i, i, vp]
         _lib = lib
     return _lib
 
@@ -163,6 +176,61 @@ def argmax(v) -> int:
     return int(_load().orc_argmax(v.ctypes.data, v.size))
 
 
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for the two NaN patterns)."""
+    return float(_load().orc_e4m3_value(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code of a finite x with |x| <= 448, ties to the even code."""
+    return int(_load().orc_e4m3_encode(float(x)))
+
+
+def fp8_row_exponent(w_bf16) -> int:
+    w = _u16(w_bf16)
+    return int(_load().orc_fp8_row_exponent(w.ctypes.data, w.size))
+
+
+def quantize_e4m3_rows(W_bf16) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row power-of-two scaled E4M3 codes of a [rows][K] bf16 matrix: (codes uint8, exponents int32)."""
+    W = _u16(W_bf16)
+    rows, K = W.shape
+    codes = np.empty((rows, K), dtype=np.uint8)
+    exps = np.empty(rows, dtype=np.int32)
+    _load().orc_quantize_rows_e4m3(W.ctypes.data, rows, K, codes.ctypes.data, exps.ctypes.data)
+    return codes, exps
+
+
+def dequantize_e4m3_rows(codes, exps) -> np.ndarray:
+    """The bf16 weights the codes stand for, value(code) * 2^e (exact)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    e = np.ascontiguousarray(exps, dtype=np.int32)
+    rows, K = c.shape
+    W = np.empty((rows, K), dtype=np.uint16)
+    _load().orc_dequantize_rows_e4m3(c.ctypes.data, e.ctypes.data, rows, K, W.ctypes.data)
+    return W
+
+
+FP8_MATRICES = ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")
+
+
+def fp8_weights(weights: Dict[str, object]) -> Tuple[Dict[str, object], Dict[str, object]]:
+    """The FP8 form of a bf16 weight set: every projection matrix and the vocabulary projection (the tied
+    embedding) quantised row by row.  Returns (the quantised model as bf16 weights -- the embedding row
+    gather keeps the bf16 table, the vocabulary projection is "lm_head" --, the codes and exponents)."""
+    q = {"layers": [], "lm_head": quantize_e4m3_rows(weights["embed"])}
+    out = {"embed": weights["embed"], "final_norm": weights["final_norm"], "layers": [],
+           "lm_head": dequantize_e4m3_rows(*q["lm_head"])}
+    for L in weights["layers"]:
+        ql, ol = {}, dict(L)
+        for n in FP8_MATRICES:
+            ql[n] = quantize_e4m3_rows(L[n])
+            ol[n] = dequantize_e4m3_rows(*ql[n])
+        q["layers"].append(ql)
+        out["layers"].append(ol)
+    return out, q
+
+
 class Model:
     """Holds a workload's config, its bf16 weights and an oracle-side KV cache."""
 
@@ -189,6 +257,10 @@ class Model:
         self._keep += [emb, fn]
         w = Weights()
         w.embed, w.final_norm = emb.ctypes.data, fn.ctypes.data
+        if weights.get("lm_head") is not None:
+            lm = _u16(weights["lm_head"])
+            self._keep.append(lm)
+            w.lm_head = lm.ctypes.data
         for n, p in arrs.items():
             setattr(w, n, p)
         self.w = w

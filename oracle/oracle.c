@@ -236,7 +236,7 @@ int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kv, int
     if (tr && tr->x_final) memcpy(tr->x_final, x, sizeof(float) * H);
     /* Final norm, tied vocabulary projection, greedy argmax. */
     orc_rmsnorm(x, w->final_norm, H, c->rms_eps, xn);
-    orc_matvec(w->embed, NULL, c->vocab, H, xn, logits);
+    orc_matvec(w->lm_head ? w->lm_head : w->embed, NULL, c->vocab, H, xn, logits);
     if (argmax) *argmax = orc_argmax(logits, c->vocab);
 
     free(x); free(xn); free(q); free(k); free(v); free(o); free(gt); free(up); free(a);
@@ -249,4 +249,77 @@ int orc_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ---- FP8 weights ------------------------------------------------------------------------------------
+ * The pages name FP8 only as a direction of the project (MegaBake project site, "Next"); the format and
+ * the scaling are this implementation's readings, stated here once:
+ *  - codes are OCP 8-bit floating point, E4M3 variant: sign bit, 4 exponent bits with bias 7, 3 mantissa
+ *    bits; exponent field 0 holds the subnormals (m / 8) * 2^-6; the patterns S.1111.111 are NaN, so the
+ *    largest finite magnitude is 1.75 * 2^8 = 448; there are no infinities;
+ *  - every output row r of a weight matrix has one power-of-two scale 2^e_r, e_r the smallest integer
+ *    not below -126 with max_k |W[r][k]| / 2^e_r <= 448 (0 for an all-zero row), so no weight saturates;
+ *  - code[r][k] is W[r][k] / 2^e_r (exact: a power-of-two scaling) rounded to the nearest E4M3 value,
+ *    ties to the even code; the sign of the weight is kept, zero included.
+ * The weight a code stands for, value(code) * 2^e_r, has at most 4 significant bits and an exponent
+ * well inside bf16's range, so it is exactly a bf16 value: the quantised model is a bf16 model that
+ * orc_decode_step runs unchanged. */
+
+double orc_e4m3_value(int code) {
+    const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest E4M3 code of a finite x with |x| <= 448, ties to even: the spacing of the binade |x| falls in
+ * (2^-9 below 2^-6, else 2^(E-3) for |x| in [2^E, 2^(E+1))), the multiple of it nearest to |x| (the
+ * division is exact; nearbyint rounds halves to even), then the fields of that value. */
+uint8_t orc_e4m3_encode(double x) {
+    const int s = signbit(x) ? 1 : 0;
+    const double a = fabs(x);
+    if (a == 0.0) return (uint8_t)(s << 7);
+    int E2;
+    (void)frexp(a, &E2);          /* a = f * 2^E2, f in [0.5, 1): a in [2^(E2-1), 2^E2) */
+    const int E = E2 - 1;
+    int code;
+    if (E < -6) {
+        const double n = nearbyint(ldexp(a, 9));     /* multiples of 2^-9: 0 .. 8 */
+        code = (int)n;                                /* 8 is 2^-6, the smallest normal (field 1) */
+    } else {
+        double n = nearbyint(ldexp(a, 3 - E));        /* 8 .. 16 multiples of 2^(E-3) */
+        int Ex = E;
+        if (n >= 16.0) { n = 8.0; ++Ex; }
+        code = ((Ex + 7) << 3) | ((int)n - 8);
+    }
+    return (uint8_t)((s << 7) | code);
+}
+
+int orc_fp8_row_exponent(const uint16_t *w, int n) {
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) amax = fmax(amax, fabs((double)orc_bf16_to_f32(w[i])));
+    if (amax == 0.0) return 0;
+    int e = -126;
+    while (ldexp(amax, -e) > 448.0) ++e;
+    return e;
+}
+
+void orc_quantize_rows_e4m3(const uint16_t *W, int rows, int K, uint8_t *codes, int32_t *exps) {
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        const uint16_t *w = W + (size_t)r * K;
+        const int e = orc_fp8_row_exponent(w, K);
+        exps[r] = e;
+        for (int k = 0; k < K; ++k) codes[(size_t)r * K + k] = orc_e4m3_encode(ldexp((double)orc_bf16_to_f32(w[k]), -e));
+    }
+}
+
+/* The bf16 weights the codes stand for (exact; see above). */
+void orc_dequantize_rows_e4m3(const uint8_t *codes, const int32_t *exps, int rows, int K, uint16_t *W) {
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int k = 0; k < K; ++k)
+            W[(size_t)r * K + k] = orc_f32_to_bf16((float)ldexp(orc_e4m3_value(codes[(size_t)r * K + k]), exps[r]));
 }

@@ -21,6 +21,7 @@ typedef struct {
     const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv;
     const uint16_t *const *bq, *const *bk, *const *bv; /* used when qkv_bias != 0 */
     const uint16_t *const *wo, *const *mlp_norm, *const *wgate, *const *wup, *const *wdown;
+    const uint16_t *lm_head;    /* [vocab][hidden] vocabulary projection; NULL: the tied embedding */
 } orc_weights;
 
 /* Optional per-layer intermediates (any pointer may be NULL). */
@@ -50,5 +51,12 @@ size_t orc_kv_bytes(const orc_config *c);
 int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kv, int token, int pos, float *logits,
                     int *argmax, orc_trace *tr);
 int orc_num_threads(void);
+
+/* FP8 (OCP E4M3) weight quantisation; see oracle.c. */
+double orc_e4m3_value(int code);
+uint8_t orc_e4m3_encode(double x);
+int orc_fp8_row_exponent(const uint16_t *w, int n);
+void orc_quantize_rows_e4m3(const uint16_t *W, int rows, int K, uint8_t *codes, int32_t *exps);
+void orc_dequantize_rows_e4m3(const uint8_t *codes, const int32_t *exps, int rows, int K, uint16_t *W);
 
 #endif
