@@ -25,11 +25,21 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic_bytes(wl, pos: int) -> int:
+def algorithmic_bytes(wl, pos: int, fp8: bool = False) -> int:
     """Bytes one step must move: every weight once (tied embedding once), the embedding row,
-    the KV read over 0..pos and the append at pos, the fp32 logits, and the RoPE table row."""
+    the KV read over 0..pos and the append at pos, the fp32 logits, and the RoPE table row.
+    fp8: the projection matrices and the vocabulary projection at one byte per weight plus a 4-byte
+    scale per row; norms and biases stay bf16."""
     kv_pos = wl.n_layers * 2 * wl.n_kv_heads * wl.head_dim * 2
-    return (2 * wl.param_count() + 2 * wl.hidden + (pos + 1) * kv_pos + kv_pos + 4 * wl.vocab + 4 * wl.head_dim)
+    rest = 2 * wl.hidden + (pos + 1) * kv_pos + kv_pos + 4 * wl.vocab + 4 * wl.head_dim
+    if not fp8:
+        return 2 * wl.param_count() + rest
+    H, Q, KV, I, V, L = (wl.hidden, wl.n_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim, wl.intermediate,
+                         wl.vocab, wl.n_layers)
+    mats = L * ((Q + 2 * KV) * H + H * Q + 2 * I * H + H * I) + V * H
+    rows = L * ((Q + 2 * KV) + H + 2 * I + H) + V
+    small = 2 * (2 * L + 1) * H + (2 * L * (Q + 2 * KV) if wl.qkv_bias else 0)
+    return mats + 4 * rows + small + rest
 
 
 OPS = ["qkv", "attn", "o", "gateup", "down"]
@@ -93,7 +103,7 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def setup_workload(wl, W=None):
+def setup_workload(wl, W=None, fp8=False):
     """Packs the workload's seeded weights into a Decoder and runs its setup (the prompt stepped from position 0,
     or the N(0,1) KV prefix and the step after it).  Returns (dec, W, logits, argmax, g0, g1): greedy positions
     g0 .. g1 - 1 follow."""
@@ -107,6 +117,9 @@ def setup_workload(wl, W=None):
     Wt = {"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
           "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]}
     dec = Decoder(wl)
+    if fp8:
+        from persistent_megakernel_decode_wg_amd import MBK_WEIGHTS_FP8_E4M3
+        dec.set_weight_format(MBK_WEIGHTS_FP8_E4M3)
     dec.pack_weights(Wt)
     del Wt
     dec.alloc_kv()
@@ -187,6 +200,27 @@ def prefill_summary(wl, n: int, decode_us: float, reps: int = 5):
     return {"tokens": n, "us_p50": round(t, 1), "us_per_token": round(t / n, 2), "tok_s": round(n / t * 1e6, 1),
             "decode_steps_us": round(decode_us * n, 1), "speedup_over_decode_steps": round(decode_us * n / t, 2),
             "algorithmic_tflops": round(fl / t * 1e-6, 2), "frac_of_bf16_mfma_peak": round(fl / t * 1e-6 / 2500.0, 4)}
+
+
+def fp8_summary(wl, steps: int = 64):
+    """The workload with FP8 (OCP E4M3) weights, measured like the headline: p50 us/token and the fraction
+    of the 8 TB/s roofline for the bytes an fp8 step moves."""
+    import torch
+    dec, W, logits, am, g0, g1 = setup_workload(wl, fp8=True)
+    del W
+    stream = torch.cuda.current_stream()
+    span = g1 - g0
+    positions = lambda i: g0 + (i % span)
+    timed_steps(dec, positions, 8, logits, am, stream)
+    us = timed_steps(dec, positions, steps, logits, am, stream)
+    dec.check()
+    dec.close()
+    del dec, logits, am
+    torch.cuda.empty_cache()
+    p50 = pct(us, 0.5)
+    nb = sum(algorithmic_bytes(wl, positions(i), fp8=True) for i in range(steps)) / steps
+    return {"us_per_token_p50": round(p50, 2), "tok_s": round(1e6 / p50, 1), "bytes_per_token": int(nb),
+            "roofline_frac": round(nb / (p50 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def config_summary(wl, steps: int = 64):
@@ -418,6 +452,11 @@ def main():
             extra["prefill"]["%s/%d" % (name, n)] = prefill_summary(synth.get(name), n, dus)
             print("prefill %s/%d: %s" % (name, n, json.dumps(extra["prefill"]["%s/%d" % (name, n)])),
                   file=sys.stderr, flush=True)
+        # the same decode step streaming FP8 (OCP E4M3) weights, on the two headline shapes
+        extra["fp8_weights"] = {}
+        for name in ("smollm135m-kv128", "smollm1.7b-kv4096"):
+            extra["fp8_weights"][name] = fp8_summary(synth.get(name))
+            print("fp8 %s: %s" % (name, json.dumps(extra["fp8_weights"][name])), file=sys.stderr, flush=True)
     timed = "%d-%d" % (g0, g0 + K - 1) if K <= span else "%d-%d cycled over %d steps" % (g0, g1 - 1, K)
     out = {
         "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",

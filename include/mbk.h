@@ -125,18 +125,27 @@ int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *ds
  * are cut in 8-element groups spread over lanes_per_row = 64 / rows_per_tile
  * lanes, and the 16-byte group of packed row t * rows_per_tile + l /
  * lanes_per_row, group (l % lanes_per_row) + s * lanes_per_row sits at byte
- * offset + ((t * steps + s) * 64 + l) * 16 (s < steps; groups from cols / 8
- * on, and rows from `rows` on, are zero).  kind 0: packed row r is source row
+ * offset + ((t * steps + s) * 64 + l) * 16 for bf16 (s < steps; groups from
+ * cols / 8 on, and rows from `rows` on, are zero).  kind 0: packed row r is source row
  * r; kind 1 (Q/K/V): rows [0, n_heads * head_dim) are queries, then keys, then
  * values, and inside each query or key head packed rows 2m, 2m + 1 are head
  * dims m, m + head_dim / 2; kind 2 (gate/up): packed row 2i is gate row i and
  * 2i + 1 up row i.  which: 0 Q/K/V, 1 output projection, 2 gate/up, 3 down
- * projection of `layer`; layer = -1, which = 0: the tied embedding.
+ * projection of `layer`; layer = -1, which = 0: the embedding table the row
+ * gather reads (always bf16), which = 1: the vocabulary projection (that same
+ * table, or its fp8 copy).  format 0: bf16 groups of values_per_group = 8;
+ * format 1 (mbk_set_weight_format): groups of 16 E4M3 codes, and each tile
+ * of tile_bytes bytes ends with the fp32 scales of its rows_per_tile rows at
+ * byte scale_offset of the tile (16-byte padded, padding zero; a padding
+ * row's scale is 0).  In general the group above sits at byte offset +
+ * t * tile_bytes + (s * 64 + l) * 16, and groups from cols / values_per_group
+ * on are zero.
  * Errors: MBK_ERR_ARG (null pointer), MBK_ERR_RANGE (layer or which out of
  * range), MBK_ERR_UNSUPPORTED / MBK_ERR_HIP as when planning. */
 typedef struct {
     uint64_t offset;
     int32_t rows, cols, lanes_per_row, rows_per_tile, steps, tiles, kind;
+    int32_t format, values_per_group, tile_bytes, scale_offset;
 } mbk_matrix_layout;
 int mbk_get_matrix_layout(mbk_model *m, int32_t layer, int32_t which, mbk_matrix_layout *out);
 
@@ -297,6 +306,28 @@ int mbk_set_attention_split(mbk_model *m, int32_t min_positions);
  * hit the caches).  Only before the schedule is planned (as
  * mbk_set_workgroups); MBK_ERR_ARG for any other value. */
 int mbk_set_attention_items(mbk_model *m, int32_t heads_per_item);
+
+/* Weight storage formats (mbk_set_weight_format). */
+enum { MBK_WEIGHTS_BF16 = 0, MBK_WEIGHTS_FP8_E4M3 = 1 };
+
+/* Stores the projection matrices and the vocabulary projection as 8-bit
+ * codes instead of bf16, halving the weight bytes each decode step streams.
+ * Passage: the project site, "Next" (FP8 among the directions the project
+ * names); the format and scaling are this repository's readings: OCP 8-bit
+ * floating point, E4M3 variant (bias 7, 3 mantissa bits, subnormals, largest
+ * finite 448, no infinities), one power-of-two scale 2^e per output row (e the
+ * smallest integer >= -126 with max|w| / 2^e <= 448, 0 for a zero row, so no
+ * weight saturates), each code the weight divided by the scale (exactly)
+ * rounded to nearest, ties to even, the sign of zero kept.  mbk_pack_weights
+ * quantises the bf16 sources on the device; the embedding row gather keeps
+ * the bf16 table and the vocabulary projection reads an fp8 copy of it; norm
+ * weights and biases stay bf16; activations enter the dot products as fp32.
+ * Only before the schedule is planned (as mbk_set_workgroups): MBK_ERR_STATE
+ * after, MBK_ERR_ARG for an unknown format; planning fails with
+ * MBK_ERR_UNSUPPORTED unless hidden, n_heads*head_dim and intermediate are
+ * multiples of 16.  mbk_prefill reads bf16 weights only (MBK_ERR_UNSUPPORTED
+ * on an fp8 handle). */
+int mbk_set_weight_format(mbk_model *m, int32_t format);
 
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps
  * (the passages are given with the enum above).  MBK_ERR_ARG for any other

@@ -7,5 +7,6 @@ the import of ``Decoder`` fails loudly; there is no fallback path.
 """
 from .binding import (  # noqa: F401
     MBK_ERR_ARG, MBK_ERR_HIP, MBK_ERR_RANGE, MBK_ERR_SIZE, MBK_ERR_STATE, MBK_ERR_TIMEOUT, MBK_ERR_UNSUPPORTED,
-    MBK_LAUNCH_COOPERATIVE, MBK_LAUNCH_PLAIN, MBK_OK, MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV, Decoder,
+    MBK_LAUNCH_COOPERATIVE, MBK_LAUNCH_PLAIN, MBK_OK, MBK_SYNC_BARRIER, MBK_SYNC_DATAFLOW, MBK_TOKEN_PREV,
+    MBK_WEIGHTS_BF16, MBK_WEIGHTS_FP8_E4M3, Decoder,
     MbkError, lib, lib_path)

@@ -18,6 +18,8 @@ MBK_SYNC_DATAFLOW = 0
 MBK_SYNC_BARRIER = 1
 MBK_LAUNCH_PLAIN = 0
 MBK_LAUNCH_COOPERATIVE = 1
+MBK_WEIGHTS_BF16 = 0
+MBK_WEIGHTS_FP8_E4M3 = 1
 
 
 class MbkError(RuntimeError):
@@ -43,7 +45,8 @@ class mbk_weights(ctypes.Structure):
 
 class mbk_matrix_layout(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_uint64)] + [(n, ctypes.c_int32) for n in (
-        "rows", "cols", "lanes_per_row", "rows_per_tile", "steps", "tiles", "kind")]
+        "rows", "cols", "lanes_per_row", "rows_per_tile", "steps", "tiles", "kind", "format", "values_per_group",
+        "tile_bytes", "scale_offset")]
 
 
 _lib = None
@@ -84,12 +87,13 @@ def lib():
         L.mbk_set_launch_mode.argtypes = [vp, i32]
         L.mbk_set_workgroups.argtypes = [vp, i32]
         L.mbk_set_attention_items.argtypes = [vp, i32]
+        L.mbk_set_weight_format.argtypes = [vp, i32]
         L.mbk_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.mbk_last_error.argtypes = []
         L.mbk_last_error.restype = ctypes.c_char_p
         for n in ("mbk_create", "mbk_pack_weights", "mbk_alloc_kv", "mbk_decode_step", "mbk_decode_step_ablation",
                   "mbk_decode_step_static", "mbk_check", "mbk_barrier_bench", "mbk_barrier_stress", "mbk_get_matrix_layout", "mbk_prefill", "mbk_prefill_scratch_bytes", "mbk_num_intervals", "mbk_set_debug", "mbk_set_phase_trace",
-                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_describe"):
+                  "mbk_set_attention_split", "mbk_set_sync_mode", "mbk_set_launch_mode", "mbk_set_workgroups", "mbk_set_attention_items", "mbk_set_weight_format", "mbk_describe"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -291,6 +295,10 @@ class Decoder:
         """0 (automatic), 1 (one query head per item) or n_heads / n_kv_heads (a KV head's query heads
         packed); before the schedule is planned."""
         _chk(lib().mbk_set_attention_items(self.h, int(heads_per_item)))
+
+    def set_weight_format(self, fmt: int) -> None:
+        """MBK_WEIGHTS_BF16 (default) or MBK_WEIGHTS_FP8_E4M3; before the schedule is planned."""
+        _chk(lib().mbk_set_weight_format(self.h, int(fmt)))
 
     def describe(self) -> dict:
         import json

@@ -74,6 +74,7 @@ struct Params {
     int32_t max_splits, gqa, attn_min_chunk, piece_pos, hd_shift;
     int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
     int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
+    int32_t wfmt;             // WeightFmt of the projection matrices: GEMV inputs are hi/lo bf16 (bf16) or fp32 (fp8)
     // LDS offsets in bytes of the dynamic area
     int32_t lds_ivtab, lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_ring;
     int32_t ring_bytes, max_tasks;
@@ -505,7 +506,7 @@ MBK_DEV int n_allocs(const Params &p, const Interval &iv, const Task &T, const S
 MBK_DEV Alloc task_alloc(const Params &p, const Interval &iv, const Task &T, const StepSplit &ss, int k) {
     Alloc A;
     if (iv.op != OP_ATTN) {
-        const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
+        const uint32_t tile_bytes = (uint32_t)iv.mat.tb;
         A.g0 = p.blob + iv.mat.off + (uint64_t)T.a * tile_bytes;
         A.b0 = (uint32_t)T.n * tile_bytes;
         A.g1 = nullptr;
@@ -780,6 +781,10 @@ MBK_DEV void split8_store(float *dst, const float *v) {
     *(u32x4 *)(dst + 4) = l;
 }
 
+// GEMV input group g of 8 values: hi/lo bf16 pairs for bf16 weights, the 8 fp32 values for fp8 weights
+// (whose products are formed in fp32 after the codes are widened).
+MBK_DEV void stage8(const Params &p, float *dst, const float *v);
+
 MBK_DEV void unpack8(const u32x4 &w, float *v) {
     v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
     v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
@@ -788,6 +793,11 @@ MBK_DEV void unpack8(const u32x4 &w, float *v) {
 MBK_DEV void store8(float *dst, const float *v) {
     *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
     *(float4 *)(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+MBK_DEV void stage8(const Params &p, float *dst, const float *v) {
+    if (p.wfmt == FMT_FP8) store8(dst, v);
+    else split8_store(dst, v);
 }
 
 // xs <- hi/lo of (v * w) for the residual stream v (tagged, or the embedding
@@ -808,7 +818,7 @@ MBK_DEV float norm_input(const Params &p, float *xs, bool from_embed, int token,
             ss += v[e] * v[e];
             v[e] *= w[e];
         }
-        split8_store(xs + 8 * g, v);
+        stage8(p, xs + 8 * g, v);
     }
     return ss;
 }
@@ -824,7 +834,7 @@ MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag
         if (tid < ng) {
             float v[8];
             poll8(p, base, tid, tag, v);
-            split8_store(xs + 8 * tid, v);
+            stage8(p, xs + 8 * tid, v);
         }
         return;
     }
@@ -839,7 +849,7 @@ MBK_DEV void plain_input(const Params &p, float *xs, uint64_t base, uint32_t tag
         poll8n<kG>(p, base, g, n, tag, v);
 #pragma unroll
         for (int i = 0; i < kG; ++i)
-            if (i < n) split8_store(xs + 8 * g[i], v[i]);
+            if (i < n) stage8(p, xs + 8 * g[i], v[i]);
     }
 }
 
@@ -896,7 +906,7 @@ MBK_DEV void merge_input(const Params &p, float *xs, uint32_t tag, int nsplit, i
         const float inv = 1.f / L;
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] *= inv;
-        split8_store(xs + 8 * u, a);
+        stage8(p, xs + 8 * u, a);
     }
 }
 
@@ -946,6 +956,49 @@ MBK_DEV float gemv_tile(const MatGeom &g, const uint8_t *wt, const float *xs) {
     if (it + 2 <= g.IT) { gemv_batch<2>(w, xs, it, g.L, kl, a); it += 2; }
     if (it < g.IT) gemv_batch<1>(w, xs, it, g.L, kl, a);
     return group_sum_n((a[0] + a[1]) + (a[2] + a[3]), g.L);
+}
+
+// fp8 tile: the same lanes and steps over groups of 16 E4M3 codes; each code is widened to fp32 by the
+// hardware conversion (OCP E4M3 on gfx950) and multiplied with the fp32 input (the products carry the
+// code's 4 significant bits times the input's 24).  The row's scale is applied by the epilogue.
+template <int B>
+MBK_DEV void gemv_batch_fp8(const u32x4 *w, const float *xs, int it, int L, int kl, float *a) {
+    u32x4 c[B];
+    float4 x[B][4];
+#pragma unroll
+    for (int u = 0; u < B; ++u) c[u] = w[(it + u) * 64];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const float4 *xv = (const float4 *)(xs + (kl + (it + u) * L) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[u][j] = xv[j];
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const uint32_t cw[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[j], false);   // codes 4j, 4j + 1
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[j], true);    // codes 4j + 2, 4j + 3
+            a[j] = fmaf(lo[0], x[u][j].x, a[j]);
+            a[j] = fmaf(lo[1], x[u][j].y, a[j]);
+            a[j] = fmaf(hi[0], x[u][j].z, a[j]);
+            a[j] = fmaf(hi[1], x[u][j].w, a[j]);
+        }
+    }
+}
+
+MBK_DEV float gemv_tile_fp8(const MatGeom &g, const uint8_t *wt, const float *xs) {
+    const int lane = threadIdx.x & 63, kl = lane & (g.L - 1);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 *w = (const u32x4 *)wt + lane;
+    int it = 0;
+    for (; it + 4 <= g.IT; it += 4) gemv_batch_fp8<4>(w, xs, it, g.L, kl, a);
+    if (it + 2 <= g.IT) { gemv_batch_fp8<2>(w, xs, it, g.L, kl, a); it += 2; }
+    if (it < g.IT) gemv_batch_fp8<1>(w, xs, it, g.L, kl, a);
+    // the row's power-of-two scale, from the tile's scale block
+    const float scale = ((const float *)(wt + g.IT * 1024))[lane >> (6 - g.lrt)];
+    return group_sum_n((a[0] + a[1]) + (a[2] + a[3]), g.L) * scale;
 }
 
 // ---- GEMV epilogues (per tile; row sums in every lane of the row) ------------------------------------
@@ -1017,7 +1070,7 @@ MBK_DEV void gemv_tile_op(const Params &p, const Interval &iv, const uint8_t *ld
                           StepCtx &sc, uint32_t tag) {
     const MatGeom &g = iv.mat;
     const float *xs = (const float *)(lds + p.lds_xs + sc.in);
-    float y = gemv_tile(g, wt, xs) * sc.rnorm;
+    float y = (g.fmt == FMT_FP8 ? gemv_tile_fp8(g, wt, xs) : gemv_tile(g, wt, xs)) * sc.rnorm;
     const int lane = threadIdx.x & 63;
     const int row = t * g.RT + (lane >> (6 - g.lrt));
     const bool lead = (lane & (g.L - 1)) == 0 && row < g.rows;
@@ -1085,7 +1138,7 @@ MBK_DEV float gemv_inputs(const Params &p, const Interval &iv, const Task &T, in
     float *xs = (float *)(lds + p.lds_xs + sc.in);
     const uint32_t xtag = iv.x_src < 0 ? 0u : tag_of(sc.tag0, iv.x_src);
     // groups past the input (padding of widened tiles) are zero
-    for (int g = iv.mat.K / 8 + tid; g < iv.mat.IT * iv.mat.L; g += nt) {
+    for (int g = iv.mat.K / 8 + tid; g < iv.mat.IT * iv.mat.L * (iv.mat.gv / 8); g += nt) {
         *(u32x4 *)(xs + 8 * g) = (u32x4){0u, 0u, 0u, 0u};
         *(u32x4 *)(xs + 8 * g + 4) = (u32x4){0u, 0u, 0u, 0u};
     }
@@ -1529,7 +1582,7 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
                 // task are usually complete by then
                 read_prog(ctl, rp.seen);
                 interval_inputs<G>(p, iv, T, ivi, lds, ctl, sc);
-                const uint32_t tile_bytes = (uint32_t)iv.mat.IT * kChunk;
+                const uint32_t tile_bytes = (uint32_t)iv.mat.tb;
                 for (;;) {
                     if (T.iv != ivi) T = task_at(p, lds, k);  // further runs of the interval
                     const Alloc A = task_alloc(p, iv, T, sc.ss, 0);

@@ -24,13 +24,19 @@ constexpr int kChunk = 1024;           // bytes one wave moves with one 16-byte-
 enum Op : int32_t { OP_QKV = 0, OP_ATTN = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4, OP_LMHEAD = 5 };
 enum MatKind : int32_t { MAT_PLAIN = 0, MAT_QKV = 1, MAT_GATEUP = 2 };
 
-// A packed bf16 matrix.  Rows (in packed order) are grouped in tiles of RT
-// rows; each row's K inputs are split in 8-element groups (16 bytes) spread
-// over L = 64 / RT lanes.  Chunk (tile t, step it, lane l) holds the 8 values
+// Weight storage formats: bf16, or OCP E4M3 8-bit codes with one
+// power-of-two scale per row (fp32, in a block after each tile's codes).
+enum WeightFmt : int32_t { FMT_BF16 = 0, FMT_FP8 = 1 };
+
+// A packed matrix.  Rows (in packed order) are grouped in tiles of RT rows;
+// each row's K inputs are split in groups of gv values (one 16-byte group:
+// 8 bf16 or 16 fp8 codes) spread over L = 64 / RT lanes.  Chunk (tile t,
+// step it, lane l) holds the group
 //   packed row  t*RT + l / L,   input group  kg = (l % L) + it * L
-// and sits at byte  off + ((t * IT + it) * 64 + l) * 16,  IT * L >= K / 8
-// (groups from K / 8 on are zero padding).  So every wave-wide 16-byte load
-// of one step reads 1 KiB of contiguous memory.
+// at byte  off + t * tb + (it * 64 + l) * 16,  IT * L >= K / gv (groups
+// from K / gv on are zero padding).  So every wave-wide 16-byte load of one
+// step reads 1 KiB of contiguous memory.  A tile is tb bytes: its IT KiB of
+// groups, then (fp8) the fp32 scales of its RT rows at byte IT * 1024.
 struct MatGeom {
     uint64_t off;    // byte offset in the packed blob
     int32_t rows;    // packed rows = ntiles * RT (rows >= logical rows)
@@ -39,10 +45,14 @@ struct MatGeom {
     int32_t ntiles;
     int32_t kind;    // MatKind: how packed rows map to source rows
     int32_t lrt;     // log2(RT)
+    int32_t fmt;     // WeightFmt
+    int32_t gv;      // values per 16-byte group: 8 (bf16) or 16 (fp8)
+    int32_t tb;      // bytes per tile
+    int32_t pad_;
 };
 
 MBK_HD uint64_t chunk_offset(const MatGeom &g, int64_t tile, int it, int lane) {
-    return g.off + ((uint64_t)(tile * g.IT + it) * 64u + (uint64_t)lane) * 16u;
+    return g.off + (uint64_t)tile * (uint64_t)g.tb + ((uint64_t)it * 64u + (uint64_t)lane) * 16u;
 }
 
 // Byte offset of the 16-byte group kg of packed row r.
@@ -53,12 +63,22 @@ MBK_HD uint64_t row_group_offset(const MatGeom &g, int64_t r, int kg) {
     return chunk_offset(g, t, it, rr * g.L + kl);
 }
 
-// Geometry rule: L is the largest power of two <= 64 dividing K/8; operators
+// Byte offset of the fp32 scale of packed row r (fp8 matrices).
+MBK_HD uint64_t row_scale_offset(const MatGeom &g, int64_t r) {
+    return g.off + (uint64_t)(r / g.RT) * (uint64_t)g.tb + (uint64_t)g.IT * 1024u + (uint64_t)(r % g.RT) * 4u;
+}
+
+// Bytes of one tile: IT KiB of groups, plus the scale block of an fp8 tile (RT floats, 16-byte padded).
+MBK_HD int tile_bytes_of(int fmt, int IT, int RT) {
+    return IT * 1024 + (fmt == FMT_FP8 ? (RT * 4 + 15) / 16 * 16 : 0);
+}
+
+// Geometry rule: L is the largest power of two <= 64 dividing K/gv; operators
 // whose epilogue combines two adjacent packed rows (RoPE pairs, gate/up
 // pairs) need RT >= 2, so their L is capped at 32.  The planner may widen L
 // for operators with few tiles (see make_geom).
-MBK_HD void choose_lanes(int K, bool pairs, int *L, int *RT) {
-    int kg = K / 8, l = 1;
+MBK_HD void choose_lanes(int K, int gv, bool pairs, int *L, int *RT) {
+    int kg = K / gv, l = 1;
     while (l < 64 && kg % (l * 2) == 0) l *= 2;
     if (pairs && l > 32) l = 32;
     *L = l;

@@ -101,7 +101,86 @@ __global__ void k_pack(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16
             const uint16_t *src = s.which == 0 ? s0 : (s.which == 1 ? s1 : s2);
             v = *(const u32x4 *)(src + (uint64_t)s.row * g.K + (uint64_t)kg * 8u);
         }
-        *(u32x4 *)(dst + g.off + c * 16u) = v;
+        *(u32x4 *)(dst + chunk_offset(g, t, it, lane)) = v;
+    }
+}
+
+// OCP E4M3 code of a finite x with |x| <= 448, rounded to nearest, ties to even (sign kept, zero
+// included).  Below 2^-6 the values are the multiples of 2^-9 (the subnormals; 8 * 2^-9 is the smallest
+// normal, code 8); above, the fp32 mantissa is rounded to 3 bits and the exponent rebiased from 127 to 7.
+__device__ uint32_t e4m3_rne(float x) {
+    const uint32_t b = __float_as_uint(x), s = (b >> 24) & 0x80u, a = b & 0x7fffffffu;
+    if (a < 0x3c800000u) return s | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) & ~0xfffffu;
+    return s | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// Scale 2^e of an fp8 row with largest magnitude amax: e the smallest integer >= -126 with
+// amax / 2^e <= 448 = 1.75 * 2^8 (1 for a zero row).  For amax = 1.m * 2^E: e = E - 8 when 1.m <= 1.75,
+// else E - 7.
+__device__ float fp8_row_scale(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (b == 0u) return 1.0f;
+    const int E = (int)(b >> 23) - 127;
+    int e = (b & 0x7fffffu) <= 0x600000u ? E - 8 : E - 7;
+    if ((b >> 23) == 0u || e < -126) e = -126;
+    return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+MBK_DEV const uint16_t *source_row(const MatGeom &g, int64_t prow, const uint16_t *s0, const uint16_t *s1,
+                                   const uint16_t *s2, int hd, int nq_rows, int nkv_rows) {
+    const RowSrc s = packed_row_source(g.kind, (int)prow, hd, nq_rows, nkv_rows);
+    return (s.which == 0 ? s0 : (s.which == 1 ? s1 : s2)) + (uint64_t)s.row * g.K;
+}
+
+// Scale blocks of an fp8 matrix: one thread per fp32 slot (the scale of a row, or zero padding).
+__global__ void k_pack_scale(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16_t *s1, const uint16_t *s2,
+                             int hd, int nq_rows, int nkv_rows) {
+    const int per = (g.tb - g.IT * 1024) / 4;
+    const uint64_t n = (uint64_t)g.ntiles * per;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        const int64_t t = (int64_t)(i / (uint64_t)per);
+        const int slot = (int)(i % (uint64_t)per);
+        const int64_t prow = t * g.RT + slot;
+        float v = 0.f;
+        if (slot < g.RT && prow < g.rows) {
+            const uint16_t *src = source_row(g, prow, s0, s1, s2, hd, nq_rows, nkv_rows);
+            float amax = 0.f;
+            for (int k = 0; k < g.K; ++k) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)src[k] << 16)));
+            v = fp8_row_scale(amax);
+        }
+        *(float *)(dst + g.off + (uint64_t)t * g.tb + (uint64_t)g.IT * 1024u + (uint64_t)slot * 4u) = v;
+    }
+}
+
+// Codes of an fp8 matrix (after k_pack_scale): one thread per 16-byte chunk of 16 codes, each the bf16
+// weight divided by its row's scale (exactly: a power of two) and rounded by e4m3_rne.
+__global__ void k_pack_fp8(uint8_t *dst, MatGeom g, const uint16_t *s0, const uint16_t *s1, const uint16_t *s2, int hd,
+                           int nq_rows, int nkv_rows) {
+    const uint64_t n = (uint64_t)g.ntiles * g.IT * 64u;
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (uint64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(c % 64u);
+        const uint64_t rest = c / 64u;
+        const int it = (int)(rest % (uint64_t)g.IT);
+        const int64_t t = (int64_t)(rest / (uint64_t)g.IT);
+        const int64_t prow = t * g.RT + lane / g.L;
+        const int kg = (lane % g.L) + it * g.L;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (prow < g.rows && kg < g.K / 16) {
+            const uint16_t *src = source_row(g, prow, s0, s1, s2, hd, nq_rows, nkv_rows) + (uint64_t)kg * 16u;
+            const uint32_t sb = __float_as_uint(*(const float *)(dst + row_scale_offset(g, prow)));
+            const float inv = __uint_as_float((254u << 23) - (sb & 0x7f800000u));   // 2^-e
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                w[q] = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[q] |= e4m3_rne(__uint_as_float((uint32_t)src[4 * q + j] << 16) * inv) << (8 * j);
+            }
+            v = (u32x4){w[0], w[1], w[2], w[3]};
+        }
+        *(u32x4 *)(dst + chunk_offset(g, t, it, lane)) = v;
     }
 }
 
@@ -150,7 +229,8 @@ struct LayerPlan {
 
 struct Plan {
     std::vector<LayerPlan> layers;
-    MatGeom embed;
+    MatGeom embed;   // bf16 table of the embedding row gathers
+    MatGeom lmhead;  // vocabulary projection: the embedding itself (bf16), or its fp8 copy
     uint64_t final_norm = 0, rope = 0, table = 0, tasks = 0, task_idx = 0, total = 0;
     std::vector<Interval> iv;
     std::vector<Task> task_list;       // all workgroups' tasks, workgroup-major
@@ -193,6 +273,7 @@ struct mbk_model {
     int32_t attn_min_chunk = 128;
     int32_t n_wg_set = 0;        // mbk_set_workgroups (0: every compute unit)
     int32_t attn_items_set = 0;  // mbk_set_attention_items (0: automatic)
+    int32_t weight_fmt = 0;      // mbk_set_weight_format: FMT_BF16 or FMT_FP8
     bool kernels_ready = false;
     uint64_t *trace = nullptr;
     // graph replay of the ablation
@@ -214,10 +295,12 @@ namespace {
 // bytes.  (Measured on MI355X: one-row tiles help where they turn idle
 // workgroups into busy waves, e.g. the Qwen2-0.5B output projection; tiles of
 // 2-4 rows over more workgroups do not.)
-MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind, int n_wg) {
+MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind, int n_wg, int fmt) {
     MatGeom g{};
-    choose_lanes(K, pairs, &g.L, &g.RT);
-    const int kg = K / 8;
+    g.fmt = fmt;
+    g.gv = fmt == FMT_FP8 ? 16 : 8;
+    choose_lanes(K, g.gv, pairs, &g.L, &g.RT);
+    const int kg = K / g.gv;
     int kgp = kg;
     const int kg64 = (kg + 63) / 64 * 64;
     if (!pairs && g.L < 64 && (rows + g.RT - 1) / g.RT < n_wg && (int64_t)kg64 * 100 <= (int64_t)kg * 115) {
@@ -232,8 +315,9 @@ MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind, int n
     g.kind = kind;
     g.lrt = 0;
     while ((1 << g.lrt) < g.RT) ++g.lrt;
+    g.tb = tile_bytes_of(fmt, g.IT, g.RT);
     g.off = cursor;
-    cursor = align256(cursor + (uint64_t)g.ntiles * g.IT * 1024u);
+    cursor = align256(cursor + (uint64_t)g.ntiles * g.tb);
     return g;
 }
 
@@ -301,14 +385,17 @@ std::string build_plan(mbk_model *m) {
     Plan &P = m->plan;
     const int n_wg = m->n_wg;
     const int hd = c.head_dim, Q = c.n_heads * hd, KV = c.n_kv_heads * hd, G = c.n_heads / c.n_kv_heads;
+    if (m->weight_fmt == FMT_FP8 && (c.hidden % 16 || Q % 16 || c.intermediate % 16))
+        return "fp8 weights need hidden, heads*head_dim and intermediate to be multiples of 16";
     uint64_t cur = 0;
     P.layers.resize(c.n_layers);
     for (int l = 0; l < c.n_layers; ++l) {
         LayerPlan &L = P.layers[l];
-        L.qkv = make_geom(cur, Q + 2 * KV, c.hidden, true, MAT_QKV, n_wg);
-        L.o = make_geom(cur, c.hidden, Q, false, MAT_PLAIN, n_wg);
-        L.gu = make_geom(cur, 2 * c.intermediate, c.hidden, true, MAT_GATEUP, n_wg);
-        L.down = make_geom(cur, c.hidden, c.intermediate, false, MAT_PLAIN, n_wg);
+        const int f = m->weight_fmt;
+        L.qkv = make_geom(cur, Q + 2 * KV, c.hidden, true, MAT_QKV, n_wg, f);
+        L.o = make_geom(cur, c.hidden, Q, false, MAT_PLAIN, n_wg, f);
+        L.gu = make_geom(cur, 2 * c.intermediate, c.hidden, true, MAT_GATEUP, n_wg, f);
+        L.down = make_geom(cur, c.hidden, c.intermediate, false, MAT_PLAIN, n_wg, f);
         L.attn_norm = cur;
         cur = align256(cur + 2u * c.hidden);
         L.mlp_norm = cur;
@@ -319,7 +406,8 @@ std::string build_plan(mbk_model *m) {
             cur = align256(cur + 2u * (Q + 2 * KV));
         }
     }
-    P.embed = make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN, n_wg);
+    P.embed = make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN, n_wg, FMT_BF16);
+    P.lmhead = m->weight_fmt == FMT_FP8 ? make_geom(cur, c.vocab, c.hidden, false, MAT_PLAIN, n_wg, FMT_FP8) : P.embed;
     P.final_norm = cur;
     cur = align256(cur + 2u * c.hidden);
     P.rope = cur;
@@ -360,7 +448,7 @@ std::string build_plan(mbk_model *m) {
         P.iv.push_back(gemv_interval(OP_GATEUP, l, L.gu, L.mlp_norm, none, base + 2));
         P.iv.push_back(gemv_interval(OP_DOWN, l, L.down, none, none, base + 2));
     }
-    P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.embed, P.final_norm, none, 5 * c.n_layers - 1));
+    P.iv.push_back(gemv_interval(OP_LMHEAD, -1, P.lmhead, P.final_norm, none, 5 * c.n_layers - 1));
     const int n_iv = (int)P.iv.size();
     for (const Interval &v : P.iv)
         if (v.n_items >= (1 << 23)) return "too many tiles in one operator";
@@ -379,7 +467,7 @@ std::string build_plan(mbk_model *m) {
                 max_rows = std::max(max_rows, (block_begin(v.n_items, k + 1, v.nwg) - block_begin(v.n_items, k, v.nwg)) * v.mat.RT);
     int kmax = 8;  // longest (padded) GEMV input
     for (const Interval &v : P.iv)
-        if (v.op != OP_ATTN) kmax = std::max(kmax, v.mat.IT * v.mat.L * 8);
+        if (v.op != OP_ATTN) kmax = std::max(kmax, v.mat.IT * v.mat.L * v.mat.gv);
     size_t off = 0;
     P.lds_ivtab = (int)off; off = a16(off + (size_t)n_iv * sizeof(Interval));
     const size_t task_slot = off;
@@ -411,7 +499,7 @@ std::string build_plan(mbk_model *m) {
     // to what the lists leave.
     size_t max_tile = 0;
     for (const Interval &v : P.iv)
-        if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.IT * kChunk);
+        if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.tb);
     auto build_tasks = [&](size_t ring) {
         const size_t max_alloc = ring / 2;
         P.task_list.clear();
@@ -434,9 +522,9 @@ std::string build_plan(mbk_model *m) {
                     // multiple of kCW tiles, at least one round) of at most a third of the ring: the ring
                     // then holds three runs or more, so the bytes in flight are what the run being
                     // computed leaves free, and each run still gives every compute wave several tiles
-                    int per = std::max<int>(1, (int)(max_alloc / ((size_t)v.mat.IT * kChunk)));
+                    int per = std::max<int>(1, (int)(max_alloc / (size_t)v.mat.tb));
                     if (per >= kCW && b1 - b0 > per)
-                        per = std::max<int>(kCW, (int)(ring / 3 / ((size_t)kCW * v.mat.IT * kChunk)) * kCW);
+                        per = std::max<int>(kCW, (int)(ring / 3 / ((size_t)kCW * v.mat.tb)) * kCW);
                     for (int t = b0; t < b1; t += per)
                         P.task_list.push_back(Task{i, t, std::min(per, b1 - t), b1 << 8});
                 }
@@ -601,6 +689,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.in_bytes = P.in_bytes;
     p.in_double = P.in_double;
     p.attn_hpi = P.attn_hpi;
+    p.wfmt = m->weight_fmt;
     p.max_tasks = P.max_tasks;
     p.eps = c.rms_eps;
     p.scale = 1.0f / std::sqrt((float)c.head_dim);
@@ -646,12 +735,19 @@ int launch_persistent(const mbk_model *m, Params &p, void *stream) {
 }
 
 int pack_matrix(mbk_model *m, const MatGeom &g, const void *s0, const void *s1, const void *s2, hipStream_t st) {
-    const int hd = m->c.head_dim;
+    const int hd = m->c.head_dim, nq_rows = m->c.n_heads * hd, nkv_rows = m->c.n_kv_heads * hd;
     const uint64_t n = (uint64_t)g.ntiles * g.IT * 64u;
     const int threads = 256;
     const int blocks = (int)std::min<uint64_t>((n + threads - 1) / threads, 65536);
-    hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(threads), 0, st, m->blob, g, (const uint16_t *)s0,
-                       (const uint16_t *)s1, (const uint16_t *)s2, hd, m->c.n_heads * hd, m->c.n_kv_heads * hd);
+    const uint16_t *a = (const uint16_t *)s0, *b = (const uint16_t *)s1, *d = (const uint16_t *)s2;
+    if (g.fmt == FMT_FP8) {
+        const uint64_t ns = (uint64_t)g.ntiles * ((g.tb - g.IT * 1024) / 4);
+        const int bs = (int)std::min<uint64_t>((ns + threads - 1) / threads, 65536);
+        hipLaunchKernelGGL(k_pack_scale, dim3(bs), dim3(threads), 0, st, m->blob, g, a, b, d, hd, nq_rows, nkv_rows);
+        hipLaunchKernelGGL(k_pack_fp8, dim3(blocks), dim3(threads), 0, st, m->blob, g, a, b, d, hd, nq_rows, nkv_rows);
+    } else {
+        hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(threads), 0, st, m->blob, g, a, b, d, hd, nq_rows, nkv_rows);
+    }
     HIPCHK(hipGetLastError());
     return MBK_OK;
 }
@@ -759,6 +855,7 @@ int mbk_pack_weights(mbk_model *m, const mbk_weights *src, void *dst, size_t *ds
         }
     }
     if ((rc = pack_matrix(m, P.embed, src->embed, nullptr, nullptr, st))) return rc;
+    if (P.lmhead.off != P.embed.off && (rc = pack_matrix(m, P.lmhead, src->embed, nullptr, nullptr, st))) return rc;
     HIPCHK(hipMemcpyAsync(m->blob + P.final_norm, src->final_norm, 2u * c.hidden, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(m->blob + P.rope, m->rope_host.data(), m->rope_host.size() * 4, hipMemcpyHostToDevice, st));
     HIPCHK(hipMemcpyAsync(m->blob + P.table, P.iv.data(), P.iv.size() * sizeof(Interval), hipMemcpyHostToDevice, st));
@@ -1008,6 +1105,7 @@ int mbk_get_matrix_layout(mbk_model *m, int32_t layer, int32_t which, mbk_matrix
     const Plan &P = m->plan;
     const MatGeom *g = nullptr;
     if (layer == -1 && which == 0) g = &P.embed;
+    else if (layer == -1 && which == 1) g = &P.lmhead;
     else if (layer >= 0 && layer < m->c.n_layers && which >= 0 && which < 4) {
         const LayerPlan &L = P.layers[(size_t)layer];
         g = which == 0 ? &L.qkv : which == 1 ? &L.o : which == 2 ? &L.gu : &L.down;
@@ -1021,6 +1119,10 @@ int mbk_get_matrix_layout(mbk_model *m, int32_t layer, int32_t which, mbk_matrix
     out->steps = g->IT;
     out->tiles = g->ntiles;
     out->kind = g->kind;
+    out->format = g->fmt;
+    out->values_per_group = g->gv;
+    out->tile_bytes = g->tb;
+    out->scale_offset = g->fmt == FMT_FP8 ? g->IT * 1024 : -1;
     return MBK_OK;
 }
 
@@ -1075,6 +1177,7 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
     for (int i = 0; i < n_tokens; ++i)
         if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(MBK_ERR_ARG, "token %d at %d outside [0, %d)", tokens[i], i, c.vocab);
     if (!m->blob || !m->kv) return fail(MBK_ERR_STATE, "weights not packed or KV cache not bound");
+    if (m->weight_fmt != FMT_BF16) return fail(MBK_ERR_UNSUPPORTED, "prefill reads bf16 weights only");
     const PfLayout L = pf_layout(c, n_tokens);
     if (!scratch || scratch_bytes < L.total) return fail(MBK_ERR_SIZE, "prefill scratch %zu < %zu bytes", scratch_bytes, L.total);
     if (!aligned(scratch, 256)) return fail(MBK_ERR_ARG, "prefill scratch not 256-byte aligned");
@@ -1184,6 +1287,15 @@ int mbk_set_attention_items(mbk_model *m, int32_t heads_per_item) {
     return MBK_OK;
 }
 
+int mbk_set_weight_format(mbk_model *m, int32_t format) {
+    if (!m || (format != MBK_WEIGHTS_BF16 && format != MBK_WEIGHTS_FP8_E4M3))
+        return fail(MBK_ERR_ARG, "format must be MBK_WEIGHTS_BF16 or MBK_WEIGHTS_FP8_E4M3");
+    const int f = format == MBK_WEIGHTS_FP8_E4M3 ? FMT_FP8 : FMT_BF16;
+    if (m->planned && f != m->weight_fmt) return fail(MBK_ERR_STATE, "the schedule is already planned");
+    m->weight_fmt = f;
+    return MBK_OK;
+}
+
 int mbk_describe(mbk_model *m, char *buf, size_t len) {
     if (!m || !buf || len == 0) return fail(MBK_ERR_ARG, "bad arguments");
     int rc = ensure_plan(m);
@@ -1191,17 +1303,18 @@ int mbk_describe(mbk_model *m, char *buf, size_t len) {
     const Plan &P = m->plan;
     size_t tile_max = 0, task_max = 0;
     for (const Interval &v : P.iv)
-        if (v.op != OP_ATTN) tile_max = std::max(tile_max, (size_t)v.mat.IT * kChunk);
+        if (v.op != OP_ATTN) tile_max = std::max(tile_max, (size_t)v.mat.tb);
     for (const Task &t : P.task_list)
-        if (P.iv[t.iv].op != OP_ATTN) task_max = std::max(task_max, (size_t)t.n * P.iv[t.iv].mat.IT * kChunk);
+        if (P.iv[t.iv].op != OP_ATTN) task_max = std::max(task_max, (size_t)t.n * P.iv[t.iv].mat.tb);
     const int n = snprintf(buf, len,
         "{\"workgroups\": %d, \"threads\": %d, \"compute_waves\": %d, \"loader_waves\": %d, \"intervals\": %zu, "
         "\"packed_bytes\": %llu, \"workspace_bytes\": %llu, \"lds_bytes\": %zu, \"ring_bytes\": %d, "
         "\"max_tasks\": %d, \"tasks\": %zu, \"max_task_bytes\": %zu, \"max_tile_bytes\": %zu, "
-        "\"max_splits\": %d, \"piece_positions\": %d, \"double_inputs\": %d, \"attention_heads_per_item\": %d}",
+        "\"max_splits\": %d, \"piece_positions\": %d, \"double_inputs\": %d, \"attention_heads_per_item\": %d, "
+        "\"weight_format\": \"%s\"}",
         m->n_wg, kThreads, kCW, kLW, P.iv.size(), (unsigned long long)P.total, (unsigned long long)P.ws.total,
         P.lds_bytes, P.ring_bytes, P.max_tasks, P.task_list.size(), task_max, tile_max, P.max_splits, P.piece_pos, P.in_double,
-        P.attn_hpi);
+        P.attn_hpi, m->weight_fmt == FMT_FP8 ? "fp8_e4m3" : "bf16");
     if (n < 0 || (size_t)n >= len) return fail(MBK_ERR_SIZE, "description needs %d bytes", n + 1);
     return MBK_OK;
 }

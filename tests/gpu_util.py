@@ -61,8 +61,9 @@ def kv_slot_check(gpu: np.ndarray, want: np.ndarray):
 class Pair:
     """A GPU decoder and the oracle on the same workload, weights and KV prefix."""
 
-    def __init__(self, wl, W=None, kv_prefix=None, setup=None):
-        """setup(decoder), if given, runs before the weights are packed (plan-time settings)."""
+    def __init__(self, wl, W=None, kv_prefix=None, setup=None, oracle_W=None):
+        """setup(decoder), if given, runs before the weights are packed (plan-time settings); oracle_W,
+        if given, are the weights the oracle runs (the model the packed weights stand for)."""
         import torch
         from persistent_megakernel_decode_wg_amd import Decoder
         from persistent_megakernel_decode_wg_amd import build as mbk_build
@@ -74,7 +75,7 @@ class Pair:
             setup(self.dec)
         self.dec.pack_weights(upload(self.W))
         self.dec.alloc_kv()
-        self.ref = oracle.Model(wl, self.W)
+        self.ref = oracle.Model(wl, self.W if oracle_W is None else oracle_W)
         if kv_prefix is not None:
             P = kv_prefix.shape[3]
             self.dec.kv[:, :, :, :P, :] = torch.from_numpy(np.ascontiguousarray(kv_prefix).view(np.int16)).cuda()
