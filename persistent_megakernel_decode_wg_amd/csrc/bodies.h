@@ -51,8 +51,14 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kBatch = 8;                          // loader: chunks per wave between progress updates
-constexpr int kInflight = 24;                      // loader: chunks per wave left in flight (3 batches)
+// Loader pacing.  A loader wave learns that a chunk has landed only by waiting for its count of
+// outstanding loads, so the chunks it reports complete lag the chunks it has issued by the number it keeps
+// in flight; the compute waves can use only reported chunks.  The window is a trade: more chunks in
+// flight per wave stream faster, but hold back more of the ring from the compute waves (measured on
+// MI355X with the SmolLM-1.7B shape: 8 in flight, reported every 4, beat 24 and 8 by 9 %; 4 or 16 in
+// flight were slower).
+constexpr int kBatch = 4;                          // loader: chunks per wave between progress updates
+constexpr int kInflight = 8;                       // loader: chunks per wave left in flight (2 batches)
 constexpr uint32_t kCacheSc1 = 16;                 // cache-policy bits: device-coherent access
 
 // Per-launch parameters (kernel argument, passed by value).
@@ -596,13 +602,14 @@ MBK_DEV void dma_segment(const uint8_t *src, uint8_t *dst, uint32_t bytes, int l
     const int lane = threadIdx.x & 63;
     const int full = (int)(bytes / kChunk);
     const uint8_t *g = src + lane * 16;
+    static_assert(kInflight == 8, "the wait below names kInflight");
     for (int c = lw; c < full; c += kLW) {
         __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)c * kChunk), (lds_void_t *)(dst + c * kChunk), 16, 0,
                                          SC1 ? (int)kCacheSc1 : 0);
         ++issued;
         if (++inbatch == kBatch) {
             inbatch = 0;
-            asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // kInflight
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // kInflight
             if (issued - (uint32_t)kInflight > published && issued > (uint32_t)kInflight) {
                 published = issued - (uint32_t)kInflight;
                 lds_st_opaque(&ctl.prog[lw], published);
