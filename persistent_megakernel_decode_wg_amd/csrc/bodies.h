@@ -82,7 +82,7 @@ struct Params {
     int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
     int32_t wfmt;             // WeightFmt of the projection matrices: GEMV inputs are hi/lo bf16 (bf16) or fp32 (fp8)
     // LDS offsets in bytes of the dynamic area
-    int32_t lds_ivtab, lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_ring;
+    int32_t lds_tasks, lds_rope, lds_qkv, lds_bias, lds_xs, lds_xres, lds_attn, lds_ring;
     int32_t ring_bytes, max_tasks;
     int32_t in_bytes, in_double;  // LDS input block [qkv | bias | xs | xres] size; 1: two copies used in turn
     float eps, scale;         // RMSNorm eps, 1/sqrt(head_dim)
@@ -562,20 +562,17 @@ MBK_DEV uint32_t ring_place(RingCursor &c, uint32_t size, uint32_t R) {
 
 // ---- loader waves ------------------------------------------------------------------------------------
 
-// Interval descriptor from the LDS table, read opaquely (loader waves).
-MBK_DEV Interval interval_opaque(const Params &p, const uint8_t *lds, int ivi) {
+// Interval descriptor ivi (uniform) from the table in the blob, through the constant address space: the
+// kernels never write the table, so these are scalar loads through the scalar cache, which keeps the
+// table out of LDS (the ring gets the space) and, in the loader waves, out of the count of outstanding
+// vector loads.
+MBK_DEV Interval interval_at(const Params &p, int ivi) {
     static_assert(sizeof(Interval) % 16 == 0, "interval size");
-    constexpr int nq = (int)(sizeof(Interval) / 16);
-    u32x4 w[nq];
-    const uint8_t *src = lds + p.lds_ivtab + (size_t)ivi * sizeof(Interval);
+    constexpr int nw = (int)(sizeof(Interval) / 4);
+    const auto *src = (__attribute__((address_space(4))) const uint32_t *)p.iv + ivi * nw;
+    uint32_t w[nw];
 #pragma unroll
-    for (int i = 0; i < nq; ++i) {
-        w[i] = lds_ld16_opaque(src + 16 * i);
-        w[i].x = __builtin_amdgcn_readfirstlane(w[i].x);
-        w[i].y = __builtin_amdgcn_readfirstlane(w[i].y);
-        w[i].z = __builtin_amdgcn_readfirstlane(w[i].z);
-        w[i].w = __builtin_amdgcn_readfirstlane(w[i].w);
-    }
+    for (int i = 0; i < nw; ++i) w[i] = src[i];
     Interval v;
     __builtin_memcpy(&v, w, sizeof v);
     return v;
@@ -639,7 +636,7 @@ MBK_DEV void loader(const Params &p, uint8_t *lds, Ctl &ctl, int nt, int pos) {
     for (int k = 0; k < nt; ++k) {
         const Task T = task_opaque(lds, p, k);
         if (T.iv != cur) {
-            iv = interval_opaque(p, lds, T.iv);
+            iv = interval_at(p, T.iv);
             cur = T.iv;
         }
         const int na = n_allocs(p, iv, T, ss);
@@ -1485,17 +1482,6 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
 
 // ---- compute waves: the interval loop -----------------------------------------------------------------
 
-MBK_DEV Interval interval_at(const Params &p, const uint8_t *lds, int ivi) {
-    constexpr int nw = (int)(sizeof(Interval) / 4);
-    const uint32_t *src = (const uint32_t *)(lds + p.lds_ivtab) + ivi * nw;
-    uint32_t w[nw];
-#pragma unroll
-    for (int i = 0; i < nw; ++i) w[i] = __builtin_amdgcn_readfirstlane(src[i]);
-    Interval v;
-    __builtin_memcpy(&v, w, sizeof v);
-    return v;
-}
-
 MBK_DEV Task task_at(const Params &p, const uint8_t *lds, int k) {
     const int32_t *src = (const int32_t *)(lds + p.lds_tasks) + 4 * k;
     Task t;
@@ -1561,7 +1547,7 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
         if ((int)blockIdx.x == p.skip_wg && ivi == p.skip_interval) return false;
         const int tiv = k < nt ? task_at(p, lds, k).iv : -1;
         if (tiv == ivi) {
-            const Interval iv = interval_at(p, lds, ivi);
+            const Interval iv = interval_at(p, ivi);
             stamp(p, lds, ivi, 0);
             const uint32_t tag = tag_of(sc.tag0, ivi);
             if (iv.op == OP_ATTN) {
@@ -1611,14 +1597,10 @@ MBK_DEV bool compute(const Params &p0, uint8_t *lds, Ctl &ctl, int nt, StepCtx &
 
 // ---- launch prologue -------------------------------------------------------------------------
 
-// Copies the interval table, this workgroup's tasks of [first_iv, last_iv)
-// and this step's RoPE row into LDS and clears the control words.  Returns
-// the number of tasks.  All threads.
+// Copies this workgroup's tasks of [first_iv, last_iv) and this step's RoPE
+// row into LDS and clears the control words.  Returns the number of tasks.
+// All threads.
 MBK_DEV int prologue(const Params &p, uint8_t *lds, Ctl &ctl, int pos) {
-    const uint32_t *ivs = (const uint32_t *)p.iv;
-    uint32_t *ivd = (uint32_t *)(lds + p.lds_ivtab);
-    const int nw = p.n_intervals * (int)(sizeof(Interval) / 4);
-    for (int i = threadIdx.x; i < nw; i += kThreads) ivd[i] = ivs[i];
     const int32_t *ti = p.task_idx + (size_t)blockIdx.x * (p.n_intervals + 1);
     const int k0 = ti[p.first_iv], k1 = ti[p.last_iv];
     const int nt = min(k1 - k0, p.max_tasks);

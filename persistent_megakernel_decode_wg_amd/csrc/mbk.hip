@@ -237,7 +237,7 @@ struct Plan {
     std::vector<int32_t> task_index;   // [n_wg][n_iv + 1]
     int max_splits = 1, piece_pos = 1, max_tasks = 0, in_bytes = 0, in_double = 0, attn_hpi = 1;
     // LDS layout (bytes of the dynamic area)
-    int lds_ivtab = 0, lds_tasks = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
+    int lds_tasks = 0, lds_rope = 0, lds_qkv = 0, lds_bias = 0, lds_xs = 0,
         lds_xres = 0, lds_attn = 0, lds_ring = 0, ring_bytes = 0;
     size_t lds_bytes = 0;
     WsLayout ws{};
@@ -469,7 +469,6 @@ std::string build_plan(mbk_model *m) {
     for (const Interval &v : P.iv)
         if (v.op != OP_ATTN) kmax = std::max(kmax, v.mat.IT * v.mat.L * v.mat.gv);
     size_t off = 0;
-    P.lds_ivtab = (int)off; off = a16(off + (size_t)n_iv * sizeof(Interval));
     const size_t task_slot = off;
     // tasks are laid out below, once their count is known; reserve after the fixed parts
     P.lds_rope = 0;
@@ -676,7 +675,6 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
     p.piece_pos = P.piece_pos;
     p.hd_shift = 0;
     while ((1 << p.hd_shift) < c.head_dim) ++p.hd_shift;
-    p.lds_ivtab = P.lds_ivtab;
     p.lds_tasks = P.lds_tasks;
     p.lds_rope = P.lds_rope;
     p.lds_qkv = P.lds_qkv;
