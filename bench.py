@@ -197,8 +197,10 @@ def prefill_summary(wl, n: int, decode_us: float, reps: int = 5):
     torch.cuda.empty_cache()
     t = pct(us, 0.5)
     fl = prefill_flops(wl, n)
-    return {"tokens": n, "us_p50": round(t, 1), "us_per_token": round(t / n, 2), "tok_s": round(n / t * 1e6, 1),
-            "decode_steps_us": round(decode_us * n, 1), "speedup_over_decode_steps": round(decode_us * n / t, 2),
+    res = {"tokens": n, "us_p50": round(t, 1), "us_per_token": round(t / n, 2), "tok_s": round(n / t * 1e6, 1)}
+    if decode_us is not None:
+        res.update({"decode_steps_us": round(decode_us * n, 1), "speedup_over_decode_steps": round(decode_us * n / t, 2)})
+    return {**res,
             "algorithmic_tflops": round(fl / t * 1e-6, 2), "frac_of_bf16_mfma_peak": round(fl / t * 1e-6 / 2500.0, 4)}
 
 
@@ -279,6 +281,10 @@ def main():
                     help="skip the per-config summary of every workload (extra.configs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--weights", choices=["bf16", "fp8"], default="bf16",
+                    help="weight storage of the timed decoder: bf16, or OCP E4M3 codes with per-row scales")
+    ap.add_argument("--prefill-tokens", type=int, default=0, metavar="N",
+                    help="time only a prefill of N tokens of the workload (one JSON line, no decode steps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -295,7 +301,12 @@ def main():
     mbk_build.ensure_built()
     torch.cuda.set_device(0)
     wl = synth.get(args.workload)
-    dec, W, logits, am, g0, g1 = setup_workload(wl)
+    if args.prefill_tokens:
+        res = prefill_summary(wl, args.prefill_tokens, None)
+        print(json.dumps({"metric": "prefill us (one call)", "workload": wl.name, **res}), flush=True)
+        return
+    fp8 = args.weights == "fp8"
+    dec, W, logits, am, g0, g1 = setup_workload(wl, fp8=fp8)
     if args.attn_split:
         dec.set_attention_split(args.attn_split)
     sync_modes = {"dataflow": MBK_SYNC_DATAFLOW, "barrier": MBK_SYNC_BARRIER}
@@ -328,7 +339,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     mean_kern_us = sum(kern_us) / K
-    bytes_mean = sum(algorithmic_bytes(wl, positions(i)) for i in range(K)) / K
+    bytes_mean = sum(algorithmic_bytes(wl, positions(i), fp8=fp8) for i in range(K)) / K
     achieved = bytes_mean / (mean_kern_us * 1e-6) / 1e9
 
     # complete synchronized call (host + GPU), as the pages' leaderboard measures
@@ -430,7 +441,8 @@ def main():
 
     # HBM bytes per launch from the committed counter summary, while it matches these kernel sources
     from persistent_megakernel_decode_wg_amd import profile_traffic
-    rec = profile_traffic.read(os.path.join(ROOT, "profiles", "traffic_k_persistent_%s.md" % wl.name))
+    rec = profile_traffic.read(os.path.join(ROOT, "profiles", "traffic_k_persistent_%s%s.md"
+                                            % (wl.name, "-fp8" if fp8 else "")))
     traffic = round(rec["traffic_bytes"]) if rec else None
     if rec:
         extra["traffic_fetch_bytes"] = round(rec["fetch_bytes"])
@@ -462,11 +474,12 @@ def main():
         "metric": "batch-1 decode tok/s (us/token) + achieved HBM GB/s vs 8 TB/s peak, 1 GPU",
         "value": round(K / elapsed, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(elapsed / K * 1e3, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights)",
+        "vs_baseline": None, "dtype": "fp8-e4m3 weights, f32 products" if fp8 else "bf16",
+        "data": "synthetic (seeded random-init weights)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": wl.n_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "intermediate": wl.intermediate,
                    "vocab": wl.vocab, "kv_capacity": wl.kv_capacity, "batch": 1,
-                   "positions": timed, "parallelism": "none (1 GPU)"},
+                   "positions": timed, "weights": args.weights, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
