@@ -320,6 +320,147 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfParams p, int layer, int dst)
     }
 }
 
+// Causal attention on the matrix cores, head size HD (a multiple of 32): one wave per workgroup takes
+// queries q0 .. q0 + 15 (prompt positions pos0 + q0 ..) of head h; keys in blocks of 32 aligned at cache
+// position 0.  Scores as S^T = K Q^T: operand A is 16 cached keys x 32 head dims (16 contiguous bytes of
+// a key row per lane, read straight from the cache), operand B the 16 queries' 32 dims as hi/lo bf16 pairs
+// (held in registers, pre-scaled); lane (g = l / 16, c = l % 16) gets keys 4 g + r of each 16-key tile for
+// query c.  Online softmax per query over the lane's 8 keys and the 4 lane groups of its column (a block
+// wholly past a query's position leaves its state exactly unchanged).  Weighted values as O^T = V^T P^T:
+// operand B is exactly those 8 probabilities per lane (hi/lo pairs; the order of the 32 keys in the
+// contraction is the lanes' own: tile 0 keys 4 g .. 4 g + 3, then tile 1's), operand A the values of the
+// same keys at 16 head dims, read from the block's values staged transposed in LDS.  Lane (g, c), register
+// r of output tile dt holds query c, dim 16 dt + 4 g + r.  Output hi/lo into input buffer dst.
+template <int HD>
+__global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int dst) {
+    constexpr int KS = HD / 32, DT = HD / 16, VR = 32 + 4;   // score k steps, output tiles, V^T row (bf16)
+    __shared__ uint16_t vt[HD * VR];
+    const int l = threadIdx.x, g = l >> 4, c = l & 15;
+    const int h = blockIdx.y, j = h / p.gqa, q0 = blockIdx.x * 16;
+    const int nqb = min(16, p.P - q0);
+    const int qc = min(c, nqb - 1);                 // padding columns repeat the last query (never stored)
+    const int qpos = p.pos0 + q0 + qc;              // keys 0 .. qpos for this lane's query
+    const int Lmax = p.pos0 + q0 + nqb;             // keys the block's last query sees
+    pf_bf16x8 qh[KS], ql[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float *qr = p.q + (size_t)(q0 + qc) * p.nq * HD + h * HD + 32 * s + 8 * g;
+        uint16_t hb[8], lb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = qr[e] * p.scale;
+            hb[e] = pf_to_bf16(v);
+            lb[e] = pf_to_bf16(v - pf_bf16f(hb[e]));
+        }
+        qh[s] = __builtin_bit_cast(pf_bf16x8, hb);
+        ql[s] = __builtin_bit_cast(pf_bf16x8, lb);
+    }
+    const uint16_t *K = p.kv + (((size_t)layer * 2 + 0) * p.nkv + j) * p.S * HD;
+    const uint16_t *V = p.kv + (((size_t)layer * 2 + 1) * p.nkv + j) * p.S * HD;
+    float M = -INFINITY, Ls = 0.f;
+    pf_f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
+    // a block's keys (operand A tiles) and values (the lane's 16-byte chunks), loaded one block ahead
+    constexpr int VC = HD / 16;                     // value chunks per lane and block
+    pf_u32x4 kw[2][KS], vw[VC];
+    auto load_block = [&](int t0) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const int key = t0 + 16 * tau + c;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                kw[tau][s] = (pf_u32x4){0u, 0u, 0u, 0u};
+                if (key < Lmax) kw[tau][s] = *(const pf_u32x4 *)(K + (size_t)key * HD + 32 * s + 8 * g);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < VC; ++u) {
+            const int ci = l + 64 * u, key = ci / (HD / 8), dc = ci % (HD / 8);
+            vw[u] = (pf_u32x4){0u, 0u, 0u, 0u};
+            if (t0 + key < Lmax) vw[u] = *(const pf_u32x4 *)(V + (size_t)(t0 + key) * HD + 8 * dc);
+        }
+    };
+    load_block(0);
+    for (int t0 = 0; t0 < Lmax; t0 += 32) {
+        // this block's values, transposed: vt[d][key] (keys past the last query's position are zero)
+#pragma unroll
+        for (int u = 0; u < VC; ++u) {
+            const int ci = l + 64 * u, key = ci / (HD / 8), dc = ci % (HD / 8);
+            const uint32_t ww[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vt[(8 * dc + 2 * e) * VR + key] = (uint16_t)(ww[e] & 0xffffu);
+                vt[(8 * dc + 2 * e + 1) * VR + key] = (uint16_t)(ww[e] >> 16);
+            }
+        }
+        // scores of keys t0 + 16 tau + 4 g + r for query c
+        float sc[2][4];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            pf_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const pf_bf16x8 a = __builtin_bit_cast(pf_bf16x8, kw[tau][s]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[s], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[tau][r] = t0 + 16 * tau + 4 * g + r <= qpos ? acc[r] : -INFINITY;
+        }
+        if (t0 + 32 < Lmax) load_block(t0 + 32);   // the next block's loads overlap this block's math
+        float mb = sc[0][0];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sc[tau][r]);
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mn = fmaxf(M, mb);
+        const float cf = M == -INFINITY ? 0.f : __expf(M - mn);
+        float pw[8], sb = 0.f;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = sc[tau][r] == -INFINITY ? 0.f : __expf(sc[tau][r] - mn);
+                pw[4 * tau + r] = v;
+                sb += v;
+            }
+        sb += __shfl_xor(sb, 16);
+        sb += __shfl_xor(sb, 32);
+        Ls = Ls * cf + sb;
+        M = mn;
+        uint16_t ph[8], pl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ph[e] = pf_to_bf16(pw[e]);
+            pl[e] = pf_to_bf16(pw[e] - pf_bf16f(ph[e]));
+        }
+        const pf_bf16x8 bh = __builtin_bit_cast(pf_bf16x8, ph), bl = __builtin_bit_cast(pf_bf16x8, pl);
+        __syncthreads();
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t *row = vt + (16 * dt + c) * VR;
+            const uint2 v0 = *(const uint2 *)(row + 4 * g), v1 = *(const uint2 *)(row + 16 + 4 * g);
+            const pf_u32x4 vw = {v0.x, v0.y, v1.x, v1.y};
+            const pf_bf16x8 a = __builtin_bit_cast(pf_bf16x8, vw);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] *= cf;
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, o[dt], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    if (c >= nqb) return;
+    const float inv = 1.f / Ls;
+    uint16_t *dh = p.inh[dst] + (size_t)(q0 + c) * p.ks + h * HD, *dl = p.inl[dst] + (size_t)(q0 + c) * p.ks + h * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pf_store_split(dh, dl, 16 * dt + 4 * g + r, o[dt][r] * inv);
+}
+
 // Greedy argmax of the V logits (lowest index among equal maxima); also the decode step's previous token.
 __global__ __launch_bounds__(1024) void k_pf_argmax(PfParams p) {
     __shared__ float bv[1024];
