@@ -97,34 +97,87 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
 }
 
 // C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  One wave per workgroup: packed rows
-// [16 bx, 16 bx + 16) and positions [32 by, 32 by + 32) of input buffer `src` (np_rows rows in all, a
-// multiple of 16).  Lane l feeds row l % 16 of each operand with input group 4 s + l / 16 of k step s (32
-// inputs); the k steps go in batches of 8 whose weight and activation loads are all issued before the
-// batch's products, so a batch costs one memory latency rather than eight.  After the k loop lane l holds
-// C[32 by + 16 j + 4 (l / 16) + r][16 bx + l % 16] in acc[j][r].  Epilogue by op.
-constexpr int kPfRows = 16, kPfPos = 32, kPfBatch = 8;
+// [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [32 by, 32 by + 32) (two position blocks)
+// of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds RB matrix
+// products and every weight load two.  RB = 4 where that still leaves enough workgroups to fill the device,
+// else 1.  Lane l feeds row l % 16 of each operand with input group 4 s + l / 16 of k step s (32 inputs); the
+// k steps go in batches (8 with one row block, 4 with four) whose loads are all issued before the batch's
+// products.  After the k loop lane
+// l holds C[32 by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
+constexpr int kPfPos = 32;
 template <int OP>
+__device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g, int layer, int dst, uint64_t bias_off,
+                                            int n, int pos, float y) {
+    const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
+    const bool nrow = n < g.rows;
+    if (OP == OP_QKV) {
+        // packed rows 2m, 2m+1 of a query or key head are its dims m, m + hd/2 (adjacent lanes)
+        const int which = n >= Q + KVr ? 2 : (n >= Q ? 1 : 0);
+        const int base = n - (which == 0 ? 0 : (which == 1 ? Q : Q + KVr));
+        const int i = base & (hd - 1);
+        const int srow = which == 2 ? base : (base & ~(hd - 1)) + ((i & 1) ? (i >> 1) + half : (i >> 1));
+        if (bias_off != ~(uint64_t)0 && nrow)
+            y += pf_bf16f(((const uint16_t *)(p.blob + bias_off))[(which == 0 ? 0 : (which == 1 ? Q : Q + KVr)) + srow]);
+        const float partner = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
+        if (!nrow || pos >= p.P) return;
+        const int slot = p.pos0 + pos;
+        if (which == 2) {
+            const int jh = srow >> p.hd_shift, d = srow & (hd - 1);
+            p.kv[((((size_t)layer * 2 + 1) * p.nkv + jh) * p.S + slot) * hd + d] = pf_to_bf16(y);
+            return;
+        }
+        if (i & 1) return;  // the odd row is the partner of this pair
+        const int h = srow >> p.hd_shift, m = srow & (hd - 1);
+        const float2 cs = ((const float2 *)(p.blob + p.rope))[(size_t)slot * half + m];
+        const float r0 = y * cs.x - partner * cs.y, r1 = partner * cs.x + y * cs.y;
+        if (which == 0) {
+            p.q[(size_t)pos * Q + h * hd + m] = r0;
+            p.q[(size_t)pos * Q + h * hd + m + half] = r1;
+        } else {
+            uint16_t *kc = p.kv + ((((size_t)layer * 2 + 0) * p.nkv + h) * p.S + slot) * hd;
+            kc[m] = pf_to_bf16(r0);
+            kc[m + half] = pf_to_bf16(r1);
+        }
+    } else if (OP == OP_O || OP == OP_DOWN) {
+        if (nrow && pos < p.P) p.x[(size_t)pos * p.H + n] += y;
+    } else if (OP == OP_GATEUP) {
+        // packed row 2i is gate row i, 2i + 1 up row i (adjacent lanes)
+        const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
+        if (!nrow || pos >= p.P || (n & 1)) return;
+        pf_store_split(p.inh[dst] + (size_t)pos * p.ks, p.inl[dst] + (size_t)pos * p.ks, n >> 1, y / (1.f + __expf(-y)) * up);
+    } else {  // vocabulary projection of the last position (row 0 of the block)
+        if (nrow && pos == 0) p.logits[n] = y;
+    }
+}
+
+template <int OP, int kPfRB>
 __global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                 uint64_t bias_off) {
+    constexpr int kPfBatch = kPfRB == 1 ? 8 : 4;
     const int l = threadIdx.x;
-    const int n = blockIdx.x * kPfRows + (l & 15);
+    const int n0 = blockIdx.x * 16 * kPfRB + (l & 15);  // this lane's row in row block 0 (+16 rb)
     const int pb = blockIdx.y * kPfPos;
     const int nb = min(kPfPos, np_rows - pb) >> 4;       // position blocks of 16: 1 or 2
     const int kq = l >> 4, ngrp = g.K >> 3, nsteps = (ngrp + 3) >> 2;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
     const size_t arow0 = (size_t)(pb + (l & 15)) * p.ks, arow1 = arow0 + (size_t)16 * p.ks;
-    pf_f32x4 acc[2];
-    acc[0] = acc[1] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
-    const bool nrow = n < g.rows;
+    pf_f32x4 acc[kPfRB][2];
+#pragma unroll
+    for (int rb = 0; rb < kPfRB; ++rb) acc[rb][0] = acc[rb][1] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsteps; s0 += kPfBatch) {
-        pf_u32x4 bw[kPfBatch], a0h[kPfBatch], a0l[kPfBatch], a1h[kPfBatch], a1l[kPfBatch];
+        pf_u32x4 bw[kPfRB][kPfBatch], a0h[kPfBatch], a0l[kPfBatch], a1h[kPfBatch], a1l[kPfBatch];
 #pragma unroll
         for (int i = 0; i < kPfBatch; ++i) {
             const int kg = 4 * (s0 + i) + kq;
-            bw[i] = (pf_u32x4){0u, 0u, 0u, 0u};
+            const bool step = s0 + i < nsteps;
+#pragma unroll
+            for (int rb = 0; rb < kPfRB; ++rb) {
+                const int n = n0 + 16 * rb;
+                bw[rb][i] = (pf_u32x4){0u, 0u, 0u, 0u};
+                if (step && n < g.rows && kg < ngrp) bw[rb][i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+            }
             a0h[i] = a0l[i] = a1h[i] = a1l[i] = (pf_u32x4){0u, 0u, 0u, 0u};
-            if (s0 + i < nsteps) {
-                if (nrow && kg < ngrp) bw[i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+            if (step) {
                 a0h[i] = *(const pf_u32x4 *)(ah + arow0 + 8 * kg);
                 a0l[i] = *(const pf_u32x4 *)(al + arow0 + 8 * kg);
                 if (nb > 1) {
@@ -135,63 +188,27 @@ __global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer
         }
 #pragma unroll
         for (int i = 0; i < kPfBatch; ++i) {
-            const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw[i]);
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a0h[i]), b, acc[0], 0, 0, 0);
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a0l[i]), b, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a1h[i]), b, acc[1], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a1l[i]), b, acc[1], 0, 0, 0);
-        }
-    }
-    // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n]
-    const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
+            const pf_bf16x8 x0h = __builtin_bit_cast(pf_bf16x8, a0h[i]), x0l = __builtin_bit_cast(pf_bf16x8, a0l[i]);
+            const pf_bf16x8 x1h = __builtin_bit_cast(pf_bf16x8, a1h[i]), x1l = __builtin_bit_cast(pf_bf16x8, a1l[i]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        if (j >= nb) break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int pos = pb + 16 * j + 4 * kq + r;
-            float y = acc[j][r];
-            if (OP == OP_QKV) {
-                // packed rows 2m, 2m+1 of a query or key head are its dims m, m + hd/2 (adjacent lanes)
-                const int which = n >= Q + KVr ? 2 : (n >= Q ? 1 : 0);
-                const int base = n - (which == 0 ? 0 : (which == 1 ? Q : Q + KVr));
-                const int i = base & (hd - 1);
-                const int srow = which == 2 ? base : (base & ~(hd - 1)) + ((i & 1) ? (i >> 1) + half : (i >> 1));
-                if (bias_off != ~(uint64_t)0 && nrow)
-                    y += pf_bf16f(((const uint16_t *)(p.blob + bias_off))[(which == 0 ? 0 : (which == 1 ? Q : Q + KVr)) + srow]);
-                const float partner = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
-                if (!nrow || pos >= p.P) continue;
-                const int slot = p.pos0 + pos;
-                if (which == 2) {
-                    const int jh = srow >> p.hd_shift, d = srow & (hd - 1);
-                    p.kv[((((size_t)layer * 2 + 1) * p.nkv + jh) * p.S + slot) * hd + d] = pf_to_bf16(y);
-                    continue;
-                }
-                if (i & 1) continue;  // the odd row is the partner of this pair
-                const int h = srow >> p.hd_shift, m = srow & (hd - 1);
-                const float2 cs = ((const float2 *)(p.blob + p.rope))[(size_t)slot * half + m];
-                const float r0 = y * cs.x - partner * cs.y, r1 = partner * cs.x + y * cs.y;
-                if (which == 0) {
-                    p.q[(size_t)pos * Q + h * hd + m] = r0;
-                    p.q[(size_t)pos * Q + h * hd + m + half] = r1;
-                } else {
-                    uint16_t *kc = p.kv + ((((size_t)layer * 2 + 0) * p.nkv + h) * p.S + slot) * hd;
-                    kc[m] = pf_to_bf16(r0);
-                    kc[m + half] = pf_to_bf16(r1);
-                }
-            } else if (OP == OP_O || OP == OP_DOWN) {
-                if (nrow && pos < p.P) p.x[(size_t)pos * p.H + n] += y;
-            } else if (OP == OP_GATEUP) {
-                // packed row 2i is gate row i, 2i + 1 up row i (adjacent lanes)
-                const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0xB1, 0xf, 0xf, false));
-                if (!nrow || pos >= p.P || (n & 1)) continue;
-                pf_store_split(p.inh[dst] + (size_t)pos * p.ks, p.inl[dst] + (size_t)pos * p.ks, n >> 1,
-                               y / (1.f + __expf(-y)) * up);
-            } else {  // vocabulary projection of the last position (row 0 of the block)
-                if (nrow && pos == 0) p.logits[n] = y;
+            for (int rb = 0; rb < kPfRB; ++rb) {
+                const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw[rb][i]);
+                acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0h, b, acc[rb][0], 0, 0, 0);
+                acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0l, b, acc[rb][0], 0, 0, 0);
+                acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1h, b, acc[rb][1], 0, 0, 0);
+                acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1l, b, acc[rb][1], 0, 0, 0);
             }
         }
     }
+    // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n0 + 16 rb]
+#pragma unroll
+    for (int rb = 0; rb < kPfRB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j >= nb) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pf_epilogue<OP>(p, g, layer, dst, bias_off, n0 + 16 * rb, pb + 16 * j + 4 * kq + r, acc[rb][j][r]);
+        }
 }
 
 // Columns [K, ks) of the rows written by the gate/up epilogue (the down projection's k tail reads them).
