@@ -1152,13 +1152,15 @@ PfLayout pf_layout(const mbk_config &c, int n) {
 template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
     // four row blocks per workgroup (every activation load feeds four products) while that leaves at least
-    // 512 workgroups, else one (more, shorter workgroups)
+    // 512 workgroups, else one row block, and with fewer than 512 of those its k steps split over four waves
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
     if (x4 * py >= 512)
-        hipLaunchKernelGGL((k_pf_gemm<OP, 4>), dim3(x4, py), dim3(64), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 1>), dim3(x4, py), dim3(64), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    else if (x1 * py >= 512)
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 1>), dim3(x1, py), dim3(64), 0, st, pp, g, layer, src, dst, np_rows, bias);
     else
-        hipLaunchKernelGGL((k_pf_gemm<OP, 1>), dim3(x1, py), dim3(64), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
 }
 
 }  // namespace

@@ -96,13 +96,15 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
     }
 }
 
-// C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  One wave per workgroup: packed rows
+// C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  A workgroup takes packed rows
 // [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [32 by, 32 by + 32) (two position blocks)
 // of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds RB matrix
-// products and every weight load two.  RB = 4 where that still leaves enough workgroups to fill the device,
-// else 1.  Lane l feeds row l % 16 of each operand with input group 4 s + l / 16 of k step s (32 inputs); the
-// k steps go in batches (8 with one row block, 4 with four) whose loads are all issued before the batch's
-// products.  After the k loop lane
+// products and every weight load two.  RB = 4 (one wave) where that still leaves enough workgroups to fill
+// the device; else RB = 1 with the k steps split over KS waves (contiguous ranges; the partial tiles are
+// added through LDS in wave order by wave 0, so the result does not depend on timing), which multiplies the
+// loads in flight and shortens each wave's chain where a matrix has few row blocks.  Lane l feeds row l % 16
+// of each operand with input group 4 s + l / 16 of k step s (32 inputs); the k steps go in batches (8 with
+// one row block, 4 with four) whose loads are all issued before the batch's products.  After the k loop lane
 // l holds C[32 by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
 constexpr int kPfPos = 32;
 template <int OP>
@@ -150,15 +152,17 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g,
     }
 }
 
-template <int OP, int kPfRB>
-__global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
-                                                uint64_t bias_off) {
+template <int OP, int kPfRB, int KS>
+__global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
+                                                     uint64_t bias_off) {
     constexpr int kPfBatch = kPfRB == 1 ? 8 : 4;
-    const int l = threadIdx.x;
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16 * kPfRB + (l & 15);  // this lane's row in row block 0 (+16 rb)
     const int pb = blockIdx.y * kPfPos;
     const int nb = min(kPfPos, np_rows - pb) >> 4;       // position blocks of 16: 1 or 2
-    const int kq = l >> 4, ngrp = g.K >> 3, nsteps = (ngrp + 3) >> 2;
+    const int kq = l >> 4, ngrp = g.K >> 3, nall = (ngrp + 3) >> 2;
+    // this wave's k steps [sb, sb + nsteps)
+    const int sb = nall * wv / KS, nsteps = nall * (wv + 1) / KS - sb;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
     const size_t arow0 = (size_t)(pb + (l & 15)) * p.ks, arow1 = arow0 + (size_t)16 * p.ks;
     pf_f32x4 acc[kPfRB][2];
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer
         pf_u32x4 bw[kPfRB][kPfBatch], a0h[kPfBatch], a0l[kPfBatch], a1h[kPfBatch], a1l[kPfBatch];
 #pragma unroll
         for (int i = 0; i < kPfBatch; ++i) {
-            const int kg = 4 * (s0 + i) + kq;
+            const int kg = 4 * (sb + s0 + i) + kq;
             const bool step = s0 + i < nsteps;
 #pragma unroll
             for (int rb = 0; rb < kPfRB; ++rb) {
@@ -199,6 +203,25 @@ __global__ __launch_bounds__(64) void k_pf_gemm(PfParams p, MatGeom g, int layer
                 acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1l, b, acc[rb][1], 0, 0, 0);
             }
         }
+    }
+    if (KS > 1) {
+        // partial tiles of the waves, added in wave order
+        __shared__ pf_f32x4 part[KS > 1 ? KS - 1 : 1][kPfRB][2][64];
+        if (wv > 0)
+#pragma unroll
+            for (int rb = 0; rb < kPfRB; ++rb) {
+                part[wv - 1][rb][0][l] = acc[rb][0];
+                part[wv - 1][rb][1][l] = acc[rb][1];
+            }
+        __syncthreads();
+        if (wv > 0) return;
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+            for (int rb = 0; rb < kPfRB; ++rb) {
+                acc[rb][0] += part[w][rb][0][l];
+                acc[rb][1] += part[w][rb][1][l];
+            }
     }
     // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n0 + 16 rb]
 #pragma unroll
