@@ -79,6 +79,8 @@ struct Params {
     int32_t H, nq, nkv, hd, I, V, S, NL;
     int32_t max_splits, gqa, attn_min_chunk, piece_pos, hd_shift;
     int32_t merge_in_o;       // 1: split partials are merged by the output projection's workgroups
+    int32_t merge_dist;       // else 1: every split merges a slice of its group's outputs; 0: the last split
+                              // to arrive merges them all (no workgroup waits for another inside a launch)
     int32_t attn_hpi;         // query heads per attention item: gqa (packed) or 1 (one item per query head)
     int32_t wfmt;             // WeightFmt of the projection matrices: GEMV inputs are hi/lo bf16 (bf16) or fp32 (fp8)
     // LDS offsets in bytes of the dynamic area
@@ -1229,26 +1231,20 @@ MBK_DEV void attn_inputs(const Params &p, const Task &T, int ivi, uint8_t *lds, 
 // context; the planner chooses, see the attention items rule in mbk.hip).
 // Lane (slot, dl) of a compute wave
 // takes one position per block and head dims dl*8 .. dl*8+7 (LP = hd/8
-// lanes per position); the compute waves take alternate blocks.  Positions
-// arrive in segments (the ring pieces, the last one extended by the position
-// appended this step).  Every lane keeps the running maximum, sum and
-// weighted values of its own positions (online softmax in one pass over the
-// keys and values: a score above the maximum rescales what the lane holds),
-// so neither the lanes nor the waves wait for one another inside an item; at
-// its end the slots of a wave, then the waves in LDS, are combined with the
+// lanes per position); the compute waves take alternate blocks.  Cached
+// positions arrive in the ring pieces; the position appended this step is
+// read from LDS.  Every lane keeps the running maximum, sum and weighted
+// values of its own positions (online softmax in one pass over the keys and
+// values: a new maximum rescales what the lane holds; a lane folds several
+// positions in at once, so their scores are formed side by side), so neither
+// the lanes nor the waves wait for one another inside an item; at its end
+// the slots of a wave, then the waves in LDS, are combined with the
 // log-sum-exp rule, like the partials of different splits.
 
-// Key (or value) of position t of a segment: ring positions t < nring
-// (bf16), then the appended position (fp32 in LDS at cur).
 // 8 floats from LDS.
 MBK_DEV void load8f(const float *src, float *f) {
     const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
-MBK_DEV void seg_row(int t, int nring, const uint8_t *rb, const float *cur, int hd, int dl, float *f) {
-    if (t < nring) unpack8(*(const u32x4 *)(rb + (size_t)t * hd * 2 + dl * 16), f);
-    else load8f(cur + dl * 8, f);
 }
 
 // Sum (max) over the slots of a wave: the lanes with the same lane % LP.
@@ -1273,6 +1269,54 @@ template <int LP> MBK_DEV float slot_max(float v) {
 // Tagged 16-byte store of entries i, i+1 (i even).
 MBK_DEV void put2(const Params &p, uint64_t base, int i, float a, float b, uint32_t tag) {
     stc16(p.ws, (uint32_t)(base + 8u * (uint32_t)i), (u32x4){__float_as_uint(a), tag, __float_as_uint(b), tag});
+}
+
+// Split-context merge done by all the splits of a merge group at once (gh query heads hb .. hb + gh - 1
+// of KV head j, their outputs taken in pairs of dims): split s merges pairs s, s + nsplit, ... from
+// the tagged partials {acc[hd] | max, sum} of every split, in split order with the largest maximum
+// first (the same arithmetic as a single merging workgroup, so the result does not depend on which
+// workgroup merges), and publishes them as the attention output.  A pair's inputs are polled by one
+// thread per split; scr holds [nsplit][pairs][4] floats.  All compute-wave threads; the workgroup has no
+// other item in the interval (the plan gives each workgroup at most one item when splits are used).
+template <int G>
+MBK_DEV void merge_slice(const Params &p, int j, int s, int gh, int hb, int nsplit, float *scr, uint32_t tag,
+                         Ctl &ctl, StepCtx &sc) {
+    const int hd = p.hd, npairs = gh * hd / 2;
+    const int np = s < npairs ? (npairs - s + nsplit - 1) / nsplit : 0;
+    cw_barrier(p, ctl, sc.gen);  // compute wave 0 is done with the wave partials in scr
+    for (int i = threadIdx.x; i < nsplit * np; i += kCW * 64) {
+        const int q = i / np, pi = i - q * np, v = s + pi * nsplit, h = (2 * v) / hd, e = 2 * v - h * hd;
+        const uint32_t e0 = (uint32_t)(((j * p.max_splits + q) * G + hb + h) * (hd + 2));
+        const uint32_t oa = (uint32_t)p.wl.part + 8u * (e0 + (uint32_t)hd), ob = (uint32_t)p.wl.part + 8u * (e0 + (uint32_t)e);
+        u32x4 a, b;
+        for (int it = 0;; ++it) {
+            a = ldc16(p.ws, oa);
+            b = ldc16(p.ws, ob);
+            const bool ready = a.y == tag && a.w == tag && b.y == tag && b.w == tag;
+            if (ready || it >= p.spin_limit || aborted(p, it)) {
+                if (!ready && it >= p.spin_limit) set_error(p);
+                break;
+            }
+            reread();
+        }
+        *(float4 *)(scr + 4 * i) = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(b.x),
+                                               __uint_as_float(b.z));
+    }
+    cw_barrier(p, ctl, sc.gen);
+    for (int pi = threadIdx.x; pi < np; pi += kCW * 64) {
+        const int v = s + pi * nsplit, h = (2 * v) / hd, e = 2 * v - h * hd;
+        float mm = -INFINITY;
+        for (int q = 0; q < nsplit; ++q) mm = fmaxf(mm, scr[4 * (q * np + pi)]);
+        float ll = 0.f, a0 = 0.f, a1 = 0.f;
+        for (int q = 0; q < nsplit; ++q) {
+            const float *r = scr + 4 * (q * np + pi);
+            const float c = r[0] == -INFINITY ? 0.f : __expf(r[0] - mm);  // a split without positions
+            ll = fmaf(r[1], c, ll);
+            a0 = fmaf(r[2], c, a0);
+            a1 = fmaf(r[3], c, a1);
+        }
+        put2(p, p.wl.o, (j * G + hb + h) * hd + e, a0 / ll, a1 / ll, tag);
+    }
 }
 
 // One attention item, for head size LP * 8 (LP lanes per position).
@@ -1314,67 +1358,93 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
     }
     const uint8_t *ring = lds + p.lds_ring;
     const int na = n_allocs(p, iv, T, sc.ss);
-    const bool has_cur = pos >= sp.t0 && pos < sp.t1;
-    const int nseg = na > 0 ? na : (has_cur ? 1 : 0);
-    for (int k = 0; k < nseg; ++k) {
-        const uint8_t *kb = nullptr, *vb = nullptr;
-        int nring = 0;
-        if (k < na) {
-            const Alloc A = task_alloc(p, iv, T, sc.ss, k);
-            const uint32_t start = ring_acquire(p, ctl, rp, A);
-            kb = ring + start;
-            vb = kb + A.r1;
-            nring = (int)(A.b0 / (uint32_t)(hd * 2));
-        }
-        const int npos = nring + (has_cur && k == nseg - 1 ? 1 : 0);
-        // one pass over the segment: every lane keeps the running maximum, sum and weighted values of
-        // its own positions (a raised maximum rescales what the lane holds)
-        for (int b = cw; b * PPW < npos; b += kCW) {
-            const int t = b * PPW + slot;
-            const bool valid = t < npos, cached = t < nring;
-            // a cached key and value (bf16 in the ring), this step's (fp32 in LDS), or nothing past the segment
-            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            float kf[8], vf[8];
-            if (cached) {
-                kw = *(const u32x4 *)(kb + (size_t)t * hd * 2 + dl * 16);
-                vw = *(const u32x4 *)(vb + (size_t)t * hd * 2 + dl * 16);
-            } else if (valid) {
-                seg_row(t, nring, kb, cur, hd, dl, kf);
-                seg_row(t, nring, vb, cur + hd, hd, dl, vf);
+    // cached positions, one ring piece at a time: each round a lane takes NB positions (blocks b,
+    // b + kCW, ... of its wave), whose scores are independent of each other, and folds them into its
+    // running state with one rescale
+    constexpr int NB = G <= 4 ? 4 : (G <= 6 ? 2 : 1);
+    for (int k = 0; k < na; ++k) {
+        const Alloc A = task_alloc(p, iv, T, sc.ss, k);
+        const uint8_t *kb = ring + ring_acquire(p, ctl, rp, A);
+        const uint8_t *vb = kb + A.r1;
+        const int nring = (int)(A.b0 / (uint32_t)(hd * 2));
+        for (int b = cw; b * PPW < nring; b += kCW * NB) {
+            u32x4 kw[NB], vw[NB];
+            bool ok[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int t = (b + u * kCW) * PPW + slot;
+                ok[u] = t < nring;
+                const size_t at = (size_t)(ok[u] ? t : nring - 1) * hd * 2 + dl * 16;  // in the piece
+                kw[u] = *(const u32x4 *)(kb + at);
+                vw[u] = *(const u32x4 *)(vb + at);
             }
-            if (cached) unpack8(vw, vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 if (h >= nh) break;
-                float d = 0.f;
-                if (cached) {
-                    d = dot2(kw.x, qh[h].x, d); d = dot2(kw.y, qh[h].y, d);
-                    d = dot2(kw.z, qh[h].z, d); d = dot2(kw.w, qh[h].w, d);
-                    d = dot2(kw.x, ql[h].x, d); d = dot2(kw.y, ql[h].y, d);
-                    d = dot2(kw.z, ql[h].z, d); d = dot2(kw.w, ql[h].w, d);
-                } else if (valid) {
-                    float qf[8];
-                    load8f(qkv + h * hd + dl * 8, qf);
+                float d[NB];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+                for (int u = 0; u < NB; ++u) {
+                    float x = 0.f;
+                    x = dot2(kw[u].x, qh[h].x, x); x = dot2(kw[u].y, qh[h].y, x);
+                    x = dot2(kw[u].z, qh[h].z, x); x = dot2(kw[u].w, qh[h].w, x);
+                    x = dot2(kw[u].x, ql[h].x, x); x = dot2(kw[u].y, ql[h].y, x);
+                    x = dot2(kw[u].z, ql[h].z, x); x = dot2(kw[u].w, ql[h].w, x);
+                    d[u] = x;
                 }
-                d = group_sum<LP>(d);
-                if (valid) {
-                    if (d > M[h]) {
-                        const float c = __expf(M[h] - d);  // 0 while M is -inf
-                        l[h] *= c;
+                float mn = M[h];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[h][e] *= c;
-                        M[h] = d;
-                    }
-                    const float w = __expf(d - M[h]);
-                    l[h] += w;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+                for (int u = 0; u < NB; ++u) {
+                    d[u] = ok[u] ? group_sum<LP>(d[u]) : -INFINITY;
+                    mn = fmaxf(mn, d[u]);
                 }
+                // new maximum mn: what the lane holds is scaled by exp(M - mn), each position weighs
+                // exp(d - mn); a lane that has seen no position yet keeps zeros (base 0 avoids -inf - -inf)
+                const float base = mn == -INFINITY ? 0.f : mn;
+                const float c = __expf(M[h] - base);
+                float w[NB];
+#pragma unroll
+                for (int u = 0; u < NB; ++u) w[u] = __expf(d[u] - base);
+                float ws = w[0];
+#pragma unroll
+                for (int u = 1; u < NB; ++u) ws += w[u];
+                l[h] = fmaf(l[h], c, ws);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= c;
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    float vf[8];
+                    unpack8(vw[u], vf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w[u], vf[e], acc[h][e]);
+                }
+                M[h] = mn;
             }
         }
-        if (k < na) ring_release(ctl, rp);
+        ring_release(ctl, rp);
+    }
+    // the position appended this step (fp32 key and value in LDS, against the fp32 queries): slot 0 of
+    // the last compute wave
+    if (pos >= sp.t0 && pos < sp.t1 && cw == kCW - 1) {
+        float kf[8], vf[8];
+        load8f(cur + dl * 8, kf);
+        load8f(cur + hd + dl * 8, vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (h >= nh) break;
+            float qf[8];
+            load8f(qkv + h * hd + dl * 8, qf);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+            d = group_sum<LP>(d);
+            if (slot == 0) {
+                const float mn = fmaxf(M[h], d), c = __expf(M[h] - mn), w = __expf(d - mn);
+                l[h] = fmaf(l[h], c, w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e] * c);
+                M[h] = mn;
+            }
+        }
     }
     // wave partials {max, sum, -, -, acc[hd]} to LDS (the slots of the wave combined by the log-sum-exp
     // rule); compute wave 0 combines them
@@ -1413,7 +1483,7 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
                 ll = fmaf(r[1], c, ll);
                 a = fmaf(r[4 + d], c, a);
             }
-            if (p.merge_in_o) {
+            if (p.merge_in_o || (p.merge_dist && nsplit > 1)) {
                 // tagged partial: entries [acc[hd] | max, sum] of (j, s, h)
                 const int e0 = ((j * p.max_splits + s) * G + h0 + h) * (hd + 2);
                 put(p, p.wl.part, e0 + d, a, tag);
@@ -1432,7 +1502,11 @@ MBK_DEV void attention_task(const Params &p, const Interval &iv, int ivi, const 
             }
         }
     }
-    if (nsplit > 1 && !p.merge_in_o) {
+    if (nsplit > 1 && !p.merge_in_o && p.merge_dist) {
+        // every split merges a slice of its group's outputs from the tagged partials of all splits
+        // (a merge group is the query head of a single-head item, else the G heads of the KV head)
+        merge_slice<G>(p, j, s, nh == 1 ? 1 : G, nh == 1 ? h0 : 0, nsplit, scr, tag, ctl, sc);
+    } else if (nsplit > 1 && !p.merge_in_o) {
         // the last split to arrive (one atomic per split) merges the partials in split order, so the
         // result does not depend on arrival order.  A merge group is the query head of a single-head
         // item (gh = 1 head, counter j * G + h0), else the KV head (gh = G heads, counter j)

@@ -672,6 +672,7 @@ Params make_params(const mbk_model *m, int32_t token, int32_t pos, float *logits
         const int splits = std::min(P.max_splits, (c.kv_capacity + m->attn_min_chunk - 1) / m->attn_min_chunk);
         p.merge_in_o = splits > 1 && (size_t)c.n_heads * splits * (c.head_dim + 2) * 8u <= 48u * 1024u ? 1 : 0;
     }
+    p.merge_dist = 1;
     p.piece_pos = P.piece_pos;
     p.hd_shift = 0;
     while ((1 << p.hd_shift) < c.head_dim) ++p.hd_shift;
@@ -956,6 +957,7 @@ int mbk_decode_step_ablation(mbk_model *m, int32_t token, int32_t pos, float *lo
     next_seq(m);
     Params p = make_params(m, token, pos, logits, argmax);
     p.barrier = 0;
+    p.merge_dist = 0;  // a launch of one interval: its workgroups never wait for each other
     const unsigned lds = (unsigned)m->plan.lds_bytes;
     if (!use_graph) {
         for (int i = 0; i < p.n_intervals; ++i) {
