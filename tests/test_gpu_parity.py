@@ -135,8 +135,9 @@ def test_smollm135m_kv128_full_schedule(pair_factory):
 
 def test_smollm135m_kv4096_prefilled_long_context(pair_factory):
     """The 4096-slot cache pre-filled at 0..4031: all 64 steps 4032..4095 (the last slot), every step
-    checked; split-context attention with the cross-workgroup merge gives the same bits in every
-    executor."""
+    checked; split-context attention gives the same bits in every executor, although the persistent
+    kernel merges the splits in all of them at once (each a slice of the head) and a one-interval launch
+    merges them in the last split to arrive."""
     wl = synth.get("smollm135m-kv4096")
     p = pair_factory(wl, kv_prefix=synth.kv_prefill(wl))
     positions = synth.decode_schedule(wl)
@@ -175,8 +176,9 @@ def test_smollm135m_kv128_split_attention_merged_by_output_projection(pair_facto
 
 def test_smollm135m_kv4096_packed_gqa_items(pair_factory):
     """The query heads of a KV head packed into one attention item (each cached key and value read
-    once), with the split merge by the last split to arrive: all 64 steps to the last slot (every 4th
-    checked, and the last), and equal bits across executors."""
+    once), the split merge spread over the splits (persistent kernel) or done by the last split to arrive
+    (ablation): all 64 steps to the last slot (every 4th checked, and the last), and equal bits across
+    executors."""
     wl = synth.get("smollm135m-kv4096")
     G = wl.n_heads // wl.n_kv_heads
     p = pair_factory(wl, kv_prefix=synth.kv_prefill(wl), setup=lambda d: d.set_attention_items(G))
