@@ -1232,8 +1232,8 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
         pf_gemm<OP_QKV>(pp, Y.qkv, l, 0, 0, L.Pp, Y.bias, st);
         if (c.head_dim == 64 || c.head_dim == 128) {
             const dim3 grid((unsigned)((n_tokens + 15) / 16), (unsigned)c.n_heads);
-            if (c.head_dim == 64) hipLaunchKernelGGL(k_pf_attn_mma<64>, grid, dim3(64), 0, st, pp, l, 1);
-            else hipLaunchKernelGGL(k_pf_attn_mma<128>, grid, dim3(64), 0, st, pp, l, 1);
+            if (c.head_dim == 64) hipLaunchKernelGGL((k_pf_attn_mma<64, 4>), grid, dim3(256), 0, st, pp, l, 1);
+            else hipLaunchKernelGGL((k_pf_attn_mma<128, 4>), grid, dim3(256), 0, st, pp, l, 1);
         } else {
             hipLaunchKernelGGL(k_pf_attn, dim3((unsigned)((n_tokens + kPfAttnQ - 1) / kPfAttnQ), (unsigned)c.n_heads),
                                dim3(256), 0, st, pp, l, 1);

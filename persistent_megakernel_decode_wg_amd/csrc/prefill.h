@@ -370,12 +370,19 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfParams p, int layer, int dst)
 // operand B is exactly those 8 probabilities per lane (hi/lo pairs; the order of the 32 keys in the
 // contraction is the lanes' own: tile 0 keys 4 g .. 4 g + 3, then tile 1's), operand A the values of the
 // same keys at 16 head dims, read from the block's values staged transposed in LDS.  Lane (g, c), register
-// r of output tile dt holds query c, dim 16 dt + 4 g + r.  Output hi/lo into input buffer dst.
-template <int HD>
-__global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int dst) {
+// r of output tile dt holds query c, dim 16 dt + 4 g + r.  The W waves of a workgroup take the key blocks in
+// turn (wave w blocks w, w + W, ...), each with its own running state and its own staging area, so the
+// longest chain of blocks (the last queries of a long prompt) is W times shorter; at the end the waves'
+// states meet in LDS and wave 0 combines them in wave order with the log-sum-exp rule (a wave whose blocks
+// all lie past a query's position adds exactly nothing).  Output hi/lo into input buffer dst.
+template <int HD, int W>
+__global__ __launch_bounds__(64 * W) void k_pf_attn_mma(PfParams p, int layer, int dst) {
     constexpr int KS = HD / 32, DT = HD / 16, VR = 32 + 4;   // score k steps, output tiles, V^T row (bf16)
-    __shared__ uint16_t vt[HD * VR];
-    const int l = threadIdx.x, g = l >> 4, c = l & 15;
+    constexpr int NS = 2 + 4 * DT;                           // floats of one lane's state: max, sum, outputs
+    static_assert((W - 1) * 64 * NS * 4 <= W * HD * VR * 2, "the waves' states fit the staging areas");
+    __shared__ __attribute__((aligned(16))) uint16_t vts[W * HD * VR];
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6, g = l >> 4, c = l & 15;
+    uint16_t *vt = vts + wv * HD * VR;
     const int h = blockIdx.y, j = h / p.gqa, q0 = blockIdx.x * 16;
     const int nqb = min(16, p.P - q0);
     const int qc = min(c, nqb - 1);                 // padding columns repeat the last query (never stored)
@@ -421,8 +428,8 @@ __global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int d
             if (t0 + key < Lmax) vw[u] = *(const pf_u32x4 *)(V + (size_t)(t0 + key) * HD + 8 * dc);
         }
     };
-    load_block(0);
-    for (int t0 = 0; t0 < Lmax; t0 += 32) {
+    if (32 * wv < Lmax) load_block(32 * wv);
+    for (int t0 = 32 * wv; t0 < Lmax; t0 += 32 * W) {
         // this block's values, transposed: vt[d][key] (keys past the last query's position are zero)
 #pragma unroll
         for (int u = 0; u < VC; ++u) {
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int d
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[tau][r] = t0 + 16 * tau + 4 * g + r <= qpos ? acc[r] : -INFINITY;
         }
-        if (t0 + 32 < Lmax) load_block(t0 + 32);   // the next block's loads overlap this block's math
+        if (t0 + 32 * W < Lmax) load_block(t0 + 32 * W);   // the next block's loads overlap this block's math
         float mb = sc[0][0];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int d
             pl[e] = pf_to_bf16(pw[e] - pf_bf16f(ph[e]));
         }
         const pf_bf16x8 bh = __builtin_bit_cast(pf_bf16x8, ph), bl = __builtin_bit_cast(pf_bf16x8, pl);
-        __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's staged values are in LDS
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const uint16_t *row = vt + (16 * dt + c) * VR;
@@ -490,7 +497,42 @@ __global__ __launch_bounds__(64) void k_pf_attn_mma(PfParams p, int layer, int d
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, o[dt], 0, 0, 0);
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, o[dt], 0, 0, 0);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next block is staged
+    }
+    if (W > 1) {
+        // the waves' states, then wave 0 combines them in wave order
+        float *st = (float *)vts;
+        __syncthreads();   // every wave is past its last block (the states reuse the staging areas)
+        if (wv > 0) {
+            float *d = st + ((wv - 1) * 64 + l) * NS;
+            d[0] = M;
+            d[1] = Ls;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[2 + 4 * dt + r] = o[dt][r];
+        }
         __syncthreads();
+        if (wv > 0) return;
+        float mm = M;
+#pragma unroll
+        for (int w = 1; w < W; ++w) mm = fmaxf(mm, st[((w - 1) * 64 + l) * NS]);
+        const float f0 = M == -INFINITY ? 0.f : __expf(M - mm);
+        Ls *= f0;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] *= f0;
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+            const float *d = st + ((w - 1) * 64 + l) * NS;
+            const float f = d[0] == -INFINITY ? 0.f : __expf(d[0] - mm);
+            Ls = fmaf(d[1], f, Ls);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[dt][r] = fmaf(d[2 + 4 * dt + r], f, o[dt][r]);
+        }
     }
     if (c >= nqb) return;
     const float inv = 1.f / Ls;
