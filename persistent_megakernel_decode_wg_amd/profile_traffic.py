@@ -4,7 +4,7 @@ Two `rocprofv3 --pmc` passes over `bench.py --calib-copy-mib N` (FETCH_SIZE, the
 see the decode kernel and a plain device-to-device copy of N MiB. The copy's counters give the scale of each counter
 (bytes the copy must read or write / what the counter reports); the decode kernel's per-dispatch averages are
 multiplied by those scales.  The result is written as one machine-readable line into a summary under profiles/,
-tagged with a hash of the kernel sources, so that bench.py reports it only while the kernel is unchanged.
+tagged with a hash of the decode kernel's sources, so that bench.py reports it only while that kernel is unchanged.
 
   python -m persistent_megakernel_decode_wg_amd.profile_traffic --fetch FETCH_counter_collection.csv \\
       --write WRITE_counter_collection.csv --copy-mib 256 --workload smollm135m-kv128 --out profiles/....md
@@ -23,11 +23,16 @@ KERNEL = "k_persistent"
 MARK = "traffic-json: "
 
 
+# The sources the decode kernel is built from (its bodies, the layouts, the kernel entry and the host code that
+# plans and launches it); the prefill kernels (prefill.h) are separate launches and do not enter it.
+DECODE_SOURCES = ("bodies.h", "layout.h", "mbk.hip")
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources (the counters describe exactly this code)."""
+    """Hash of the decode kernel's sources (the counters describe exactly this code)."""
     h = hashlib.sha256()
     d = os.path.join(_HERE, "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
