@@ -590,38 +590,39 @@ MBK_DEV Task task_opaque(const uint8_t *lds, const Params &p, int k) {
     return t;
 }
 
+// After each chunk a loader wave issues: every kBatch chunks it waits until at most kInflight of its chunks
+// are in flight and publishes the count of its completed chunks.
+MBK_DEV void batch_step(Ctl &ctl, int lw, uint32_t issued, uint32_t &published, int &inbatch) {
+    static_assert(kInflight == 8, "the wait below names kInflight");
+    if (++inbatch < kBatch) return;
+    inbatch = 0;
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // kInflight
+    if (issued > (uint32_t)kInflight && issued - (uint32_t)kInflight > published) {
+        published = issued - (uint32_t)kInflight;
+        lds_st_opaque(&ctl.prog[lw], published);
+    }
+}
+
 // Loader wave lw's share of one segment: chunks lw, lw + kLW, ... of `bytes`
 // (a multiple of 16) from global src to LDS dst, 16 bytes per lane per
-// chunk; the last chunk may be partial.  Every kBatch chunks the wave waits
-// until at most kInflight of its chunks are in flight and publishes the
-// count of its completed chunks.
+// chunk; the last chunk may be partial (it counts like any other chunk).
 template <int SC1>
 MBK_DEV void dma_segment(const uint8_t *src, uint8_t *dst, uint32_t bytes, int lw, Ctl &ctl, uint32_t &issued,
                          uint32_t &published, int &inbatch) {
     const int lane = threadIdx.x & 63;
     const int full = (int)(bytes / kChunk);
     const uint8_t *g = src + lane * 16;
-    static_assert(kInflight == 8, "the wait below names kInflight");
     for (int c = lw; c < full; c += kLW) {
         __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)c * kChunk), (lds_void_t *)(dst + c * kChunk), 16, 0,
                                          SC1 ? (int)kCacheSc1 : 0);
-        ++issued;
-        if (++inbatch == kBatch) {
-            inbatch = 0;
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // kInflight
-            if (issued - (uint32_t)kInflight > published && issued > (uint32_t)kInflight) {
-                published = issued - (uint32_t)kInflight;
-                lds_st_opaque(&ctl.prog[lw], published);
-            }
-        }
+        batch_step(ctl, lw, ++issued, published, inbatch);
     }
     const uint32_t rest = bytes - (uint32_t)full * kChunk;
     if (rest && full % kLW == lw) {
         if ((uint32_t)lane * 16u < rest)
             __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)full * kChunk), (lds_void_t *)(dst + full * kChunk), 16,
                                              0, SC1 ? (int)kCacheSc1 : 0);
-        ++issued;
-        ++inbatch;
+        batch_step(ctl, lw, ++issued, published, inbatch);
     }
 }
 
