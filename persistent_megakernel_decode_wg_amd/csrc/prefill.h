@@ -99,10 +99,10 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
 // C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  A workgroup takes packed rows
 // [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [32 by, 32 by + 32) (two position blocks)
 // of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds RB matrix
-// products and every weight load two.  RB = 4 (one wave) where that still leaves enough workgroups to fill
-// the device; else RB = 1 with the k steps split over KS waves (contiguous ranges; the partial tiles are
-// added through LDS in wave order by wave 0, so the result does not depend on timing), which multiplies the
-// loads in flight and shortens each wave's chain where a matrix has few row blocks.  Lane l feeds row l % 16
+// products and every weight load two.  RB = 4 where that still leaves enough workgroups to fill the device,
+// else RB = 1.  The k steps are split over KS waves (contiguous ranges; the partial tiles are added through
+// LDS in wave order by wave 0, so the result depends neither on timing nor on RB), which multiplies the loads
+// in flight and shortens each wave's chain.  Lane l feeds row l % 16
 // of each operand with input group 4 s + l / 16 of k step s (32 inputs); the k steps go in batches (8 with
 // one row block, 4 with four) whose loads are all issued before the batch's products.  After the k loop lane
 // l holds C[32 by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.

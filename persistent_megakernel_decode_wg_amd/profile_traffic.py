@@ -24,7 +24,7 @@ MARK = "traffic-json: "
 
 
 # The sources the decode kernel is built from (its bodies, the layouts, the kernel entry and the host code that
-# plans and launches it); the prefill kernels (prefill.h) are separate launches and do not enter it.
+# plans and launches it); the prefill kernels and their host code (prefill.h, prefill_host.h) do not enter it.
 DECODE_SOURCES = ("bodies.h", "layout.h", "mbk.hip")
 
 

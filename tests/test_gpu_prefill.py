@@ -154,3 +154,26 @@ def test_prefill_argument_errors(make):
         with pytest.raises(MbkError) as e:
             p.dec.prefill(toks, pos0, p.logits, p.am)
         assert e.value.code == code
+
+
+# (query heads, KV heads, head size): the matrix-core attention at head size 128 (per-head KV and G = 8), and the
+# VALU attention at head size 32 (G = 5); 2-layer decoders on a 256-slot cache
+PREFILL_SHAPES = [(6, 6, 128), (16, 2, 128), (10, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=["nq%d-nkv%d-hd%d" % s for s in PREFILL_SHAPES])
+def test_prefill_head_sizes_and_group_sizes(make, shape):
+    """A 77-token prompt (a ragged last block of queries and keys) against the stepped oracle, then the same
+    prompt as 0..40 and 41..76 giving the one-shot bits."""
+    import torch
+    nq, nkv, hd = shape
+    wl = synth.Workload("pf-%d-%d-hd%d" % shape, 2, 256, nq, nkv, hd, 512, 1024, 256, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=0, n_decode=0)
+    W = synth.make_weights(wl)
+    a, b = make(wl, W), make(wl, W)
+    toks = [int(t) for t in synth.tokens(13, "prefill-shapes", 77, wl.vocab)]
+    la, ia, _, _ = a.check(toks, 0, "prefill nq %d nkv %d hd %d" % shape)
+    b.prefill(toks[:41], 0)
+    lb, ib = b.prefill(toks[41:], 41)
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+    assert torch.equal(a.dec.kv, b.dec.kv)
