@@ -31,10 +31,10 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     // every matrix's k steps are split over four waves whatever the prompt length: the split fixes the order
     // in which a row's products are added, so a prompt's results do not depend on how it is cut into calls.
     // Four row blocks per workgroup (every activation load feeds four products) while that leaves at least
-    // 512 workgroups, else one (the row blocks per workgroup do not change the order)
+    // 256 workgroups, else one (the row blocks per workgroup do not change the order)
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
-    if (x4 * py >= 512)
+    if (x4 * py >= 256)
         hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     else
         hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
