@@ -7,7 +7,9 @@ round depending on G; the model shapes of the other tests cover G = 1, 2, 3 and 
 the cache slot written), once with one attention item per query head and once with the query heads of a KV
 head packed into one item, with the split partials merged by the output projection (few partials) or by the
 splits themselves (many: a 32-position split), and checks that the one-launch-per-interval executor gives
-the persistent kernel's bits.  Shapes and values are synthetic (seeded random-init weights)."""
+the persistent kernel's bits.  The largest shape the kernel takes (every GEMV input 8,192 wide, G = 8 at head
+size 128, a one-layer decoder whose 8,192-slot cache is pre-filled to position 8,188) is stepped to the last
+slot the same way.  Shapes and values are synthetic (seeded random-init weights)."""
 import pytest
 
 import synth
@@ -48,6 +50,32 @@ def test_gqa_group_sizes_and_head_sizes(shape, packed, split):
         positions = synth.decode_schedule(wl)
         label = "G=%d hd=%d %s split %s" % (G, hd, "packed" if packed else "per-head", split or "default")
         log("%s: positions %d..%d, max_splits %d" % (label, positions[0], positions[-1], d["max_splits"]))
+        worst = teacher_forced(p, positions, [synth.first_token(wl)], label=label)
+        log("%s: worst max|dlogit|/std = %.3g" % (label, worst))
+        tok, pos = synth.first_token(wl), positions[-1]
+        a, ia = p.gpu_step(tok, pos, "mega")
+        b, ib = p.gpu_step(tok, pos, "ablation")
+        assert (a.view("u4") == b.view("u4")).all() and ia == ib, label
+    finally:
+        p.close()
+
+
+# the largest shape the kernel takes: every GEMV input 8,192 wide (hidden, query heads x head size,
+# intermediate), G = 8 at head size 128, and the 8,192-slot cache filled to its last slot
+MAX_WL = synth.Workload("max-h8192-kv8192", 1, 8192, 64, 8, 128, 8192, 4096, 8192, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=8189, n_decode=3)
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["perhead", "packed"])
+def test_maximum_sizes_to_the_last_slot(packed):
+    wl = MAX_WL
+    G = wl.n_heads // wl.n_kv_heads
+    p = Pair(wl, kv_prefix=synth.kv_prefill(wl), setup=(lambda d: d.set_attention_items(G)) if packed else None)
+    try:
+        positions = synth.decode_schedule(wl)
+        assert positions[-1] == wl.kv_capacity - 1
+        label = "max sizes %s" % ("packed" if packed else "per-head")
+        log("%s: positions %d..%d, %s" % (label, positions[0], positions[-1], p.dec.describe()))
         worst = teacher_forced(p, positions, [synth.first_token(wl)], label=label)
         log("%s: worst max|dlogit|/std = %.3g" % (label, worst))
         tok, pos = synth.first_token(wl), positions[-1]
