@@ -138,6 +138,18 @@ def test_fp8_smollm1p7b_kv4096_prefilled(fp8_pair):
     log("fp8 smollm1.7b-kv4096 worst max|dlogit|/std = %.3g" % worst)
 
 
+def test_fp8_maximum_sizes_to_the_last_slot(fp8_pair):
+    """The largest shape the kernel takes (every GEMV input 8,192 wide: fp8 tiles of 8,192 codes per row;
+    G = 8 at head size 128), one layer, the 8,192-slot cache pre-filled to 8,188 and stepped to slot 8,191."""
+    wl = synth.Workload("max-h8192-kv8192", 1, 8192, 64, 8, 128, 8192, 4096, 8192, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=8189, n_decode=3)
+    p = fp8_pair(wl, kv_prefix=synth.kv_prefill(wl))
+    positions = synth.decode_schedule(wl)
+    assert positions[-1] == wl.kv_capacity - 1
+    worst = teacher_forced(p, positions, [synth.first_token(wl)], label="fp8 max sizes")
+    log("fp8 max sizes worst max|dlogit|/std = %.3g" % worst)
+
+
 def test_fp8_handle_rejects_prefill_and_late_format_change():
     from persistent_megakernel_decode_wg_amd import (MBK_ERR_STATE, MBK_ERR_UNSUPPORTED, MBK_WEIGHTS_BF16, Decoder,
                                                      MbkError)
