@@ -177,3 +177,20 @@ def test_prefill_head_sizes_and_group_sizes(make, shape):
     lb, ib = b.prefill(toks[41:], 41)
     assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
     assert torch.equal(a.dec.kv, b.dec.kv)
+
+
+def test_prefill_maximum_sizes_to_the_last_slot(make):
+    """The largest shape taken (hidden, query heads x head size and intermediate all 8,192, G = 8 at head size
+    128), one layer: the cache pre-filled at 0..8,091 and a 100-token prompt prefilled at 8,092..8,191, the
+    last slot, against the oracle stepped over the same positions."""
+    import torch
+    wl = synth.Workload("max-h8192-kv8192", 1, 8192, 64, 8, 128, 8192, 4096, 8192, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=8092, n_decode=0)
+    p = make(wl)
+    kv = synth.kv_prefill(wl)
+    P = kv.shape[3]
+    p.dec.kv[:, :, :, :P, :] = torch.from_numpy(np.ascontiguousarray(kv).view(np.int16)).cuda()
+    p.ref.prefill_kv(kv)
+    toks = [int(t) for t in synth.tokens(17, "prefill-max", 100, wl.vocab)]
+    assert P + len(toks) == wl.kv_capacity
+    p.check(toks, P, "prefill max sizes")
