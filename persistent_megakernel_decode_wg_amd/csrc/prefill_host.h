@@ -26,6 +26,8 @@ PfLayout pf_layout(const mbk_config &c, int n) {
     return L;
 }
 
+constexpr unsigned kPfLMinGroups = 128;  // workgroups the shared-tile GEMM needs to fill the device
+
 template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
     // every matrix's k steps are split over four waves whatever the prompt length: the split fixes the order
@@ -34,7 +36,15 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     // 256 workgroups, else one (the row blocks per workgroup do not change the order)
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
-    if (x4 * py >= 256)
+    const unsigned xl = (unsigned)((g.rows + 127) / 128), pl = (unsigned)(np_rows / 64);
+    if (np_rows % 64 == 0 && xl * pl >= kPfLMinGroups) {
+        static bool lds_set = false;  // per instance: its LDS above the default limit, once
+        if (!lds_set) {
+            (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP>, hipFuncAttributeMaxDynamicSharedMemorySize, kPfLLds);
+            lds_set = true;
+        }
+        hipLaunchKernelGGL((k_pf_gemm_lds<OP>), dim3(xl, pl), dim3(256), (unsigned)kPfLLds, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (x4 * py >= 256)
         hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     else
         hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);

@@ -194,3 +194,20 @@ def test_prefill_maximum_sizes_to_the_last_slot(make):
     toks = [int(t) for t in synth.tokens(17, "prefill-max", 100, wl.vocab)]
     assert P + len(toks) == wl.kv_capacity
     p.check(toks, P, "prefill max sizes")
+
+
+def test_prefill_long_prompt_equals_short_chunks_bitwise(make):
+    """A 512-token prompt on the SmolLM-135M shape in one call (its gate/up projection then runs with operand
+    tiles shared through LDS by four waves) and in eight calls of 64 tokens (every projection with per-wave
+    operands): the same logits, argmax and cache, bit for bit -- both forms add each row's products in the
+    same order."""
+    import torch
+    wl = synth.get("smollm135m-kv4096")
+    W = synth.make_weights(wl)
+    a, b = make(wl, W), make(wl, W)
+    toks = [int(t) for t in synth.tokens(19, "prefill-long", 512, wl.vocab)]
+    la, ia = a.prefill(toks, 0)
+    for c in range(0, 512, 64):
+        lb, ib = b.prefill(toks[c:c + 64], c)
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+    assert torch.equal(a.dec.kv, b.dec.kv)
