@@ -456,10 +456,10 @@ def main():
         for name in synth.WORKLOAD_ORDER:
             extra["configs"][name] = config_summary(synth.get(name))
             print("config %s: %s" % (name, json.dumps(extra["configs"][name])), file=sys.stderr, flush=True)
-        # multi-token prefill: the 64-token prompt of the SmolLM-135M shape and a 512-token prompt on its
-        # 4096-slot cache, against as many decode steps
+        # multi-token prefill: the 64-token prompt of the SmolLM-135M shape, a 512-token prompt on its
+        # 4096-slot cache and a 1024-token prompt of the SmolLM-1.7B shape, against as many decode steps
         extra["prefill"] = {}
-        for name, n in (("smollm135m-kv128", 64), ("smollm135m-kv4096", 512)):
+        for name, n in (("smollm135m-kv128", 64), ("smollm135m-kv4096", 512), ("smollm1.7b-kv4096", 1024)):
             dus = extra["configs"][name]["us_per_token_p50"]
             extra["prefill"]["%s/%d" % (name, n)] = prefill_summary(synth.get(name), n, dus)
             print("prefill %s/%d: %s" % (name, n, json.dumps(extra["prefill"]["%s/%d" % (name, n)])),
