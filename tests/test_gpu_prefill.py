@@ -94,6 +94,17 @@ def test_prefill_after_decode_steps_and_in_chunks(make):
     p.check(toks[21:31], 21, "tiny prefill 21..30")
 
 
+def test_prefill_single_tokens_at_the_cache_edges(make):
+    """The degenerate prompt of one token (63 padding rows in the GEMMs): at position 0, then 1..30 in one call,
+    then one token into the last slot, 31 -- each against the oracle."""
+    wl = synth.get("tiny-2L-h64-kv32")
+    p = make(wl)
+    toks = [int(t) for t in synth.tokens(14, "prefill-single", wl.kv_capacity, wl.vocab)]
+    p.check(toks[:1], 0, "tiny prefill of one token at 0")
+    p.check(toks[1:31], 1, "tiny prefill 1..30")
+    p.check(toks[31:32], 31, "tiny prefill of one token at the last slot")
+
+
 def test_prefill_chunked_equals_one_shot_bitwise(make):
     """Every position's projections are independent rows of the GEMMs and its attention reads the same
     cache slots, so prefilling 0..63 in one call or as 0..23, 24..63 gives the same bits (logits, argmax
