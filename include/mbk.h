@@ -183,8 +183,8 @@ int mbk_decode_step(mbk_model *m, int32_t token, int32_t pos, float *logits, int
  * argmax (argmax[0], device int32) of the last position; a following
  * mbk_decode_step with MBK_TOKEN_PREV continues from that argmax.  Equal, to
  * rounding, to n_tokens decode steps at those positions.  The projections
- * run as matrix-core GEMMs over the packed weights (activations as hi/lo bf16
- * pairs, ~16 significant bits, fp32 accumulation); attention is causal over
+ * run as matrix-core GEMMs over the packed weights, bf16 or fp8 (activations
+ * as hi/lo bf16 pairs, ~16 significant bits, fp32 accumulation); attention is causal over
  * cache slots 0 .. pos0 + i for prompt position i, in fp32.  Passage: the
  * MegaBake third-party article, "Where it breaks today" (prefill through the
  * decode-shaped bodies is slow above ~64 tokens) and the project site, "Next"
@@ -325,8 +325,9 @@ enum { MBK_WEIGHTS_BF16 = 0, MBK_WEIGHTS_FP8_E4M3 = 1 };
  * Only before the schedule is planned (as mbk_set_workgroups): MBK_ERR_STATE
  * after, MBK_ERR_ARG for an unknown format; planning fails with
  * MBK_ERR_UNSUPPORTED unless hidden, n_heads*head_dim and intermediate are
- * multiples of 16.  mbk_prefill reads bf16 weights only (MBK_ERR_UNSUPPORTED
- * on an fp8 handle). */
+ * multiples of 16.  mbk_prefill on an fp8 handle runs the same quantised
+ * model (each code widened exactly to bf16 in the GEMM, the row's scale
+ * applied to its output). */
 int mbk_set_weight_format(mbk_model *m, int32_t format);
 
 /* Selects MBK_SYNC_DATAFLOW or MBK_SYNC_BARRIER for following steps

@@ -112,6 +112,8 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g,
                                             int n, int pos, float y) {
     const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
     const bool nrow = n < g.rows;
+    // fp8 rows: the products were formed with the codes' values; the row's power-of-two scale comes here
+    if (g.fmt == FMT_FP8 && nrow) y *= *(const float *)(p.blob + row_scale_offset(g, n));
     if (OP == OP_QKV) {
         // packed rows 2m, 2m+1 of a query or key head are its dims m, m + hd/2 (adjacent lanes)
         const int which = n >= Q + KVr ? 2 : (n >= Q ? 1 : 0);
@@ -152,6 +154,20 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g,
     }
 }
 
+// Eight E4M3 codes (k order, byte j = code j) as the eight bf16 inputs of a matrix-instruction lane: each code
+// is widened to fp32 by the hardware conversion (OCP E4M3 on gfx950) and its top half taken -- exact, since
+// a code's value has at most four significant bits.
+__device__ __forceinline__ pf_u32x4 pf_fp8x8_to_bf16(uint2 c) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false), e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    pf_u32x4 r;
+    r.x = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    r.y = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+    r.z = (__float_as_uint(d[0]) >> 16) | (__float_as_uint(d[1]) & 0xffff0000u);
+    r.w = (__float_as_uint(e[0]) >> 16) | (__float_as_uint(e[1]) & 0xffff0000u);
+    return r;
+}
+
 template <int OP, int kPfRB, int KS>
 __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                      uint64_t bias_off) {
@@ -178,7 +194,13 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
             for (int rb = 0; rb < kPfRB; ++rb) {
                 const int n = n0 + 16 * rb;
                 bw[rb][i] = (pf_u32x4){0u, 0u, 0u, 0u};
-                if (step && n < g.rows && kg < ngrp) bw[rb][i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+                if (step && n < g.rows && kg < ngrp) {
+                    // fp8: the 8 inputs kg are half kg & 1 of 16-code group kg / 2
+                    if (g.fmt == FMT_FP8)
+                        bw[rb][i] = pf_fp8x8_to_bf16(*(const uint2 *)(p.blob + row_group_offset(g, n, kg >> 1) + 8 * (kg & 1)));
+                    else
+                        bw[rb][i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
+                }
             }
             a0h[i] = a0l[i] = a1h[i] = a1l[i] = (pf_u32x4){0u, 0u, 0u, 0u};
             if (step) {

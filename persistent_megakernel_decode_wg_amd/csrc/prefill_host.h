@@ -32,12 +32,13 @@ template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
     // every matrix's k steps are split over four waves whatever the prompt length: the split fixes the order
     // in which a row's products are added, so a prompt's results do not depend on how it is cut into calls.
-    // Four row blocks per workgroup (every activation load feeds four products) while that leaves at least
-    // 256 workgroups, else one (the row blocks per workgroup do not change the order)
+    // Long prompts over bf16 weights: operand tiles shared through LDS; else four row blocks per workgroup
+    // (every activation load feeds four products) while that leaves at least 256 workgroups, else one (none of
+    // these choices changes the order; fp8 matrices always take the per-wave kernel, which widens their codes)
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
     const unsigned xl = (unsigned)((g.rows + 127) / 128), pl = (unsigned)(np_rows / 64);
-    if (np_rows % 64 == 0 && xl * pl >= kPfLMinGroups) {
+    if (g.fmt == FMT_BF16 && np_rows % 64 == 0 && xl * pl >= kPfLMinGroups) {
         static bool lds_set = false;  // per instance: its LDS above the default limit, once
         if (!lds_set) {
             (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP>, hipFuncAttributeMaxDynamicSharedMemorySize, kPfLLds);
@@ -70,7 +71,6 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
     for (int i = 0; i < n_tokens; ++i)
         if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(MBK_ERR_ARG, "token %d at %d outside [0, %d)", tokens[i], i, c.vocab);
     if (!m->blob || !m->kv) return fail(MBK_ERR_STATE, "weights not packed or KV cache not bound");
-    if (m->weight_fmt != FMT_BF16) return fail(MBK_ERR_UNSUPPORTED, "prefill reads bf16 weights only");
     const PfLayout L = pf_layout(c, n_tokens);
     if (!scratch || scratch_bytes < L.total) return fail(MBK_ERR_SIZE, "prefill scratch %zu < %zu bytes", scratch_bytes, L.total);
     if (!aligned(scratch, 256)) return fail(MBK_ERR_ARG, "prefill scratch not 256-byte aligned");
@@ -132,7 +132,7 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
     }
     // the last position: final norm, tied vocabulary projection, argmax
     hipLaunchKernelGGL(k_pf_norm, dim3(1), dim3(256), 0, st, pp, P.final_norm, 0, 0, 1);
-    pf_gemm<OP_LMHEAD>(pp, P.embed, -1, 0, 0, 16, none, st);
+    pf_gemm<OP_LMHEAD>(pp, P.lmhead, -1, 0, 0, 16, none, st);
     hipLaunchKernelGGL(k_pf_argmax, dim3(1), dim3(1024), 0, st, pp);
     HIPCHK(hipGetLastError());
     return MBK_OK;

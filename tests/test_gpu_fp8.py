@@ -5,13 +5,15 @@
 * The decode step of an FP8 handle matches the oracle run on the quantised model -- the bf16 weights the
   codes stand for, value(code) * 2^e, which are exact -- to the same bar as the bf16 path: logits within
   2e-2 of the oracle's standard deviation, the argmax rule, and the cache slot each step writes (layer 0
-  within one bf16 step plus 2^-10 of the RMS, every layer within 2e-2 relative L2)."""
+  within one bf16 step plus 2^-10 of the RMS, every layer within 2e-2 relative L2).
+* Prefill on an FP8 handle matches the same oracle to the same bar, and a prompt taken in two calls gives the
+  one-call bits."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import Pair, log, teacher_forced, upload
+from gpu_util import LOGIT_TOL, Pair, compare, kv_slot_check, log, teacher_forced, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -150,23 +152,79 @@ def test_fp8_maximum_sizes_to_the_last_slot(fp8_pair):
     log("fp8 max sizes worst max|dlogit|/std = %.3g" % worst)
 
 
-def test_fp8_handle_rejects_prefill_and_late_format_change():
-    from persistent_megakernel_decode_wg_amd import (MBK_ERR_STATE, MBK_ERR_UNSUPPORTED, MBK_WEIGHTS_BF16, Decoder,
-                                                     MbkError)
-    import torch
+def test_fp8_handle_rejects_late_format_change():
+    from persistent_megakernel_decode_wg_amd import MBK_ERR_STATE, MBK_WEIGHTS_BF16, Decoder, MbkError
     wl = synth.get("tiny-2L-h64-kv32")
     d = Decoder(wl)
     try:
         _fp8_setup(d)
         d.pack_weights(upload(synth.make_weights(wl)))
         d.alloc_kv()
-        lg = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
-        am = torch.empty(1, dtype=torch.int32, device="cuda")
-        with pytest.raises(MbkError) as e:
-            d.prefill([1, 2, 3], 0, lg, am)
-        assert e.value.code == MBK_ERR_UNSUPPORTED
         with pytest.raises(MbkError) as e:
             d.set_weight_format(MBK_WEIGHTS_BF16)
         assert e.value.code == MBK_ERR_STATE
     finally:
         d.close()
+
+
+class _Fp8Prefill:
+    """An FP8 handle and the oracle on the quantised model, for prefill."""
+
+    def __init__(self, wl, W):
+        import torch
+        from persistent_megakernel_decode_wg_amd import Decoder
+        Wq, _ = oracle.fp8_weights(W)
+        self.dec = Decoder(wl)
+        _fp8_setup(self.dec)
+        self.dec.pack_weights(upload(W))
+        self.dec.alloc_kv()
+        self.ref = oracle.Model(wl, Wq)
+        self.logits = torch.empty(wl.vocab, dtype=torch.float32, device="cuda")
+        self.am = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def prefill(self, toks, pos0):
+        self.dec.prefill(toks, pos0, self.logits, self.am)
+        self.dec.check()
+        return self.logits.cpu().numpy().copy(), int(self.am.item())
+
+    def check(self, toks, pos0, label):
+        lg, am = self.prefill(toks, pos0)
+        lo = ao = None
+        for i, t in enumerate(toks):
+            lo, ao, _ = self.ref.step(int(t), pos0 + i)
+        assert np.all(np.isfinite(lg)), label
+        rel, margin = compare(lg, am, lo, ao)
+        assert rel <= LOGIT_TOL, "%s: max|dlogit| = %.4g std" % (label, rel)
+        kv = self.dec.kv.cpu().numpy().view(np.uint16)
+        for slot in range(pos0, pos0 + len(toks)):
+            x0, r = kv_slot_check(kv[:, :, :, slot, :], self.ref.kv[:, :, :, slot, :])
+            assert x0.max() <= 1.0 and r.max() <= LOGIT_TOL, "%s slot %d" % (label, slot)
+        log("%s: max|dlogit|/std %.3g, margin %.3g" % (label, rel, margin))
+
+    def close(self):
+        self.dec.close()
+
+
+@pytest.mark.parametrize("name", ["tiny-2L-h64-kv32", "smollm135m-kv128"])
+def test_fp8_prefill_against_the_quantised_oracle(name):
+    """Prefill on an FP8 handle (every GEMM widens its weight codes to bf16 exactly and scales the output
+    rows; the vocabulary projection reads the fp8 copy of the embedding) against the oracle stepped on the
+    quantised model: the tiny model's whole cache, the SmolLM-135M 64-token prompt; then the prompt again
+    as two calls, bit for bit."""
+    import torch
+    wl = synth.get(name)
+    W = synth.make_weights(wl)
+    n = wl.kv_capacity if name.startswith("tiny") else wl.n_prompt
+    toks = [int(t) for t in synth.tokens(21, "fp8-prefill", n, wl.vocab)]
+    a, b = _Fp8Prefill(wl, W), _Fp8Prefill(wl, W)
+    try:
+        a.check(toks, 0, "fp8 prefill %s 0..%d" % (name, n - 1))
+        la, ia = a.logits.cpu().numpy().copy(), int(a.am.item())
+        cut = n // 3
+        b.prefill(toks[:cut], 0)
+        lb, ib = b.prefill(toks[cut:], cut)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+        assert torch.equal(a.dec.kv, b.dec.kv)
+    finally:
+        a.close()
+        b.close()
