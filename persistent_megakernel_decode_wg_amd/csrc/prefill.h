@@ -107,13 +107,13 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
 // one row block, 4 with four) whose loads are all issued before the batch's products.  After the k loop lane
 // l holds C[32 by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
 constexpr int kPfPos = 32;
-template <int OP>
+template <int OP, bool FP8 = false>
 __device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g, int layer, int dst, uint64_t bias_off,
                                             int n, int pos, float y) {
     const int hd = p.hd, half = hd >> 1, Q = p.nq * hd, KVr = p.nkv * hd;
     const bool nrow = n < g.rows;
     // fp8 rows: the products were formed with the codes' values; the row's power-of-two scale comes here
-    if (g.fmt == FMT_FP8 && nrow) y *= *(const float *)(p.blob + row_scale_offset(g, n));
+    if (FP8 && nrow) y *= *(const float *)(p.blob + row_scale_offset(g, n));
     if (OP == OP_QKV) {
         // packed rows 2m, 2m+1 of a query or key head are its dims m, m + hd/2 (adjacent lanes)
         const int which = n >= Q + KVr ? 2 : (n >= Q ? 1 : 0);
@@ -168,7 +168,7 @@ __device__ __forceinline__ pf_u32x4 pf_fp8x8_to_bf16(uint2 c) {
     return r;
 }
 
-template <int OP, int kPfRB, int KS>
+template <int OP, int kPfRB, int KS, bool FP8>
 __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                      uint64_t bias_off) {
     constexpr int kPfBatch = kPfRB == 1 ? 8 : 4;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
                 bw[rb][i] = (pf_u32x4){0u, 0u, 0u, 0u};
                 if (step && n < g.rows && kg < ngrp) {
                     // fp8: the 8 inputs kg are half kg & 1 of 16-code group kg / 2
-                    if (g.fmt == FMT_FP8)
+                    if (FP8)
                         bw[rb][i] = pf_fp8x8_to_bf16(*(const uint2 *)(p.blob + row_group_offset(g, n, kg >> 1) + 8 * (kg & 1)));
                     else
                         bw[rb][i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
         for (int j = 0; j < 2; ++j) {
             if (j >= nb) break;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pf_epilogue<OP>(p, g, layer, dst, bias_off, n0 + 16 * rb, pb + 16 * j + 4 * kq + r, acc[rb][j][r]);
+            for (int r = 0; r < 4; ++r) pf_epilogue<OP, FP8>(p, g, layer, dst, bias_off, n0 + 16 * rb, pb + 16 * j + 4 * kq + r, acc[rb][j][r]);
         }
 }
 

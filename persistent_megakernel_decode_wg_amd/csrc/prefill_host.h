@@ -45,10 +45,16 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
             lds_set = true;
         }
         hipLaunchKernelGGL((k_pf_gemm_lds<OP>), dim3(xl, pl), dim3(256), (unsigned)kPfLLds, st, pp, g, layer, src, dst, np_rows, bias);
-    } else if (x4 * py >= 256)
-        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    else
-        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (g.fmt == FMT_FP8) {
+        if (x4 * py >= 256)
+            hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, true>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        else
+            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (x4 * py >= 256) {
+        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, false>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else {
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    }
 }
 
 }  // namespace
