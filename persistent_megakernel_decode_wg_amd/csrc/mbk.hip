@@ -308,6 +308,12 @@ MatGeom make_geom(uint64_t &cursor, int rows, int K, bool pairs, int kind, int n
         g.RT = 1;
         kgp = kg64;
     }
+    // bf16 rows of 2,048 inputs (4 KiB) go two to a tile where there are rows enough for every workgroup: each
+    // tile's reduction and epilogue then serve two rows
+    if (!pairs && fmt == FMT_BF16 && g.L == 64 && kg == 256 && (rows + 1) / 2 >= n_wg) {
+        g.L = 32;
+        g.RT = 2;
+    }
     g.K = K;
     g.IT = kgp / g.L;
     g.rows = rows;
