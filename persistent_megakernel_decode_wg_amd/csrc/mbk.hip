@@ -574,8 +574,13 @@ std::string build_plan(mbk_model *m) {
     if (P.lds_tasks + (size_t)P.max_tasks * 16 > (size_t)P.lds_rope) return "task list does not fit its LDS slot";
     P.ring_bytes = (int)ring;
     P.lds_bytes = off + ring;
-    // attention pieces: at most a third of the ring, keys and values each rounded up to whole chunks
-    P.piece_pos = std::min(kPiecePos, (int)((ring / 3 / 2) / kChunk * kChunk / ((size_t)hd * 2)));
+    // attention pieces: at most a third of the ring, keys and values each rounded up to whole chunks; where
+    // every split holds at most 2 kPiecePos positions, up to that many in one piece of at most 60 % of the ring
+    // (one piece per split: its bookkeeping once)
+    const int longest = std::max((c.kv_capacity + P.max_splits - 1) / P.max_splits, (int)m->attn_min_chunk);
+    const bool one_piece = longest <= 2 * kPiecePos;
+    P.piece_pos = std::min(one_piece ? 2 * kPiecePos : kPiecePos,
+                           (int)(((one_piece ? ring * 6 / 10 : ring / 3) / 2) / kChunk * kChunk / ((size_t)hd * 2)));
     if (P.piece_pos < 1) return "attention piece too small";
     while (P.piece_pos & (P.piece_pos - 1)) P.piece_pos &= P.piece_pos - 1;  // a power of two
 
