@@ -94,7 +94,8 @@ def test_no_device_is_reported_as_hip_error(L):
                                   "smollm1.7b-kv4096", "stream-1l-v262144"])
 def test_plan_fits_lds_and_ring_rules(name):
     """The host planner (no device: workgroups fixed) keeps every workgroup inside the 160 KiB of LDS, every
-    GEMV task run within half the ring, every attention piece within a third, and the packed payload at
+    GEMV task run within half the ring, every attention piece within a third (60 % where one piece holds a whole
+    split), and the packed payload at
     2 bytes per parameter."""
     from persistent_megakernel_decode_wg_amd import Decoder
     wl = synth.get(name)
@@ -107,7 +108,12 @@ def test_plan_fits_lds_and_ring_rules(name):
     assert info["max_tile_bytes"] * 3 <= info["ring_bytes"]
     assert info["piece_positions"] >= 1
     seg = (info["piece_positions"] * wl.head_dim * 2 + 1023) // 1024 * 1024   # keys (or values) of one piece
-    assert 2 * seg * 3 <= info["ring_bytes"]
+    # a third of the ring; up to 60 % where every split (at least 128 positions) fits in one piece of 256
+    longest = max(-(-wl.kv_capacity // info["max_splits"]), 128)
+    if longest <= 256:
+        assert 2 * seg * 10 <= info["ring_bytes"] * 6 and info["piece_positions"] <= 256
+    else:
+        assert 2 * seg * 3 <= info["ring_bytes"] and info["piece_positions"] <= 128
     # packed matrices are exactly 2 bytes per parameter (plus norms, RoPE table and schedule tables)
     assert info["packed_bytes"] >= 2 * wl.param_count()
     d.close()
