@@ -457,9 +457,10 @@ MBK_DEV int step_pos(const Params &p) {
 // compute waves derive the same sequence of allocations from the task list
 // and the step's position.  An allocation is placed at the current virtual
 // ring offset, or at the next multiple of the ring size if it would straddle
-// the ring's end.  A GEMV task's weights take at most half the ring (a
+// the ring's end.  A GEMV task's weights take at most a third of the ring (a
 // block longer than that goes in runs of whole rounds of the compute waves
-// of at most a third of the ring), an attention piece at most a third; a loader
+// of at most a third of the ring), an attention piece at most a third (60 %
+// where one piece holds a whole split); a loader
 // waiting for space only ever waits for allocations it has already issued,
 // which the compute waves consume and release.
 

@@ -499,14 +499,16 @@ std::string build_plan(mbk_model *m) {
         if (P.in_double) fixed += in_block;
     }
 
-    // tile runs of at most half the ring: first size the ring assuming a task
+    // tile runs of at most a third of the ring: first size the ring assuming a task
     // list of 64 entries per workgroup, then build the lists and shrink the ring
     // to what the lists leave.
     size_t max_tile = 0;
     for (const Interval &v : P.iv)
         if (v.op != OP_ATTN) max_tile = std::max(max_tile, (size_t)v.mat.tb);
     auto build_tasks = [&](size_t ring) {
-        const size_t max_alloc = ring / 2;
+        // a run takes at most a third of the ring (the loader then has two runs' room while one is computed:
+        // the SmolLM-1.7B down projection's 16 KiB tiles go two to a run rather than three)
+        const size_t max_alloc = ring / 3;
         P.task_list.clear();
         P.task_index.assign((size_t)n_wg * (n_iv + 1), 0);
         int max_tasks = 0;

@@ -94,7 +94,7 @@ def test_no_device_is_reported_as_hip_error(L):
                                   "smollm1.7b-kv4096", "stream-1l-v262144"])
 def test_plan_fits_lds_and_ring_rules(name):
     """The host planner (no device: workgroups fixed) keeps every workgroup inside the 160 KiB of LDS, every
-    GEMV task run within half the ring, every attention piece within a third (60 % where one piece holds a whole
+    GEMV task run within a third of the ring, every attention piece within a third (60 % where one piece holds a whole
     split), and the packed payload at
     2 bytes per parameter."""
     from persistent_megakernel_decode_wg_amd import Decoder
@@ -104,7 +104,7 @@ def test_plan_fits_lds_and_ring_rules(name):
     info = d.describe()
     assert info["workgroups"] == 256 and info["intervals"] == 5 * wl.n_layers + 1
     assert info["lds_bytes"] + 512 <= 160 * 1024
-    assert info["max_task_bytes"] * 2 <= info["ring_bytes"]
+    assert info["max_task_bytes"] * 3 <= info["ring_bytes"]
     assert info["max_tile_bytes"] * 3 <= info["ring_bytes"]
     assert info["piece_positions"] >= 1
     seg = (info["piece_positions"] * wl.head_dim * 2 + 1023) // 1024 * 1024   # keys (or values) of one piece
