@@ -257,10 +257,10 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
 }
 
 // The same products for long prompts, with operand tiles shared by the workgroup's four waves: a workgroup
-// takes 128 packed rows x 64 positions; wave (wr, wc) = (w / 2, w % 2) computes rows 64 wr .. + 63 (four
-// row blocks) x positions 32 wc .. + 31 (two position blocks).  Every 16 x 32 operand tile of a k step (the
-// 16 rows' input groups 4 s .. 4 s + 3, one 16-byte group per lane exactly as the matrix instruction takes
-// it) is loaded once for the workgroup straight into LDS (global_load_lds, 1 KiB per wave-wide load), so each
+// takes 32 WRB packed rows x 64 positions; wave (wr, wc) = (w / 2, w % 2) computes rows 16 WRB wr .. (WRB row
+// blocks) x positions 32 wc .. + 31 (two position blocks).  Every 16 x 32 operand tile of a k step (the 16
+// rows' input groups 4 s .. 4 s + 3, one 16-byte group per lane exactly as the matrix instruction takes it)
+// is loaded once for the workgroup straight into LDS (global_load_lds, 1 KiB per wave-wide load), so each
 // weight tile feeds two waves and each activation tile two; the loads run kPfLAhead stages (of kPfLStep k
 // steps) ahead of the products.  Each row's products are formed in the order of k_pf_gemm<., ., 4>: the k
 // steps in four contiguous quarters, each quarter's chain from zero (hi then lo input per step), and the
@@ -268,27 +268,32 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
 // matrix's K and rows past its end are read clamped: they meet zero inputs or feed no output).
 constexpr int kPfLStep = 1;                              // k steps per stage
 constexpr int kPfLAhead = 2;                             // stages in flight ahead of the one computed
-constexpr int kPfLTiles = 16 * kPfLStep;                 // 1 KiB tiles per stage: 8 activation + 8 weight per step
-constexpr int kPfLStageBytes = kPfLTiles * 1024;
-constexpr int kPfLLds = (kPfLAhead + 1) * kPfLStageBytes;
+template <int WRB> struct PfLGeom {
+    static constexpr int kTiles = (8 + 2 * WRB) * kPfLStep;  // 1 KiB tiles per stage: 8 activation + 2 WRB weight
+    static constexpr int kStageBytes = kTiles * 1024;
+    static constexpr int kLds = (kPfLAhead + 1) * kStageBytes;
+    static_assert(kTiles % 4 == 0, "every wave issues the same number of loads per stage");
+};
 typedef __attribute__((address_space(3))) void pf_lds_void_t;
 typedef __attribute__((address_space(1))) void pf_glb_void_t;
 
-template <int OP>
+template <int OP, int WRB>
 __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                      uint64_t bias_off) {
+    typedef PfLGeom<WRB> Gm;
+    constexpr int kPerStep = 8 + 2 * WRB;                 // tiles of one k step
     extern __shared__ __attribute__((aligned(16))) uint8_t pf_ring[];
     const int l = threadIdx.x & 63, wv = threadIdx.x >> 6, wr = wv >> 1, wc = wv & 1;
-    const int rbase = blockIdx.x * 128, pbase = blockIdx.y * 64;
+    const int rbase = blockIdx.x * 32 * WRB, pbase = blockIdx.y * 64;
     const int ngrp = g.K >> 3, nall = (ngrp + 3) >> 2, nst = (nall + kPfLStep - 1) / kPfLStep;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
-    // the loads of stage st: wave w issues tiles w, w + 4, ... of the stage (4 per k step); tile u of a k step
-    // is activation block u / 2 (hi for even u, lo for odd) for u < 8, weight row block u - 8 after
+    // the loads of stage st: wave w issues tiles w, w + 4, ... of the stage; tile u of a k step is
+    // activation block u / 2 (hi for even u, lo for odd) for u < 8, weight row block u - 8 after
     auto issue = [&](int st) {
-        uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * kPfLStageBytes;
+        uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * Gm::kStageBytes;
 #pragma unroll
-        for (int t = wv; t < kPfLTiles; t += 4) {
-            const int i = t >> 4, u = t & 15, s = st * kPfLStep + i;
+        for (int t = wv; t < Gm::kTiles; t += 4) {
+            const int i = t / kPerStep, u = t - i * kPerStep, s = st * kPfLStep + i;
             if (s >= nall) continue;
             const int kg = 4 * s + (l >> 4);
             const uint8_t *a;
@@ -302,15 +307,15 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
             __builtin_amdgcn_global_load_lds((pf_glb_void_t *)a, (pf_lds_void_t *)(buf + t * 1024), 16, 0, 0);
         }
     };
-    pf_f32x4 acc[4][2], tot[4][2];
+    pf_f32x4 acc[WRB][2], tot[WRB][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < WRB; ++rb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[rb][j] = tot[rb][j] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
     int q = 0, qend = nall / 4;  // current quarter and its end (quarter q is [nall q / 4, nall (q + 1) / 4))
     auto close_quarter = [&]() {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < WRB; ++rb)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 tot[rb][j] = q == 0 ? acc[rb][j] : tot[rb][j] + acc[rb][j];
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
     for (int st = 0; st < kPfLAhead && st < nst; ++st) issue(st);
     for (int st = 0; st < nst; ++st) {
         // this wave's loads of stage st are complete once at most those of the later stages in flight remain
-        // (4 per k step; the last stage may hold fewer, so near the end nothing may remain)
-        // (and its reads of stage st - 1 are complete before another wave's loads may overwrite that stage)
-        constexpr int kLater = 4 * kPfLStep * (kPfLAhead - 1);  // this wave's loads of kPfLAhead - 1 full stages
+        // (the last stage may hold fewer, so near the end nothing may remain), and its reads of stage st - 1
+        // are complete before another wave's loads may overwrite that stage
+        constexpr int kLater = Gm::kTiles / 4 * (kPfLAhead - 1);  // this wave's loads of kPfLAhead - 1 full stages
         static_assert(kLater < 64, "vmcnt range");
         if (st + kPfLAhead < nst) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kLater) : "memory");
         else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -333,23 +338,23 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (st + kPfLAhead < nst) issue(st + kPfLAhead);
-        const uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * kPfLStageBytes;
+        const uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * Gm::kStageBytes;
 #pragma unroll
         for (int i = 0; i < kPfLStep; ++i) {
             const int s = st * kPfLStep + i;
             if (s >= nall) break;
             while (q < 3 && s >= qend) close_quarter();
-            const uint8_t *tb = buf + i * 16 * 1024 + l * 16;
-            pf_u32x4 xa[2][2], wb[4];
+            const uint8_t *tb = buf + i * kPerStep * 1024 + l * 16;
+            pf_u32x4 xa[2][2], wb[WRB];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 xa[j][0] = *(const pf_u32x4 *)(tb + (2 * (2 * wc + j) + 0) * 1024);
                 xa[j][1] = *(const pf_u32x4 *)(tb + (2 * (2 * wc + j) + 1) * 1024);
             }
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) wb[rb] = *(const pf_u32x4 *)(tb + (8 + 4 * wr + rb) * 1024);
+            for (int rb = 0; rb < WRB; ++rb) wb[rb] = *(const pf_u32x4 *)(tb + (8 + WRB * wr + rb) * 1024);
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int rb = 0; rb < WRB; ++rb) {
                 const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, wb[rb]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
@@ -364,12 +369,12 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
     while (q < 4) close_quarter();  // the remaining quarters (possibly empty) in order
     const int kq = l >> 4;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < WRB; ++rb)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                pf_epilogue<OP>(p, g, layer, dst, bias_off, rbase + 64 * wr + 16 * rb + (l & 15),
+                pf_epilogue<OP>(p, g, layer, dst, bias_off, rbase + 16 * WRB * wr + 16 * rb + (l & 15),
                                 pbase + 32 * wc + 16 * j + 4 * kq + r, tot[rb][j][r]);
 }
 

@@ -28,23 +28,41 @@ PfLayout pf_layout(const mbk_config &c, int n) {
 
 constexpr unsigned kPfLMinGroups = 128;  // workgroups the shared-tile GEMM needs to fill the device
 
+// One shared-tile GEMM launch (its LDS above the default limit is allowed once per instance).
+template <int OP, int WRB>
+void pf_gemm_lds(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias,
+                 hipStream_t st) {
+    static bool lds_set = false;
+    if (!lds_set) {
+        (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP, WRB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  PfLGeom<WRB>::kLds);
+        lds_set = true;
+    }
+    const dim3 grid((unsigned)((g.rows + 32 * WRB - 1) / (32 * WRB)), (unsigned)(np_rows / 64));
+    hipLaunchKernelGGL((k_pf_gemm_lds<OP, WRB>), grid, dim3(256), (unsigned)PfLGeom<WRB>::kLds, st, pp, g, layer, src,
+                       dst, np_rows, bias);
+}
+
 template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
     // every matrix's k steps are split over four waves whatever the prompt length: the split fixes the order
     // in which a row's products are added, so a prompt's results do not depend on how it is cut into calls.
-    // Long prompts over bf16 weights: operand tiles shared through LDS; else four row blocks per workgroup
-    // (every activation load feeds four products) while that leaves at least 256 workgroups, else one (none of
-    // these choices changes the order; fp8 matrices always take the per-wave kernel, which widens their codes)
+    // Long prompts over bf16 weights: operand tiles shared through LDS (128-row workgroup tiles, or 64-row ones
+    // where the 128-row tiles would leave fewer than two workgroups per compute unit); else four row blocks
+    // per workgroup (every activation load feeds four products) while that leaves at least 256 workgroups,
+    // else one (none of these choices changes the order; fp8 matrices always take the per-wave kernel, which
+    // widens their codes)
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
-    const unsigned xl = (unsigned)((g.rows + 127) / 128), pl = (unsigned)(np_rows / 64);
-    if (g.fmt == FMT_BF16 && np_rows % 64 == 0 && xl * pl >= kPfLMinGroups) {
-        static bool lds_set = false;  // per instance: its LDS above the default limit, once
-        if (!lds_set) {
-            (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP>, hipFuncAttributeMaxDynamicSharedMemorySize, kPfLLds);
-            lds_set = true;
-        }
-        hipLaunchKernelGGL((k_pf_gemm_lds<OP>), dim3(xl, pl), dim3(256), (unsigned)kPfLLds, st, pp, g, layer, src, dst, np_rows, bias);
+    const unsigned pl = (unsigned)(np_rows / 64);
+    const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
+    const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
+    if (lds_ok && g4 >= 512) {
+        pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
+    } else if (lds_ok && g2 >= 256 && g4 >= kPfLMinGroups) {
+        pf_gemm_lds<OP, 2>(pp, g, layer, src, dst, np_rows, bias, st);
+    } else if (lds_ok && g4 >= kPfLMinGroups) {
+        pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
     } else if (g.fmt == FMT_FP8) {
         if (x4 * py >= 256)
             hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, true>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
