@@ -97,15 +97,15 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
 }
 
 // C[pos][n] = sum_k in[pos][k] W[n][k] for the packed matrix g.  A workgroup takes packed rows
-// [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [32 by, 32 by + 32) (two position blocks)
-// of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds RB matrix
-// products and every weight load two.  RB = 4 where that still leaves enough workgroups to fill the device,
-// else RB = 1.  The k steps are split over KS waves (contiguous ranges; the partial tiles are added through
-// LDS in wave order by wave 0, so the result depends neither on timing nor on RB), which multiplies the loads
-// in flight and shortens each wave's chain.  Lane l feeds row l % 16
+// [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [16 NPB by, 16 NPB (by + 1)) (NPB position
+// blocks of 16) of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds
+// RB matrix products and every weight load NPB.  RB = 4, NPB = 2 where that still leaves enough workgroups to
+// fill the device, else RB = NPB = 1.  The k steps are split over KS waves (contiguous ranges; the partial
+// tiles are added through LDS in wave order by wave 0, so the result depends neither on timing nor on RB or
+// NPB), which multiplies the loads in flight and shortens each wave's chain.  Lane l feeds row l % 16
 // of each operand with input group 4 s + l / 16 of k step s (32 inputs); the k steps go in batches (8 with
 // one row block, 4 with four) whose loads are all issued before the batch's products.  After the k loop lane
-// l holds C[32 by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
+// l holds C[16 NPB by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
 constexpr int kPfPos = 32;
 template <int OP, bool FP8 = false>
 __device__ __forceinline__ void pf_epilogue(const PfParams &p, const MatGeom &g, int layer, int dst, uint64_t bias_off,
@@ -168,24 +168,26 @@ __device__ __forceinline__ pf_u32x4 pf_fp8x8_to_bf16(uint2 c) {
     return r;
 }
 
-template <int OP, int kPfRB, int KS, bool FP8>
+template <int OP, int kPfRB, int KS, bool FP8, int NPB>
 __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                      uint64_t bias_off) {
     constexpr int kPfBatch = kPfRB == 1 ? 8 : 4;
     const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16 * kPfRB + (l & 15);  // this lane's row in row block 0 (+16 rb)
-    const int pb = blockIdx.y * kPfPos;
-    const int nb = min(kPfPos, np_rows - pb) >> 4;       // position blocks of 16: 1 or 2
+    const int pb = blockIdx.y * 16 * NPB;
+    const int nb = min(16 * NPB, np_rows - pb) >> 4;    // position blocks of 16: 1 .. NPB
     const int kq = l >> 4, ngrp = g.K >> 3, nall = (ngrp + 3) >> 2;
     // this wave's k steps [sb, sb + nsteps)
     const int sb = nall * wv / KS, nsteps = nall * (wv + 1) / KS - sb;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
-    const size_t arow0 = (size_t)(pb + (l & 15)) * p.ks, arow1 = arow0 + (size_t)16 * p.ks;
-    pf_f32x4 acc[kPfRB][2];
+    const size_t arow0 = (size_t)(pb + (l & 15)) * p.ks;
+    pf_f32x4 acc[kPfRB][NPB];
 #pragma unroll
-    for (int rb = 0; rb < kPfRB; ++rb) acc[rb][0] = acc[rb][1] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kPfRB; ++rb)
+#pragma unroll
+        for (int j = 0; j < NPB; ++j) acc[rb][j] = (pf_f32x4){0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsteps; s0 += kPfBatch) {
-        pf_u32x4 bw[kPfRB][kPfBatch], a0h[kPfBatch], a0l[kPfBatch], a1h[kPfBatch], a1l[kPfBatch];
+        pf_u32x4 bw[kPfRB][kPfBatch], xh[NPB][kPfBatch], xl[NPB][kPfBatch];
 #pragma unroll
         for (int i = 0; i < kPfBatch; ++i) {
             const int kg = 4 * (sb + s0 + i) + kq;
@@ -202,54 +204,53 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(PfParams p, MatGeom g, int 
                         bw[rb][i] = *(const pf_u32x4 *)(p.blob + row_group_offset(g, n, kg));
                 }
             }
-            a0h[i] = a0l[i] = a1h[i] = a1l[i] = (pf_u32x4){0u, 0u, 0u, 0u};
-            if (step) {
-                a0h[i] = *(const pf_u32x4 *)(ah + arow0 + 8 * kg);
-                a0l[i] = *(const pf_u32x4 *)(al + arow0 + 8 * kg);
-                if (nb > 1) {
-                    a1h[i] = *(const pf_u32x4 *)(ah + arow1 + 8 * kg);
-                    a1l[i] = *(const pf_u32x4 *)(al + arow1 + 8 * kg);
+#pragma unroll
+            for (int j = 0; j < NPB; ++j) {
+                xh[j][i] = xl[j][i] = (pf_u32x4){0u, 0u, 0u, 0u};
+                if (step && j < nb) {
+                    const size_t at = arow0 + (size_t)16 * j * p.ks + 8 * kg;
+                    xh[j][i] = *(const pf_u32x4 *)(ah + at);
+                    xl[j][i] = *(const pf_u32x4 *)(al + at);
                 }
             }
         }
 #pragma unroll
         for (int i = 0; i < kPfBatch; ++i) {
-            const pf_bf16x8 x0h = __builtin_bit_cast(pf_bf16x8, a0h[i]), x0l = __builtin_bit_cast(pf_bf16x8, a0l[i]);
-            const pf_bf16x8 x1h = __builtin_bit_cast(pf_bf16x8, a1h[i]), x1l = __builtin_bit_cast(pf_bf16x8, a1l[i]);
 #pragma unroll
             for (int rb = 0; rb < kPfRB; ++rb) {
                 const pf_bf16x8 b = __builtin_bit_cast(pf_bf16x8, bw[rb][i]);
-                acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0h, b, acc[rb][0], 0, 0, 0);
-                acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0l, b, acc[rb][0], 0, 0, 0);
-                acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1h, b, acc[rb][1], 0, 0, 0);
-                acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1l, b, acc[rb][1], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NPB; ++j) {
+                    acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, xh[j][i]), b,
+                                                                         acc[rb][j], 0, 0, 0);
+                    acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, xl[j][i]), b,
+                                                                         acc[rb][j], 0, 0, 0);
+                }
             }
         }
     }
     if (KS > 1) {
         // partial tiles of the waves, added in wave order
-        __shared__ pf_f32x4 part[KS > 1 ? KS - 1 : 1][kPfRB][2][64];
+        __shared__ pf_f32x4 part[KS > 1 ? KS - 1 : 1][kPfRB][NPB][64];
         if (wv > 0)
 #pragma unroll
-            for (int rb = 0; rb < kPfRB; ++rb) {
-                part[wv - 1][rb][0][l] = acc[rb][0];
-                part[wv - 1][rb][1][l] = acc[rb][1];
-            }
+            for (int rb = 0; rb < kPfRB; ++rb)
+#pragma unroll
+                for (int j = 0; j < NPB; ++j) part[wv - 1][rb][j][l] = acc[rb][j];
         __syncthreads();
         if (wv > 0) return;
 #pragma unroll
         for (int w = 0; w < KS - 1; ++w)
 #pragma unroll
-            for (int rb = 0; rb < kPfRB; ++rb) {
-                acc[rb][0] += part[w][rb][0][l];
-                acc[rb][1] += part[w][rb][1][l];
-            }
+            for (int rb = 0; rb < kPfRB; ++rb)
+#pragma unroll
+                for (int j = 0; j < NPB; ++j) acc[rb][j] += part[w][rb][j][l];
     }
     // epilogue: lane l holds C[pb + 16 j + 4 kq + r][n0 + 16 rb]
 #pragma unroll
     for (int rb = 0; rb < kPfRB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NPB; ++j) {
             if (j >= nb) break;
 #pragma unroll
             for (int r = 0; r < 4; ++r) pf_epilogue<OP, FP8>(p, g, layer, dst, bias_off, n0 + 16 * rb, pb + 16 * j + 4 * kq + r, acc[rb][j][r]);

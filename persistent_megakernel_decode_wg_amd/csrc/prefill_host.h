@@ -27,6 +27,7 @@ PfLayout pf_layout(const mbk_config &c, int n) {
 }
 
 constexpr unsigned kPfLMinGroups = 128;  // workgroups the shared-tile GEMM needs to fill the device
+constexpr size_t kPfOnePbWeights = (size_t)8 << 20;  // largest matrix whose per-wave GEMM takes one position block
 
 // One shared-tile GEMM launch (its LDS above the default limit is allowed once per instance).
 template <int OP, int WRB>
@@ -49,14 +50,17 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     // in which a row's products are added, so a prompt's results do not depend on how it is cut into calls.
     // Long prompts over bf16 weights: operand tiles shared through LDS (128-row workgroup tiles, or 64-row ones
     // where the 128-row tiles would leave fewer than two workgroups per compute unit); else four row blocks
-    // per workgroup (every activation load feeds four products) while that leaves at least 256 workgroups,
-    // else one (none of these choices changes the order; fp8 matrices always take the per-wave kernel, which
-    // widens their codes)
-    const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos);
+    // and two position blocks per workgroup (every activation load feeds four products, every weight load
+    // two) while that leaves at least 256 workgroups, else one row block and one position block for matrices
+    // of up to 8M weights (four times the workgroups; the weights, read once per position block, come back
+    // from cache) and two position blocks for larger ones (none of these choices changes the order; fp8
+    // matrices always take the per-wave kernel, which widens their codes)
+    const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos), p16 = (unsigned)(np_rows / 16);
     const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
     const unsigned pl = (unsigned)(np_rows / 64);
     const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
     const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
+    const bool one_pb = (size_t)g.rows * g.K <= kPfOnePbWeights;
     if (lds_ok && g4 >= 512) {
         pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
     } else if (lds_ok && g2 >= 256 && g4 >= kPfLMinGroups) {
@@ -65,13 +69,17 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
         pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
     } else if (g.fmt == FMT_FP8) {
         if (x4 * py >= 256)
-            hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, true>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+            hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, true, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        else if (one_pb)
+            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
         else
-            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     } else if (x4 * py >= 256) {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, false>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, false, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (one_pb) {
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     } else {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     }
 }
 

@@ -222,3 +222,24 @@ def test_prefill_long_prompt_equals_short_chunks_bitwise(make):
         lb, ib = b.prefill(toks[c:c + 64], c)
     assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
     assert torch.equal(a.dec.kv, b.dec.kv)
+
+
+def test_prefill_1p7b_shape_kernel_forms_agree_bitwise(make):
+    """Two layers of the SmolLM-1.7B shape: a 256-token prompt in one call (query/key/value and gate/up
+    projections with operand tiles shared through LDS, output and down projections with four row blocks and two
+    position blocks per workgroup) and in four calls of 64 tokens (gate/up still through LDS; one row block per
+    workgroup for the rest, with one position block for the 4M-weight output projection and two for the larger
+    query/key/value and down matrices) give the same logits, argmax and cache bit for bit; the first 64-token
+    call is also checked against the oracle."""
+    import torch
+    wl = synth.Workload("smollm1.7b-2L-kv512", 2, 2048, 32, 32, 64, 8192, 49152, 512, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=0, n_decode=0)
+    W = synth.make_weights(wl)
+    a, b = make(wl, W), make(wl, W)
+    toks = [int(t) for t in synth.tokens(23, "prefill-forms", 256, wl.vocab)]
+    la, ia = a.prefill(toks, 0)
+    b.check(toks[:64], 0, "smollm1.7b shape, 2 layers, prefill 0..63")
+    for c in range(64, 256, 64):
+        lb, ib = b.prefill(toks[c:c + 64], c)
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+    assert torch.equal(a.dec.kv, b.dec.kv)
