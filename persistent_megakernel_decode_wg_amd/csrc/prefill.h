@@ -100,11 +100,11 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
 // [16 RB bx, 16 RB (bx + 1)) (RB row blocks of 16) and positions [16 NPB by, 16 NPB (by + 1)) (NPB position
 // blocks of 16) of input buffer `src` (np_rows rows in all, a multiple of 16), so every activation load feeds
 // RB matrix products and every weight load NPB.  RB = 4, NPB = 2 where that still leaves enough workgroups to
-// fill the device, else RB = NPB = 1.  The k steps are split over KS waves (contiguous ranges; the partial
+// fill the device, else RB = 2 or 1 and NPB = 1 or 2 by the matrix's size.  The k steps are split over KS waves (contiguous ranges; the partial
 // tiles are added through LDS in wave order by wave 0, so the result depends neither on timing nor on RB or
 // NPB), which multiplies the loads in flight and shortens each wave's chain.  Lane l feeds row l % 16
 // of each operand with input group 4 s + l / 16 of k step s (32 inputs); the k steps go in batches (8 with
-// one row block, 4 with four) whose loads are all issued before the batch's products.  After the k loop lane
+// one row block, 4 with two or four) whose loads are all issued before the batch's products.  After the k loop lane
 // l holds C[16 NPB by + 16 j + 4 (l / 16) + r][16 RB bx + 16 rb + l % 16] in acc[rb][j][r].  Epilogue by op.
 constexpr int kPfPos = 32;
 template <int OP, bool FP8 = false>

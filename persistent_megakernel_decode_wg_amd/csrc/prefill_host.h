@@ -51,12 +51,12 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     // Long prompts over bf16 weights: operand tiles shared through LDS (128-row workgroup tiles, or 64-row ones
     // where the 128-row tiles would leave fewer than two workgroups per compute unit); else four row blocks
     // and two position blocks per workgroup (every activation load feeds four products, every weight load
-    // two) while that leaves at least 256 workgroups, else one row block and one position block for matrices
-    // of up to 8M weights (four times the workgroups; the weights, read once per position block, come back
-    // from cache) and two position blocks for larger ones (none of these choices changes the order; fp8
-    // matrices always take the per-wave kernel, which widens their codes)
+    // two) while that leaves at least 256 workgroups; else, for matrices of up to 8M weights, one position
+    // block per workgroup, and for larger ones two; with two row blocks while that leaves 256 workgroups, else
+    // one (none of these choices changes the order; fp8 matrices always take the per-wave kernel, which widens
+    // their codes, with four row blocks and two position blocks or one row block)
     const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos), p16 = (unsigned)(np_rows / 16);
-    const unsigned x4 = (unsigned)((g.rows + 63) / 64), x1 = (unsigned)((g.rows + 15) / 16);
+    const unsigned x4 = (unsigned)((g.rows + 63) / 64), x2 = (unsigned)((g.rows + 31) / 32), x1 = (unsigned)((g.rows + 15) / 16);
     const unsigned pl = (unsigned)(np_rows / 64);
     const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
     const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
@@ -76,8 +76,12 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
             hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     } else if (x4 * py >= 256) {
         hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, false, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (one_pb && x2 * p16 >= 256) {
+        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, false, 1>), dim3(x2, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     } else if (one_pb) {
         hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    } else if (x2 * py >= 256) {
+        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, false, 2>), dim3(x2, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     } else {
         hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
     }
