@@ -55,16 +55,18 @@ __device__ __forceinline__ void pf_store_split(uint16_t *dh, uint16_t *dl, int i
 }
 
 // RMSNorm of x row r (or of the embedding row of its token when from_embed, which also sets x) times the
-// bf16 weight at norm_off, split into hi/lo row `dst_row` of input buffer `dst`.  One workgroup of 256
-// threads per row.
+// bf16 weight at norm_off, split into hi/lo row `dst_row` of input buffer `dst`, two entries per 32-bit store;
+// entries [H, H rounded up to 32) are cleared (the GEMMs read a row's inputs in k steps of 32 and nothing past
+// them).  One workgroup of 256 threads per row.
 __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, int dst, int from_embed, int last_only) {
     __shared__ float red[8];
     const int r = last_only ? p.P - 1 : (int)blockIdx.x;
     const int dst_row = last_only ? 0 : r;
+    const int h32 = (p.H + 31) & ~31;
     float *xr = p.x + (size_t)r * p.H;
     uint16_t *dh = p.inh[dst] + (size_t)dst_row * p.ks, *dl = p.inl[dst] + (size_t)dst_row * p.ks;
     if (r >= p.P) {  // padding rows of the position tiles: zero inputs
-        for (int i = threadIdx.x; i < p.ks; i += 256) dh[i] = dl[i] = 0;
+        for (int i = 2 * (int)threadIdx.x; i < h32; i += 512) *(uint32_t *)(dh + i) = *(uint32_t *)(dl + i) = 0u;
         return;
     }
     if (from_embed) {
@@ -83,16 +85,22 @@ __global__ __launch_bounds__(256) void k_pf_norm(PfParams p, uint64_t norm_off, 
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float rn = rsqrtf(tot / (float)p.H + p.eps);
     const uint16_t *w = (const uint16_t *)(p.blob + norm_off);
-    for (int i = threadIdx.x; i < p.ks; i += 256) {
-        if (i < p.H) pf_store_split(dh, dl, i, xr[i] * rn * pf_bf16f(w[i]));
-        else dh[i] = dl[i] = 0;
+    for (int i = 2 * (int)threadIdx.x; i < h32; i += 512) {
+        uint32_t hh = 0u, ll = 0u;
+        if (i < p.H) {  // H is a multiple of 8: i + 1 < H too
+            const float v0 = xr[i] * rn * pf_bf16f(w[i]), v1 = xr[i + 1] * rn * pf_bf16f(w[i + 1]);
+            const uint16_t h0 = pf_to_bf16(v0), h1 = pf_to_bf16(v1);
+            hh = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            ll = (uint32_t)pf_to_bf16(v0 - pf_bf16f(h0)) | ((uint32_t)pf_to_bf16(v1 - pf_bf16f(h1)) << 16);
+        }
+        *(uint32_t *)(dh + i) = hh;
+        *(uint32_t *)(dl + i) = ll;
     }
     if (last_only) {
         // rows 1 .. 15 of the vocabulary projection's position block
-        for (int i = threadIdx.x; i < 15 * p.ks; i += 256) {
-            p.inh[dst][p.ks + i] = 0;
-            p.inl[dst][p.ks + i] = 0;
-        }
+        for (int rr = 1; rr < 16; ++rr)
+            for (int i = 2 * (int)threadIdx.x; i < h32; i += 512)
+                *(uint32_t *)(p.inh[dst] + (size_t)rr * p.ks + i) = *(uint32_t *)(p.inl[dst] + (size_t)rr * p.ks + i) = 0u;
     }
 }
 
@@ -379,10 +387,11 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
                                 pbase + 32 * wc + 16 * j + 4 * kq + r, tot[rb][j][r]);
 }
 
-// Columns [K, ks) of the rows written by the gate/up epilogue (the down projection's k tail reads them).
+// Columns [K, K rounded up to 32) of the rows written by the attention or the gate/up epilogue (the next
+// GEMM reads a row in k steps of 32).
 __global__ __launch_bounds__(256) void k_pf_clear_tail(PfParams p, int buf, int K) {
     const int r = blockIdx.x;
-    for (int i = K + (int)threadIdx.x; i < p.ks; i += 256) {
+    for (int i = K + (int)threadIdx.x; i < ((K + 31) & ~31); i += 256) {
         p.inh[buf][(size_t)r * p.ks + i] = 0;
         p.inl[buf][(size_t)r * p.ks + i] = 0;
     }

@@ -119,6 +119,25 @@ def test_plan_fits_lds_and_ring_rules(name):
     d.close()
 
 
+def test_planner_reports_a_tile_too_large_for_the_ring():
+    """An input width whose 8-value groups number an odd 65 (intermediate 520) packs 64 rows to a tile, 66.5 KB,
+    more than a third of the ring: planning fails with MBK_ERR_UNSUPPORTED and says why; 528 (66 groups, 32 rows
+    to a tile) plans."""
+    from persistent_megakernel_decode_wg_amd import Decoder, MbkError, MBK_ERR_UNSUPPORTED
+    for inter, ok in ((520, False), (528, True)):
+        wl = synth.Workload("ragged-%d" % inter, 2, 200, 5, 1, 16, inter, 1024, 128, False, 1e-5, 1e4,
+                            n_prompt=0, kv_prefill=0, n_decode=0)
+        d = Decoder(wl)
+        d.set_workgroups(256)
+        if ok:
+            assert d.describe()["max_tile_bytes"] * 3 <= d.describe()["ring_bytes"]
+        else:
+            with pytest.raises(MbkError) as e:
+                d.describe()
+            assert e.value.code == MBK_ERR_UNSUPPORTED and "ring" in str(e.value)
+        d.close()
+
+
 def test_set_workgroups_after_planning_is_a_state_error():
     from persistent_megakernel_decode_wg_amd import Decoder, MbkError, MBK_ERR_STATE
     d = Decoder(synth.get("tiny-2L-h64-kv32"))
