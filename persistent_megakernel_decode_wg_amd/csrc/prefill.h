@@ -698,14 +698,42 @@ __global__ __launch_bounds__(64 * W) void k_pf_attn_mma(PfParams p, int layer, i
 }
 
 // Greedy argmax of the V logits (lowest index among equal maxima); also the decode step's previous token.
+// The rule picks the largest value, then the lowest index, so any scan order gives the same index: each thread
+// takes every 1024th group of four logits (one 16-byte load, four loads in flight) where V is a multiple of 4.
+__device__ __forceinline__ void pf_amax_take(float v, int i, float &best, int &idx) {
+    if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+}
 __global__ __launch_bounds__(1024) void k_pf_argmax(PfParams p) {
     __shared__ float bv[1024];
     __shared__ int bi[1024];
     float best = -INFINITY;
     int idx = 0x7fffffff;
-    for (int i = threadIdx.x; i < p.V; i += 1024) {
-        const float v = p.logits[i];
-        if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+    if ((p.V & 3) == 0 && ((uintptr_t)p.logits & 15) == 0) {
+        const float4 *l4 = (const float4 *)p.logits;
+        const int n4 = p.V >> 2;
+        int i = threadIdx.x;
+        for (; i + 3 * 1024 < n4; i += 4 * 1024) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = l4[i + u * 1024];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = 4 * (i + u * 1024);
+                pf_amax_take(v[u].x, b, best, idx);
+                pf_amax_take(v[u].y, b + 1, best, idx);
+                pf_amax_take(v[u].z, b + 2, best, idx);
+                pf_amax_take(v[u].w, b + 3, best, idx);
+            }
+        }
+        for (; i < n4; i += 1024) {
+            const float4 v = l4[i];
+            pf_amax_take(v.x, 4 * i, best, idx);
+            pf_amax_take(v.y, 4 * i + 1, best, idx);
+            pf_amax_take(v.z, 4 * i + 2, best, idx);
+            pf_amax_take(v.w, 4 * i + 3, best, idx);
+        }
+    } else {
+        for (int i = threadIdx.x; i < p.V; i += 1024) pf_amax_take(p.logits[i], i, best, idx);
     }
     bv[threadIdx.x] = best;
     bi[threadIdx.x] = idx;

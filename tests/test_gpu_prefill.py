@@ -247,10 +247,11 @@ def test_prefill_1p7b_shape_kernel_forms_agree_bitwise(make):
 
 def test_prefill_inputs_not_a_multiple_of_32(make):
     """Hidden 200, query heads x head size 5 x 16 = 80 and intermediate 528 (each a multiple of 8 but not of
-    32, so every GEMM's last k step of 32 inputs runs past the row's end onto cleared entries): a 45-token
-    prompt against the stepped oracle, and the same prompt as 0..20 and 21..44 giving the one-shot bits."""
+    32, so every GEMM's last k step of 32 inputs runs past the row's end onto cleared entries), vocabulary 1,030
+    (a ragged last row block, and the argmax's one-logit-at-a-time scan): a 45-token prompt against the stepped
+    oracle, and the same prompt as 0..20 and 21..44 giving the one-shot bits."""
     import torch
-    wl = synth.Workload("pf-ragged-k-h200", 2, 200, 5, 1, 16, 528, 1024, 128, False, 1e-5, 1e4,
+    wl = synth.Workload("pf-ragged-k-h200", 2, 200, 5, 1, 16, 528, 1030, 128, False, 1e-5, 1e4,
                         n_prompt=0, kv_prefill=0, n_decode=0)
     W = synth.make_weights(wl)
     a, b = make(wl, W), make(wl, W)
