@@ -164,16 +164,19 @@ def prefill_flops(wl, n: int, pos0: int = 0) -> float:
     return 2.0 * n * per_layer * wl.n_layers + 2.0 * 2 * hd * nq * attended * wl.n_layers + 2.0 * wl.vocab * H
 
 
-def prefill_summary(wl, n: int, decode_us: float, reps: int = 5):
+def prefill_summary(wl, n: int, decode_us: float, reps: int = 5, fp8: bool = False):
     """p50 time of one prefill of n seeded tokens at position 0 (HIP events on the stream), against n decode
     steps of the same model (decode_us per step), and its algorithmic TFLOP/s against the bf16 matrix-core
-    peak (the hi/lo input pairs double the products actually executed)."""
+    peak (the hi/lo input pairs double the products actually executed); fp8: on the E4M3-quantised weights."""
     import torch
     import synth
     from persistent_megakernel_decode_wg_amd import Decoder
     W = synth.make_weights(wl)
     dev = lambda a: torch.from_numpy(a.view("int16")).cuda()
     dec = Decoder(wl)
+    if fp8:
+        from persistent_megakernel_decode_wg_amd import MBK_WEIGHTS_FP8_E4M3
+        dec.set_weight_format(MBK_WEIGHTS_FP8_E4M3)
     dec.pack_weights({"embed": dev(W["embed"]), "final_norm": dev(W["final_norm"]),
                       "layers": [{k: dev(v) for k, v in L.items()} for L in W["layers"]]})
     del W
@@ -302,8 +305,9 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.get(args.workload)
     if args.prefill_tokens:
-        res = prefill_summary(wl, args.prefill_tokens, None)
-        print(json.dumps({"metric": "prefill us (one call)", "workload": wl.name, **res}), flush=True)
+        res = prefill_summary(wl, args.prefill_tokens, None, fp8=args.weights == "fp8")
+        print(json.dumps({"metric": "prefill us (one call)", "workload": wl.name, "weights": args.weights, **res}),
+              flush=True)
         return
     fp8 = args.weights == "fp8"
     dec, W, logits, am, g0, g1 = setup_workload(wl, fp8=fp8)

@@ -44,47 +44,49 @@ void pf_gemm_lds(const PfParams &pp, const MatGeom &g, int layer, int src, int d
                        dst, np_rows, bias);
 }
 
+// The per-wave kernel's launch shape (bf16 or fp8 weights alike): four row blocks and two position blocks per
+// workgroup (every activation load feeds four products, every weight load two) while that leaves at least 256
+// workgroups; else, for matrices of up to 8M weights, one position block per workgroup, and for larger ones
+// two; with two row blocks while that leaves 256 workgroups, else one.
+template <int OP, bool F8>
+void pf_gemm_wave(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias,
+                  hipStream_t st) {
+    const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos), p16 = (unsigned)(np_rows / 16);
+    const unsigned x4 = (unsigned)((g.rows + 63) / 64), x2 = (unsigned)((g.rows + 31) / 32), x1 = (unsigned)((g.rows + 15) / 16);
+    const bool one_pb = (size_t)g.rows * g.K <= kPfOnePbWeights;
+    if (x4 * py >= 256)
+        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, F8, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    else if (one_pb && x2 * p16 >= 256)
+        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, F8, 1>), dim3(x2, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    else if (one_pb)
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, F8, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    else if (x2 * py >= 256)
+        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, F8, 2>), dim3(x2, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+    else
+        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, F8, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
+}
+
 template <int OP>
 void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias, hipStream_t st) {
     // every matrix's k steps are split over four waves whatever the prompt length: the split fixes the order
     // in which a row's products are added, so a prompt's results do not depend on how it is cut into calls.
     // Long prompts over bf16 weights: operand tiles shared through LDS (128-row workgroup tiles, or 64-row ones
-    // where the 128-row tiles would leave fewer than two workgroups per compute unit); else four row blocks
-    // and two position blocks per workgroup (every activation load feeds four products, every weight load
-    // two) while that leaves at least 256 workgroups; else, for matrices of up to 8M weights, one position
-    // block per workgroup, and for larger ones two; with two row blocks while that leaves 256 workgroups, else
-    // one (none of these choices changes the order; fp8 matrices always take the per-wave kernel, which widens
-    // their codes, with four row blocks and two position blocks or one row block)
-    const unsigned py = (unsigned)((np_rows + kPfPos - 1) / kPfPos), p16 = (unsigned)(np_rows / 16);
-    const unsigned x4 = (unsigned)((g.rows + 63) / 64), x2 = (unsigned)((g.rows + 31) / 32), x1 = (unsigned)((g.rows + 15) / 16);
+    // where the 128-row tiles would leave fewer than two workgroups per compute unit); else the per-wave kernel
+    // (none of these choices changes the order; fp8 matrices always take the per-wave kernel, which widens
+    // their codes)
     const unsigned pl = (unsigned)(np_rows / 64);
     const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
     const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
-    const bool one_pb = (size_t)g.rows * g.K <= kPfOnePbWeights;
-    if (lds_ok && g4 >= 512) {
+    if (lds_ok && g4 >= 512)
         pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
-    } else if (lds_ok && g2 >= 256 && g4 >= kPfLMinGroups) {
+    else if (lds_ok && g2 >= 256 && g4 >= kPfLMinGroups)
         pf_gemm_lds<OP, 2>(pp, g, layer, src, dst, np_rows, bias, st);
-    } else if (lds_ok && g4 >= kPfLMinGroups) {
+    else if (lds_ok && g4 >= kPfLMinGroups)
         pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
-    } else if (g.fmt == FMT_FP8) {
-        if (x4 * py >= 256)
-            hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, true, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-        else if (one_pb)
-            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-        else
-            hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, true, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    } else if (x4 * py >= 256) {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 4, 4, false, 2>), dim3(x4, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    } else if (one_pb && x2 * p16 >= 256) {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, false, 1>), dim3(x2, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    } else if (one_pb) {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 1>), dim3(x1, p16), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    } else if (x2 * py >= 256) {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 2, 4, false, 2>), dim3(x2, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    } else {
-        hipLaunchKernelGGL((k_pf_gemm<OP, 1, 4, false, 2>), dim3(x1, py), dim3(256), 0, st, pp, g, layer, src, dst, np_rows, bias);
-    }
+    else if (g.fmt == FMT_FP8)
+        pf_gemm_wave<OP, true>(pp, g, layer, src, dst, np_rows, bias, st);
+    else
+        pf_gemm_wave<OP, false>(pp, g, layer, src, dst, np_rows, bias, st);
 }
 
 }  // namespace
