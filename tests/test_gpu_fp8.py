@@ -228,3 +228,27 @@ def test_fp8_prefill_against_the_quantised_oracle(name):
     finally:
         a.close()
         b.close()
+
+
+def test_fp8_prefill_1p7b_shape_kernel_forms_agree_bitwise():
+    """Two layers of the SmolLM-1.7B shape on an FP8 handle: a 256-token prompt in one call (every projection
+    with four row blocks and two position blocks per workgroup) and in four calls of 64 tokens (query/key/value
+    two row blocks and two position blocks, the 4M-weight output projection two row blocks and one position
+    block, gate/up four and two, down one and two) give the same logits, argmax and cache bit for bit; the first
+    64-token call is also checked against the oracle on the quantised model."""
+    import torch
+    wl = synth.Workload("smollm1.7b-2L-kv512", 2, 2048, 32, 32, 64, 8192, 49152, 512, False, 1e-5, 1e4,
+                        n_prompt=0, kv_prefill=0, n_decode=0)
+    W = synth.make_weights(wl)
+    toks = [int(t) for t in synth.tokens(31, "fp8-prefill-forms", 256, wl.vocab)]
+    a, b = _Fp8Prefill(wl, W), _Fp8Prefill(wl, W)
+    try:
+        la, ia = a.prefill(toks, 0)
+        b.check(toks[:64], 0, "fp8 smollm1.7b shape, 2 layers, prefill 0..63")
+        for c in range(64, 256, 64):
+            lb, ib = b.prefill(toks[c:c + 64], c)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)) and ia == ib
+        assert torch.equal(a.dec.kv, b.dec.kv)
+    finally:
+        a.close()
+        b.close()
