@@ -34,6 +34,7 @@ struct PfParams {
     float *x;                // [Pp][H] residual stream
     float *q;                // [Pp][nq * hd] rotated queries
     uint16_t *inh[2], *inl[2];  // GEMM inputs as hi/lo bf16 [Pp][ks] (two buffers, used in turn)
+    float *part;             // [4][Pp][H] quarter sums of a k-split output or down projection
     float *logits;           // [V]
     int32_t *argmax_out;     // device int32
     uint32_t *prev_token;    // the decode workspace's previous-argmax word, or null
@@ -286,7 +287,7 @@ template <int WRB> struct PfLGeom {
 typedef __attribute__((address_space(3))) void pf_lds_void_t;
 typedef __attribute__((address_space(1))) void pf_glb_void_t;
 
-template <int OP, int WRB>
+template <int OP, int WRB, bool SPLIT>
 __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int layer, int src, int dst, int np_rows,
                                                      uint64_t bias_off) {
     typedef PfLGeom<WRB> Gm;
@@ -294,7 +295,10 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
     extern __shared__ __attribute__((aligned(16))) uint8_t pf_ring[];
     const int l = threadIdx.x & 63, wv = threadIdx.x >> 6, wr = wv >> 1, wc = wv & 1;
     const int rbase = blockIdx.x * 32 * WRB, pbase = blockIdx.y * 64;
-    const int ngrp = g.K >> 3, nall = (ngrp + 3) >> 2, nst = (nall + kPfLStep - 1) / kPfLStep;
+    const int ngrp = g.K >> 3, nall = (ngrp + 3) >> 2;
+    // SPLIT: this workgroup forms only quarter blockIdx.z of the k steps and stores its chain to p.part
+    const int s_lo = SPLIT ? nall * (int)blockIdx.z / 4 : 0, s_hi = SPLIT ? nall * ((int)blockIdx.z + 1) / 4 : nall;
+    const int nst = (s_hi - s_lo + kPfLStep - 1) / kPfLStep;
     const uint16_t *ah = p.inh[src], *al = p.inl[src];
     // the loads of stage st: wave w issues tiles w, w + 4, ... of the stage; tile u of a k step is
     // activation block u / 2 (hi for even u, lo for odd) for u < 8, weight row block u - 8 after
@@ -302,8 +306,8 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
         uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * Gm::kStageBytes;
 #pragma unroll
         for (int t = wv; t < Gm::kTiles; t += 4) {
-            const int i = t / kPerStep, u = t - i * kPerStep, s = st * kPfLStep + i;
-            if (s >= nall) continue;
+            const int i = t / kPerStep, u = t - i * kPerStep, s = s_lo + st * kPfLStep + i;
+            if (s >= s_hi) continue;
             const int kg = 4 * s + (l >> 4);
             const uint8_t *a;
             if (u < 8) {
@@ -350,9 +354,10 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
         const uint8_t *buf = pf_ring + (st % (kPfLAhead + 1)) * Gm::kStageBytes;
 #pragma unroll
         for (int i = 0; i < kPfLStep; ++i) {
-            const int s = st * kPfLStep + i;
-            if (s >= nall) break;
-            while (q < 3 && s >= qend) close_quarter();
+            const int s = s_lo + st * kPfLStep + i;
+            if (s >= s_hi) break;
+            if (!SPLIT)
+                while (q < 3 && s >= qend) close_quarter();
             const uint8_t *tb = buf + i * kPerStep * 1024 + l * 16;
             pf_u32x4 xa[2][2], wb[WRB];
 #pragma unroll
@@ -375,8 +380,23 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
             }
         }
     }
-    while (q < 4) close_quarter();  // the remaining quarters (possibly empty) in order
     const int kq = l >> 4;
+    if (SPLIT) {
+#pragma unroll
+        for (int rb = 0; rb < WRB; ++rb) {
+            const int n = rbase + 16 * WRB * wr + 16 * rb + (l & 15);
+            if (n >= g.rows) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int pos = pbase + 32 * wc + 16 * j + 4 * kq + r;
+                    p.part[((size_t)blockIdx.z * np_rows + pos) * g.rows + n] = acc[rb][j][r];
+                }
+        }
+        return;
+    }
+    while (q < 4) close_quarter();  // the remaining quarters (possibly empty) in order
 #pragma unroll
     for (int rb = 0; rb < WRB; ++rb)
 #pragma unroll
@@ -385,6 +405,18 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
             for (int r = 0; r < 4; ++r)
                 pf_epilogue<OP>(p, g, layer, dst, bias_off, rbase + 16 * WRB * wr + 16 * rb + (l & 15),
                                 pbase + 32 * wc + 16 * j + 4 * kq + r, tot[rb][j][r]);
+}
+
+// The output or down projection of a k-split shared-tile GEMM: the four quarter chains added in order, as
+// the unsplit kernels add them, then the epilogue (one thread per output).
+template <int OP>
+__global__ __launch_bounds__(256) void k_pf_split_sum(PfParams p, MatGeom g, int layer, int dst, int np_rows,
+                                                      uint64_t bias_off) {
+    const int n = (int)(blockIdx.x * 256 + threadIdx.x), pos = (int)blockIdx.y;
+    if (n >= g.rows) return;
+    const size_t q = (size_t)np_rows * g.rows, at = (size_t)pos * g.rows + n;
+    const float t = ((p.part[at] + p.part[at + q]) + p.part[at + 2 * q]) + p.part[at + 3 * q];
+    pf_epilogue<OP>(p, g, layer, dst, bias_off, n, pos, t);
 }
 
 // Columns [K, K rounded up to 32) of the rows written by the attention or the gate/up epilogue (the next

@@ -7,7 +7,7 @@ namespace {
 
 // Scratch of a prefill of n tokens: token ids, residual stream, rotated queries, two hi/lo input buffers
 // and the logits.  Rows are padded to whole position tiles.
-struct PfLayout { size_t tok, x, q, in[4], logits, total; int Pp, ks; };
+struct PfLayout { size_t tok, x, q, in[4], logits, part, total; int Pp, ks; };
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
@@ -22,26 +22,32 @@ PfLayout pf_layout(const mbk_config &c, int n) {
     L.q = o; o = align256(o + 4u * (size_t)L.Pp * Q);
     for (int i = 0; i < 4; ++i) { L.in[i] = o; o = align256(o + 2u * (size_t)L.Pp * L.ks); }
     L.logits = o; o = align256(o + 4u * (size_t)c.vocab);
+    L.part = o; o = align256(o + 16u * (size_t)L.Pp * c.hidden);
     L.total = o;
     return L;
 }
 
 constexpr unsigned kPfLMinGroups = 128;  // workgroups the shared-tile GEMM needs to fill the device
+constexpr int kPfSplitMinK = 2048;       // inputs from which output / down projections split their k steps
+constexpr unsigned kPfSplitMinGroups = 64;  // 128-row tiles from which they do (x 4 workgroups)
 constexpr size_t kPfOnePbWeights = (size_t)8 << 20;  // largest matrix whose per-wave GEMM takes one position block
 
 // One shared-tile GEMM launch (its LDS above the default limit is allowed once per instance).
-template <int OP, int WRB>
+template <int OP, int WRB, bool SPLIT = false>
 void pf_gemm_lds(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, int np_rows, uint64_t bias,
                  hipStream_t st) {
     static bool lds_set = false;
     if (!lds_set) {
-        (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP, WRB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  PfLGeom<WRB>::kLds);
+        (void)hipFuncSetAttribute((const void *)k_pf_gemm_lds<OP, WRB, SPLIT>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, PfLGeom<WRB>::kLds);
         lds_set = true;
     }
-    const dim3 grid((unsigned)((g.rows + 32 * WRB - 1) / (32 * WRB)), (unsigned)(np_rows / 64));
-    hipLaunchKernelGGL((k_pf_gemm_lds<OP, WRB>), grid, dim3(256), (unsigned)PfLGeom<WRB>::kLds, st, pp, g, layer, src,
-                       dst, np_rows, bias);
+    const dim3 grid((unsigned)((g.rows + 32 * WRB - 1) / (32 * WRB)), (unsigned)(np_rows / 64), SPLIT ? 4u : 1u);
+    hipLaunchKernelGGL((k_pf_gemm_lds<OP, WRB, SPLIT>), grid, dim3(256), (unsigned)PfLGeom<WRB>::kLds, st, pp, g,
+                       layer, src, dst, np_rows, bias);
+    if (SPLIT)
+        hipLaunchKernelGGL(k_pf_split_sum<OP>, dim3((unsigned)((g.rows + 255) / 256), (unsigned)np_rows), dim3(256), 0,
+                           st, pp, g, layer, dst, np_rows, bias);
 }
 
 // The per-wave kernel's launch shape (bf16 or fp8 weights alike): four row blocks and two position blocks per
@@ -77,7 +83,12 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     const unsigned pl = (unsigned)(np_rows / 64);
     const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
     const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
-    if (lds_ok && g4 >= 512)
+    // output and down projections over wide inputs: the four k-step quarters on four workgroups each (four
+    // times the workgroups, a quarter of the chain), their sums added in order by a second kernel
+    constexpr bool kSplitOp = OP == OP_O || OP == OP_DOWN;
+    if (kSplitOp && lds_ok && g.K >= kPfSplitMinK && g4 >= kPfSplitMinGroups && g4 < 512)
+        pf_gemm_lds<OP, 4, kSplitOp>(pp, g, layer, src, dst, np_rows, bias, st);
+    else if (lds_ok && g4 >= 512)
         pf_gemm_lds<OP, 4>(pp, g, layer, src, dst, np_rows, bias, st);
     else if (lds_ok && g2 >= 256 && g4 >= kPfLMinGroups)
         pf_gemm_lds<OP, 2>(pp, g, layer, src, dst, np_rows, bias, st);
@@ -126,6 +137,7 @@ int mbk_prefill(mbk_model *m, const int32_t *tokens, int32_t n_tokens, int32_t p
     pp.inl[0] = (uint16_t *)(sc + L.in[1]);
     pp.inh[1] = (uint16_t *)(sc + L.in[2]);
     pp.inl[1] = (uint16_t *)(sc + L.in[3]);
+    pp.part = (float *)(sc + L.part);
     pp.logits = logits ? logits : (float *)(sc + L.logits);
     pp.argmax_out = argmax;
     pp.prev_token = m->ws ? (uint32_t *)(m->ws + P.ws.ctrl) + 1 : nullptr;
