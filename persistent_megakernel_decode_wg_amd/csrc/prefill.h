@@ -34,7 +34,7 @@ struct PfParams {
     float *x;                // [Pp][H] residual stream
     float *q;                // [Pp][nq * hd] rotated queries
     uint16_t *inh[2], *inl[2];  // GEMM inputs as hi/lo bf16 [Pp][ks] (two buffers, used in turn)
-    float *part;             // [4][Pp][H] quarter sums of a k-split output or down projection
+    float *part;             // [4][Pp][rows] quarter sums of a k-split projection (rows: hidden or Q/K/V rows)
     float *logits;           // [V]
     int32_t *argmax_out;     // device int32
     uint32_t *prev_token;    // the decode workspace's previous-argmax word, or null
@@ -407,8 +407,9 @@ __global__ __launch_bounds__(256) void k_pf_gemm_lds(PfParams p, MatGeom g, int 
                                 pbase + 32 * wc + 16 * j + 4 * kq + r, tot[rb][j][r]);
 }
 
-// The output or down projection of a k-split shared-tile GEMM: the four quarter chains added in order, as
-// the unsplit kernels add them, then the epilogue (one thread per output).
+// A k-split shared-tile GEMM's outputs: the four quarter chains added in order, as the unsplit kernels add
+// them, then the epilogue (one thread per output; adjacent rows in adjacent lanes, as the Q/K/V epilogue's
+// lane pairs need).
 template <int OP>
 __global__ __launch_bounds__(256) void k_pf_split_sum(PfParams p, MatGeom g, int layer, int dst, int np_rows,
                                                       uint64_t bias_off) {

@@ -5,8 +5,8 @@
 
 namespace {
 
-// Scratch of a prefill of n tokens: token ids, residual stream, rotated queries, two hi/lo input buffers
-// and the logits.  Rows are padded to whole position tiles.
+// Scratch of a prefill of n tokens: token ids, residual stream, rotated queries, two hi/lo input buffers,
+// the logits and the quarter sums of a k-split projection.  Rows are padded to whole position tiles.
 struct PfLayout { size_t tok, x, q, in[4], logits, part, total; int Pp, ks; };
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -22,13 +22,13 @@ PfLayout pf_layout(const mbk_config &c, int n) {
     L.q = o; o = align256(o + 4u * (size_t)L.Pp * Q);
     for (int i = 0; i < 4; ++i) { L.in[i] = o; o = align256(o + 2u * (size_t)L.Pp * L.ks); }
     L.logits = o; o = align256(o + 4u * (size_t)c.vocab);
-    L.part = o; o = align256(o + 16u * (size_t)L.Pp * c.hidden);
+    L.part = o; o = align256(o + 16u * (size_t)L.Pp * std::max(c.hidden, Q + 2 * c.n_kv_heads * c.head_dim));
     L.total = o;
     return L;
 }
 
 constexpr unsigned kPfLMinGroups = 128;  // workgroups the shared-tile GEMM needs to fill the device
-constexpr int kPfSplitMinK = 2048;       // inputs from which output / down projections split their k steps
+constexpr int kPfSplitMinK = 2048;       // inputs from which Q/K/V, output and down projections split their k steps
 constexpr unsigned kPfSplitMinGroups = 64;  // 128-row tiles from which they do (x 4 workgroups)
 constexpr size_t kPfOnePbWeights = (size_t)8 << 20;  // largest matrix whose per-wave GEMM takes one position block
 
@@ -83,9 +83,9 @@ void pf_gemm(const PfParams &pp, const MatGeom &g, int layer, int src, int dst, 
     const unsigned pl = (unsigned)(np_rows / 64);
     const unsigned g4 = (unsigned)((g.rows + 127) / 128) * pl, g2 = (unsigned)((g.rows + 63) / 64) * pl;
     const bool lds_ok = g.fmt == FMT_BF16 && np_rows % 64 == 0;
-    // output and down projections over wide inputs: the four k-step quarters on four workgroups each (four
+    // query/key/value, output and down projections over wide inputs: the four k-step quarters on four workgroups each (four
     // times the workgroups, a quarter of the chain), their sums added in order by a second kernel
-    constexpr bool kSplitOp = OP == OP_O || OP == OP_DOWN;
+    constexpr bool kSplitOp = OP == OP_O || OP == OP_DOWN || OP == OP_QKV;
     if (kSplitOp && lds_ok && g.K >= kPfSplitMinK && g4 >= kPfSplitMinGroups && g4 < 512)
         pf_gemm_lds<OP, 4, kSplitOp>(pp, g, layer, src, dst, np_rows, bias, st);
     else if (lds_ok && g4 >= 512)

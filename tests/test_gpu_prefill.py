@@ -225,9 +225,9 @@ def test_prefill_long_prompt_equals_short_chunks_bitwise(make):
 
 
 def test_prefill_1p7b_shape_kernel_forms_agree_bitwise(make):
-    """Two layers of the SmolLM-1.7B shape: a 256-token prompt in one call (query/key/value and gate/up
-    projections with operand tiles shared through LDS, output and down projections the same with their k-step
-    quarters on separate workgroups, summed in order by a second kernel) and in four calls of 64 tokens (gate/up still through LDS; query/key/value
+    """Two layers of the SmolLM-1.7B shape: a 256-token prompt in one call (every projection with operand tiles
+    shared through LDS; query/key/value, output and down projections with their k-step quarters on separate
+    workgroups, summed in order by a second kernel) and in four calls of 64 tokens (gate/up still through LDS; query/key/value
     with two row blocks and two position blocks, the 4M-weight output projection two row blocks and one
     position block, down one row block and two position blocks) give the same logits, argmax and cache bit for
     bit; the first 64-token call is also checked against the oracle."""
