@@ -164,7 +164,7 @@ def prefill_flops(wl, n: int, pos0: int = 0) -> float:
     return 2.0 * n * per_layer * wl.n_layers + 2.0 * 2 * hd * nq * attended * wl.n_layers + 2.0 * wl.vocab * H
 
 
-def prefill_summary(wl, n: int, decode_us: float, reps: int = 5, fp8: bool = False):
+def prefill_summary(wl, n: int, decode_us: float, reps: int = 21, fp8: bool = False):
     """p50 time of one prefill of n seeded tokens at position 0 (HIP events on the stream), against n decode
     steps of the same model (decode_us per step), and its algorithmic TFLOP/s against the bf16 matrix-core
     peak (the hi/lo input pairs double the products actually executed); fp8: on the E4M3-quantised weights."""
